@@ -1,0 +1,180 @@
+/*
+ * pa.h -- C ABI of the paged-KV attention library (libpa.so, gfx950 / MI355X).
+ *
+ * The operations follow the paged KV cache of the pages this library is built
+ * from:
+ *   - "3.3 Batching and memory management" (llm-learning-path tutorial),
+ *     section "PagedAttention: the block table": the KV pool is cut into
+ *     physical blocks of block_size tokens; entry j of a sequence's block
+ *     table names the block holding its tokens [j*block_size, (j+1)*block_size);
+ *     token p lives in block table[p / block_size] at offset p % block_size.
+ *     Section "Chunked prefill": a chunk's queries attend to a cache that
+ *     already holds the earlier chunks.
+ *   - "KV Cache: the memory bottleneck of LLM inference" (excerpt on the
+ *     "PagedAttention" tag page), section 1.1: at step t the new k_t, v_t are
+ *     appended to the cache and the output is softmax(q_t K_{1:t}^T/sqrt(d)) V_{1:t}.
+ *   - "From PagedAttention to Chunked Prefill" (ybb.press), section 2.2: the
+ *     kernel walks the blocks with the online (iterative) softmax recurrence;
+ *     section 3.2: one batch mixes query_len = 1 decode rows and
+ *     query_len = chunk prefill rows, located by cumulative offsets.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer owned by the caller.
+ *   The library allocates no device memory, keeps no per-call state and never
+ *   synchronises: each call enqueues its kernels on `stream` (a hipStream_t;
+ *   NULL = the null stream) and returns.  Calls on different streams may run
+ *   concurrently when their output buffers do not overlap.
+ * Cache layout.  k_cache and v_cache are per-layer pools, row-major
+ *   [num_blocks][block_size][n_kv_heads][head_dim] of `cache_dtype` elements.
+ * Block tables.  int32 [num_seqs][max_blocks_per_seq], row-major; only the
+ *   first ceil(context_len / block_size) entries of a row are read; padding
+ *   entries should be -1.
+ * Context lengths.  int32 [num_seqs]; context_lens[s] counts every token of
+ *   sequence s INCLUDING the ones appended in the current step (append first,
+ *   then attend).
+ * Heads.  n_q_heads = n_kv_heads * group_size; query head h reads KV head
+ *   h / group_size (grouped-query attention; group_size 1 is multi-head).
+ * Errors.  Host-checkable errors return a status before anything is enqueued;
+ *   a failed launch returns PA_ERR_HIP.  Device-resident preconditions are not
+ *   checked on the device: block ids must lie in [0, num_blocks) for the
+ *   positions that are read, context_lens[s] <= max_blocks_per_seq*block_size,
+ *   context_lens[s] <= max_context_len, append slots must be distinct.  As a
+ *   guard against memory faults only, a block id or slot outside the pool is
+ *   skipped (its tokens contribute nothing / are not written).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,        /* inconsistent or negative sizes */
+  PA_ERR_DTYPE = 3,        /* unsupported dtype or dtype pair */
+  PA_ERR_UNSUPPORTED = 4,  /* head_dim / block_size / group_size outside the supported set */
+  PA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the query function says */
+  PA_ERR_HIP = 6           /* a HIP launch or runtime call failed */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,              /* IEEE binary32 */
+  PA_BF16 = 1,             /* bfloat16 */
+  PA_FP8_E4M3 = 2          /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF) */
+} pa_dtype;
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* pa_status_string(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+int pa_abi_version(void);
+
+/*
+ * pa_slot_mapping -- the block-table address map for a ragged set of tokens.
+ *   Source: "3.3 Batching and memory management", section "PagedAttention:
+ *   the block table" (physical block = table[p / block_size], offset =
+ *   p mod block_size).
+ *
+ *   Token i of segment s (cu_tokens[s] <= i < cu_tokens[s+1]) sits at logical
+ *   position p = start_pos[s] + (i - cu_tokens[s]) of sequence s and gets
+ *     slot_mapping[i] = table[s][p / block_size] * block_size + p % block_size,
+ *   or -1 when that table entry is negative.  Decode rows use
+ *   start_pos = context_len - 1 and one token; a prefill chunk of L tokens uses
+ *   start_pos = context_len - L.
+ *
+ *   slot_mapping  int64 [num_tokens]      (out)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   cu_tokens     int32 [num_seqs + 1]    cumulative token counts, cu_tokens[num_seqs] == num_tokens
+ *   start_pos     int32 [num_seqs]
+ *   block_size    >= 1 (any value)
+ *   Positions past the table row (p / block_size >= max_blocks_per_seq) give -1.
+ */
+pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t block_size,
+                          const int32_t* cu_tokens, const int32_t* start_pos,
+                          int32_t num_seqs, int32_t num_tokens, void* stream);
+
+/*
+ * pa_kv_append -- scatter new K/V rows into their cache slots.
+ *   Source: "KV Cache: the memory bottleneck of LLM inference", section 1.1
+ *   (append k_t, v_t to the cache); slot addressing as in pa_slot_mapping.
+ *
+ *   For every i with 0 <= slot_mapping[i] < num_blocks*block_size:
+ *     k_cache[slot / block_size][slot % block_size][h][:] = enc(k_new[i][h][:])  (all h)
+ *   and the same for V.  Negative slots are skipped; no other byte of the
+ *   pools is written.  enc is a bit copy when src_dtype == cache_dtype
+ *   (F32 or BF16); for an FP8_E4M3 cache (src F32 or BF16) it is
+ *     e4m3_satfinite_rne( float(x) * (1.0f / scale) )
+ *   with the inverse computed once in binary32 on the host, the magnitude
+ *   clamped to 448 (infinities too), ties rounded to even, NaN -> 0x7F.
+ *   k_scale / v_scale are the per-tensor scales (read only for FP8 caches).
+ *
+ *   k_new, v_new  [num_tokens][n_kv_heads][head_dim] of src_dtype (contiguous)
+ *   slot_mapping  int64 [num_tokens], distinct non-negative entries
+ *   head_dim      a multiple of 8
+ */
+pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
+                       int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                       int32_t head_dim, const void* k_new, const void* v_new,
+                       int src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                       float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- scratch needed by pa_decode for these sizes.
+ *   split_tokens: 0 = the library's choice; otherwise the minimum number of
+ *   context tokens one split (one workgroup) handles, rounded up to 16.
+ *   The same split_tokens must be passed to pa_decode.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t split_tokens);
+
+/*
+ * pa_decode -- single-token paged attention for a ragged batch.
+ *   Source: attention at step t over K_{1:t}, V_{1:t} ("KV Cache: the memory
+ *   bottleneck", section 1.1) gathered through the block table ("3.3 Batching
+ *   and memory management", "PagedAttention: the block table"), computed
+ *   block by block with the online softmax recurrence ("From PagedAttention to
+ *   Chunked Prefill", section 2.2; rescale factor e^{m_old - m_new} applied
+ *   to the unnormalised accumulator, division by the running sum at the end).
+ *   Long contexts are cut into splits handled by separate workgroups; their
+ *   partial (m, l, O) are combined with the log-sum-exp merge
+ *   M = max m_k, O = sum_k e^{m_k - M} O_k / sum_k e^{m_k - M} l_k.
+ *
+ *   out[s][h][:] = sum_j softmax_j(scale * q[s][h] . K_s[j][h/g]) V_s[j][h/g][:],
+ *   j < context_lens[s]; a sequence with context 0 gets zeros.  For FP8 caches
+ *   the stored codes are multiplied by k_scale / v_scale.
+ *
+ *   out           [num_seqs][n_q_heads][head_dim], dtype = q_dtype (bf16 output is
+ *                 rounded to nearest even)
+ *   q             [num_seqs][n_q_heads][head_dim] of q_dtype
+ *   dtype pairs   (q, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}
+ *   head_dim      64 or 128;  block_size a power of two in [1, 256];
+ *   group_size    1, 2, 4 or 8
+ *   max_context_len  host-side upper bound of context_lens (sizes the plan)
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes, 256-byte aligned; contents need no initialisation and
+ *                 are clobbered.
+ *   Results are deterministic run to run (no atomics) and do not depend on
+ *   which physical blocks hold the tokens.
+ */
+pa_status pa_decode(void* out, const void* q, int q_dtype,
+                    const void* k_cache, const void* v_cache, int cache_dtype,
+                    int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t group_size,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                    float scale, float k_scale, float v_scale, int32_t split_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,170 @@
+"""Python binding of libpa.so, the paged-KV attention library for MI355X (gfx950).
+
+Argument marshalling only: each function reads sizes off torch tensors, checks
+dtypes/shapes, and passes raw device pointers plus the current HIP stream to
+the C entry point of the same name (declared in include/pa.h).  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.  If
+the library is not built, importing works but the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
+           4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.pa_status_string(status).decode() if _lib is not None else _STATUS.get(status)
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+def _c(fn, restype, *argtypes):
+    f = getattr(_lib, fn)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+
+
+def lib():
+    """Load libpa.so (after torch, so both use torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run `python -m paged_kv_cache_74_amd.build`)")
+        _lib = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        _c("pa_status_string", ctypes.c_char_p, ctypes.c_int)
+        _c("pa_abi_version", ctypes.c_int)
+        _c("pa_slot_mapping", ctypes.c_int, P, P, I, I, P, P, I, I, P)
+        _c("pa_kv_append", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int, P, I,
+           F, F, P)
+        _c("pa_decode_workspace_bytes", S, I, I, I, I, I, I)
+        _c("pa_decode", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I, P, I,
+           P, I, I, F, F, F, I, P, S, P)
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PagedAttentionError(fn, status)
+
+
+def _need(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _dev(*ts):
+    for t in ts:
+        _need(t.is_cuda, "all tensors must live on the GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+
+
+def pa_abi_version() -> int:
+    return int(lib().pa_abi_version())
+
+
+def pa_slot_mapping(block_tables: torch.Tensor, cu_tokens: torch.Tensor, start_pos: torch.Tensor,
+                    block_size: int, num_tokens: int, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Slots (int64) of ragged token segments; see pa_slot_mapping in pa.h."""
+    L = lib()
+    num_seqs = start_pos.shape[0]
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    _dev(block_tables, cu_tokens, start_pos, out)
+    _need(block_tables.dtype == cu_tokens.dtype == start_pos.dtype == torch.int32, "int32 tables")
+    _need(out.dtype == torch.int64 and out.numel() >= num_tokens, "out: int64 [num_tokens]")
+    _need(cu_tokens.numel() == num_seqs + 1, "cu_tokens: [num_seqs + 1]")
+    _check("pa_slot_mapping", L.pa_slot_mapping(
+        _ptr(out), _ptr(block_tables), block_tables.shape[1] if block_tables.dim() == 2 else 0,
+        block_size, _ptr(cu_tokens), _ptr(start_pos), num_seqs, num_tokens, _stream(stream)))
+    return out
+
+
+def pa_kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                 v_new: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
+                 v_scale: float = 1.0, stream=None) -> None:
+    """Scatter k_new/v_new [T, n_kv, hd] into the pools [num_blocks, bs, n_kv, hd]."""
+    L = lib()
+    _dev(k_cache, v_cache, k_new, v_new, slot_mapping)
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "pools: [nb, bs, n_kv, hd]")
+    _need(k_cache.dtype == v_cache.dtype and k_new.dtype == v_new.dtype, "dtype mismatch")
+    nb, bs, nkv, hd = k_cache.shape
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3 and tuple(k_new.shape[1:]) == (nkv, hd),
+          "new K/V: [T, n_kv, hd]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() >= k_new.shape[0],
+          "slot_mapping: int64 [T]")
+    _check("pa_kv_append", L.pa_kv_append(
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv, hd, _ptr(k_new),
+        _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping), k_new.shape[0], k_scale, v_scale,
+        _stream(stream)))
+
+
+def pa_decode_workspace_bytes(num_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                              max_context_len: int, split_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, n_q_heads, n_kv_heads, head_dim,
+                                               max_context_len, split_tokens))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device scratch buffer (torch's allocator aligns to 512)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+              scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+              split_tokens: int = 0, stream=None) -> torch.Tensor:
+    """Decode attention for q [B, n_q, hd] over the paged pools; returns [B, n_q, hd]."""
+    L = lib()
+    _dev(q, k_cache, v_cache, block_tables, context_lens)
+    B, nq, hd = q.shape
+    nb, bs, nkv, hd2 = k_cache.shape
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(block_tables.dtype == context_lens.dtype == torch.int32, "int32 tables / lengths")
+    _need(block_tables.shape[0] >= B and context_lens.shape[0] >= B, "one table row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    need = pa_decode_workspace_bytes(B, nq, nkv, hd, max_context_len, split_tokens)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check("pa_decode", L.pa_decode(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, max_context_len, scale, k_scale, v_scale, split_tokens, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out

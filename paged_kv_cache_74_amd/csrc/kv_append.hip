@@ -1,0 +1,220 @@
+// Slot mapping and KV append (scatter into the paged pool).
+//
+// Address map: "3.3 Batching and memory management" (llm-learning-path),
+// section "PagedAttention: the block table" -- token p of a sequence lives in
+// physical block table[p / block_size] at offset p % block_size.  Append:
+// "KV Cache: the memory bottleneck of LLM inference" (tag-page excerpt),
+// section 1.1 -- the step's new k_t, v_t are written into the cache before
+// attention reads it.
+//
+// Both kernels are tiny and latency bound (a decode step appends one token
+// per sequence).  The append kernel moves whole 16-byte (or 8-byte for fp8
+// output) pieces per lane so each row of head_dim elements is written with a
+// handful of wide, coalesced stores.
+#include "pa_device.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// slot mapping: one workgroup per segment, lanes stride over its tokens
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int64_t* __restrict__ slots, const int32_t* __restrict__ tables, int max_blocks,
+    int block_size, const int32_t* __restrict__ cu_tokens,
+    const int32_t* __restrict__ start_pos) {
+  const int s = blockIdx.x;
+  const int t0 = cu_tokens[s], t1 = cu_tokens[s + 1];
+  const int64_t p0 = start_pos[s];
+  const int32_t* row = tables + (int64_t)s * max_blocks;
+  for (int i = t0 + threadIdx.x; i < t1; i += blockDim.x) {
+    const int64_t p = p0 + (i - t0);
+    const int64_t j = p / block_size;
+    int64_t slot = -1;
+    if (p >= 0 && j < max_blocks) {
+      const int32_t blk = row[j];
+      if (blk >= 0) slot = (int64_t)blk * block_size + (p - j * block_size);
+    }
+    slots[i] = slot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// e4m3 (OCP e4m3fn) encoder: saturate to +-448, round half to even, NaN -> 0x7F.
+// Integer-only, so the result never depends on the device's float modes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = f32_bits(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                 // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;         // |x| >= 448 (and inf): saturate
+  const int e = (int)(a >> 23) - 127;                // unbiased binary32 exponent
+  const uint32_t m = (a & 0x7fffffu) | 0x800000u;    // 24-bit significand (normal input)
+  // value = m * 2^(e-23).  Normal e4m3 (e >= -6) keeps 3 fraction bits:
+  // q = m >> 20 in [8, 16); subnormal e4m3 counts units of 2^-9: q = m >> (14 - e).
+  const int shift = e >= -6 ? 20 : 14 - e;
+  if (shift >= 26) return sign;                      // below a quarter unit: +-0
+  const uint32_t q = m >> shift;
+  const uint32_t rem = m & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  const uint32_t r = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+  // Normal: code = (e + 7) * 8 + (r - 8); r == 16 carries into the exponent.
+  // Subnormal: code = r (r == 8 is the smallest normal, code 0x08).
+  const uint32_t code = e >= -6 ? (uint32_t)((e + 7) * 8) + r - 8u : r;
+  return sign | code;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte read of source rows (read once, not kept in cache).
+__device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int SRC, int DST>
+struct AppendIO;
+
+// Copies: 8 elements per lane.
+template <>
+struct AppendIO<PA_BF16, PA_BF16> {
+  static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float) {
+    *(uint4*)dst = ld_stream(src);
+  }
+};
+template <>
+struct AppendIO<PA_F32, PA_F32> {
+  static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float) {
+    const uint4 a = ld_stream(src);
+    const uint4 b = ld_stream(src + 16);
+    ((uint4*)dst)[0] = a;
+    ((uint4*)dst)[1] = b;
+  }
+};
+// Encodes: 8 elements in, 8 bytes out.
+template <>
+struct AppendIO<PA_BF16, PA_FP8_E4M3> {
+  static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float inv) {
+    const uint4 a = ld_stream(src);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = f32_to_e4m3(bf16lo_f32(w[i]) * inv);
+      const uint32_t hi = f32_to_e4m3(bf16hi_f32(w[i]) * inv);
+      out[i >> 1] |= (lo | (hi << 8)) << ((i & 1) * 16);
+    }
+    *(uint2*)dst = make_uint2(out[0], out[1]);
+  }
+};
+template <>
+struct AppendIO<PA_F32, PA_FP8_E4M3> {
+  static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float inv) {
+    const uint4 a = ld_stream(src);
+    const uint4 b = ld_stream(src + 16);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i >> 2] |= f32_to_e4m3(bits_f32(w[i]) * inv) << ((i & 3) * 8);
+    *(uint2*)dst = make_uint2(out[0], out[1]);
+  }
+};
+
+constexpr int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
+
+// One lane moves 8 elements; a row (token, head) has head_dim / 8 lanes.
+// grid.x covers num_tokens * n_kv * head_dim / 8 lanes for K, grid.y = 2 picks K or V.
+template <int SRC, int DST>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int64_t num_slots_in_pool, int lanes_per_token,
+    int64_t total_lanes, float k_inv, float v_inv) {
+  const int64_t lane = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (lane >= total_lanes) return;
+  const bool is_v = blockIdx.y != 0;
+  const int64_t tok = lane / lanes_per_token;
+  const int64_t within = lane - tok * lanes_per_token;   // which 8-element piece of the token
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots_in_pool) return;
+  constexpr int SB = elem_bytes(SRC), DB = elem_bytes(DST);
+  const int64_t tok_elems = (int64_t)lanes_per_token * 8;  // n_kv * head_dim
+  const uint8_t* src = (is_v ? v_new : k_new) + (tok * tok_elems + within * 8) * SB;
+  uint8_t* dst = (is_v ? v_cache : k_cache) + (slot * tok_elems + within * 8) * DB;
+  AppendIO<SRC, DST>::run(src, dst, is_v ? v_inv : k_inv);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent or negative sizes";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unsupported dtype or dtype pair";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim/block_size/group_size not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+extern "C" int pa_abi_version(void) { return 1; }
+
+extern "C" pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     const int32_t* cu_tokens, const int32_t* start_pos,
+                                     int32_t num_seqs, int32_t num_tokens, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || block_size < 1 || max_blocks_per_seq < 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !block_tables || !cu_tokens || !start_pos) return PA_ERR_NULL;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, (hipStream_t)stream,
+                     slot_mapping, block_tables, max_blocks_per_seq, block_size, cu_tokens,
+                     start_pos);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
+                                  int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                  int32_t head_dim, const void* k_new, const void* v_new,
+                                  int src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                                  float k_scale, float v_scale, void* stream) {
+  if (num_blocks < 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || num_tokens < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  const int lanes_per_token = n_kv_heads * head_dim / 8;
+  const int64_t total = (int64_t)num_tokens * lanes_per_token;
+  const int64_t pool_slots = (int64_t)num_blocks * block_size;
+  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* kc = (uint8_t*)k_cache;
+  uint8_t* vc = (uint8_t*)v_cache;
+  const uint8_t* kn = (const uint8_t*)k_new;
+  const uint8_t* vn = (const uint8_t*)v_new;
+  if (cache_dtype == src_dtype && cache_dtype == PA_BF16) {
+    hipLaunchKernelGGL((kv_append_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc, kn,
+                       vn, slot_mapping, pool_slots, lanes_per_token, total, 1.0f, 1.0f);
+  } else if (cache_dtype == src_dtype && cache_dtype == PA_F32) {
+    hipLaunchKernelGGL((kv_append_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc, kn,
+                       vn, slot_mapping, pool_slots, lanes_per_token, total, 1.0f, 1.0f);
+  } else if (cache_dtype == PA_FP8_E4M3 && (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f)) return PA_ERR_SHAPE;
+    const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;   // one binary32 division each
+    if (src_dtype == PA_BF16)
+      hipLaunchKernelGGL((kv_append_kernel<PA_BF16, PA_FP8_E4M3>), grid, dim3(256), 0, st, kc,
+                         vc, kn, vn, slot_mapping, pool_slots, lanes_per_token, total, k_inv,
+                         v_inv);
+    else
+      hipLaunchKernelGGL((kv_append_kernel<PA_F32, PA_FP8_E4M3>), grid, dim3(256), 0, st, kc,
+                         vc, kn, vn, slot_mapping, pool_slots, lanes_per_token, total, k_inv,
+                         v_inv);
+  } else {
+    return PA_ERR_DTYPE;
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

@@ -1,0 +1,104 @@
+// Device helpers shared by the paged-KV kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 <-> f32.  A bfloat16 is the top half of a binary32, so widening is a shift.
+__device__ __forceinline__ float bf16lo_f32(uint32_t pair) { return bits_f32(pair << 16); }
+__device__ __forceinline__ float bf16hi_f32(uint32_t pair) { return bits_f32(pair & 0xffff0000u); }
+
+// Two f32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  float2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi with bf16 pairs and f32 accumulation (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Two e4m3 codes (the low or high 16 bits of `src`) -> a bf16 pair.  Every
+// e4m3 value is exactly representable in bf16, so with a unit scale the
+// conversion is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// {a.lo16, b.lo16} and {a.hi16, b.hi16}
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+// DPP lane exchanges inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i inside each group of 8
+constexpr int DPP_ROR8 = 0x128;         // row rotate by 8: lane i <-> i^8 inside a row
+
+// Sum over the 8 lanes {8k .. 8k+7}; every lane of the group gets the total.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Reductions over the 8 lane groups that differ in lane bits 3..5.
+__device__ __forceinline__ float max_over_groups(float v) {
+  v = fmaxf(v, dpp<DPP_ROR8>(v));
+  v = fmaxf(v, shfl_xor(v, 16));
+  v = fmaxf(v, shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += dpp<DPP_ROR8>(v);
+  v += shfl_xor(v, 16);
+  v += shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Split plan of one sequence for decode: at most max_splits splits of a
+// multiple of 16 tokens, each at least min_split tokens (except the last).
+// Host and device compute it with this same function.
+__host__ __device__ __forceinline__ void decode_plan(int ctx, int max_splits, int min_split,
+                                                    int* num_splits, int* split_len) {
+  if (ctx <= 0) { *num_splits = 0; *split_len = 16; return; }
+  int ns = (ctx + min_split - 1) / min_split;
+  if (ns > max_splits) ns = max_splits;
+  int len = (ctx + ns - 1) / ns;
+  len = (len + 15) & ~15;
+  *split_len = len;
+  *num_splits = (ctx + len - 1) / len;
+}
+
+}  // namespace pa

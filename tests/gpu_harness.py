@@ -1,0 +1,82 @@
+"""GPU-side test plumbing: device pools filled through the library's own kernels.
+
+Every value written into a device pool goes through ``pa_slot_mapping`` and
+``pa_kv_append`` (the HIP path); the oracle builds its pools separately with
+``oracle.paged``.  torch is used only for device memory and streams.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_74_amd as pa
+from workloads import POISON, Workload
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
+
+
+def poison_pool(w: Workload, dev) -> torch.Tensor:
+    shape = (w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim)
+    t = torch.empty(shape, dtype=TORCH_DTYPE[w.cache_dtype], device=dev)
+    p = int(POISON[w.cache_dtype])
+    bits = {"f32": 32, "bf16": 16, "fp8": 8}[w.cache_dtype]
+    if w.cache_dtype != "fp8" and p >= 1 << (bits - 1):
+        p -= 1 << bits            # as the signed integer of the same bits
+    t.view(INT_VIEW[w.cache_dtype]).fill_(p)
+    return t
+
+
+def i32(a, dev) -> torch.Tensor:
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
+
+
+class DeviceWorkload:
+    """Device copies of a workload's tables/values plus pools built by the library."""
+
+    def __init__(self, w: Workload, dev="cuda"):
+        self.w = w
+        self.dev = dev
+        self.tables = i32(w.block_tables, dev)
+        self.ctx = i32(w.context_lens, dev)
+        self.k_cache = poison_pool(w, dev)
+        self.v_cache = poison_pool(w, dev)
+        self.q = w.q.to(dev) if w.q is not None else None
+
+    def _seg(self, start, lens, k, v):
+        w = self.w
+        cu = np.zeros(len(lens) + 1, np.int32)
+        np.cumsum(lens, out=cu[1:])
+        n = int(cu[-1])
+        slots = pa.pa_slot_mapping(self.tables, i32(cu, self.dev), i32(start, self.dev),
+                                   w.block_size, n)
+        if n:
+            pa.pa_kv_append(self.k_cache, self.v_cache, k.to(self.dev), v.to(self.dev), slots,
+                            w.k_scale, w.v_scale)
+        return slots
+
+    def append_resident(self):
+        w = self.w
+        return self._seg(w.res_start, w.res_len, w.res_k, w.res_v)
+
+    def append_new(self):
+        w = self.w
+        return self._seg(w.new_start, w.new_len, w.new_k, w.new_v)
+
+    def decode_inputs(self):
+        """q rows, tables and lengths of the decode rows (views, contiguous)."""
+        w = self.w
+        P = w.num_prefill_seqs
+        qoff = int(w.q_lens[:P].sum())
+        return self.q[qoff:], self.tables[P:], self.ctx[P:]
+
+    def decode(self, split_tokens=0, out=None, ws=None):
+        w = self.w
+        q, tables, ctx = self.decode_inputs()
+        maxc = int(w.context_lens[w.num_prefill_seqs:].max()) if len(w.decode_rows) else 0
+        return pa.pa_decode(q, self.k_cache, self.v_cache, tables, ctx, maxc, w.scale,
+                            w.k_scale, w.v_scale, out=out, ws=ws, split_tokens=split_tokens)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)

@@ -6,6 +6,7 @@ append); nothing here touches the HIP library.
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 import oracle
 from workloads import POISON, Workload
@@ -13,7 +14,6 @@ from workloads import POISON, Workload
 
 def codes(t, dtype: str) -> np.ndarray:
     """Raw element codes of a CPU/GPU torch tensor as a numpy array."""
-    import torch
     t = t.detach()
     if t.is_cuda:
         t = t.cpu()
@@ -37,16 +37,43 @@ def oracle_slots(w: Workload, which: str) -> np.ndarray:
     return oracle.paged.slot_mapping(w.block_tables, w.new_start, w.new_len, w.block_size)
 
 
-def oracle_pools(w: Workload, include_new: bool = True):
-    """Pools after appending the resident tokens (and the new ones if asked)."""
+def oracle_pools(w: Workload, include_new: bool = True, seqs=None):
+    """Pools after appending the resident tokens (and the new ones if asked).
+
+    With ``seqs`` only those sequences' tokens are appended (plus the sequence
+    that writes a shared prefix, when a listed sequence reads it).
+    """
     pk, pv = poisoned_pool(w), poisoned_pool(w)
     src = w.src_dtype
-    steps = [("res", w.res_k, w.res_v)] + ([("new", w.new_k, w.new_v)] if include_new else [])
-    for which, k, v in steps:
-        slots = oracle_slots(w, which)
-        oracle.paged.kv_append(pk, codes(k, src), slots, w.block_size, src, w.cache_dtype, w.k_scale)
-        oracle.paged.kv_append(pv, codes(v, src), slots, w.block_size, src, w.cache_dtype, w.v_scale)
+    if seqs is None:
+        seqs = list(range(w.num_seqs))
+    seqs = sorted(set(int(s) for s in seqs))
+    if w.shared_prefix_seqs and any(s in w.shared_prefix_seqs for s in seqs):
+        seqs = sorted(set(seqs) | {w.shared_prefix_seqs[0]})
+    steps = [("res", w.res_start, w.res_len, w.res_k, w.res_v)]
+    if include_new:
+        steps.append(("new", w.new_start, w.new_len, w.new_k, w.new_v))
+    for _, start, lens, k, v in steps:
+        cu = w.cu(lens)
+        idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]) if seqs else np.zeros(0, int)
+        if idx.size == 0:
+            continue
+        slots = oracle.paged.slot_mapping(w.block_tables[seqs], start[seqs], lens[seqs], w.block_size)
+        ti = torch.as_tensor(idx, device=k.device)
+        kc = codes(k.index_select(0, ti), src)
+        vc = codes(v.index_select(0, ti), src)
+        oracle.paged.kv_append(pk, kc, slots, w.block_size, src, w.cache_dtype, w.k_scale)
+        oracle.paged.kv_append(pv, vc, slots, w.block_size, src, w.cache_dtype, w.v_scale)
     return pk, pv
+
+
+def blocks_of(w: Workload, seqs) -> np.ndarray:
+    """Physical block ids read by the listed sequences."""
+    ids = []
+    for s in seqs:
+        n = -(-int(w.context_lens[s]) // w.block_size)
+        ids.extend(w.block_tables[s, :n].tolist())
+    return np.unique(np.array(ids, dtype=np.int64))
 
 
 def oracle_decode(w: Workload, pk, pv, rows=None):
