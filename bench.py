@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV decode step on one MI355X.
+
+One step = the whole hot path over one batch: slot mapping of the step's new
+tokens, KV append (scatter into the paged pool), then paged decode attention
+(split kernel + log-sum-exp merge).  Default workload: Llama-3-8B-shaped GQA
+decode -- batch 64, 32 query / 8 KV heads, head_dim 128, block 16, bf16,
+context lengths ~ U{2048..8192}, 19 sequences sharing an 800-token prefix
+through shared physical blocks, one appended token per sequence.
+
+Inputs are resident in HBM before timing.  Several copies of the pool are
+rotated so a step never finds the previous step's K/V in L2 or the MALL.
+Prints ONE JSON line on stdout (human-readable detail goes to stderr).
+
+    python bench.py [--steps K] [--warmup W] [--workload llama3-gqa|llama2|longtail|longtail-fp8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "decode paged-attn achieved HBM GB/s (% of peak) + seqs·tokens/s, 1×MI355X"
+
+WORKLOADS = {
+    "llama3-gqa": (3, "bf16"),
+    "llama2": (2, "bf16"),
+    "longtail": (4, "bf16"),
+    "longtail-fp8": (4, "fp8"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def byte_model(w):
+    """Algorithmic bytes of one step (what the method must move)."""
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    qb = {"f32": 4, "bf16": 2}[w.q_dtype]
+    sb = {"f32": 4, "bf16": 2}[w.src_dtype]
+    nkv, hd, bs = w.n_kv_heads, w.head_dim, w.block_size
+    rows = list(w.decode_rows)
+    ctx = w.context_lens[rows].astype(float)
+    kv_logical = float(ctx.sum()) * nkv * hd * 2 * eb
+    shared = max(len(w.shared_prefix_seqs) - 1, 0) * w.shared_prefix_blocks * bs
+    kv_unique = kv_logical - shared * nkv * hd * 2 * eb
+    B = len(rows)
+    q_bytes = B * w.n_q_heads * hd * qb
+    table_bytes = float(sum(math.ceil(c / bs) for c in ctx)) * 4 + B * 4
+    split = kv_unique + q_bytes + table_bytes
+    out_bytes = B * w.n_q_heads * hd * qb
+    n_new = int(w.new_len.sum())
+    append = n_new * nkv * hd * (sb + eb) * 2 + n_new * 8
+    slots = n_new * (8 + 4) + B * 8
+    return {"kv_logical": kv_logical, "kv_unique": kv_unique, "split_kernel": split,
+            "step": split + out_bytes + append + slots, "append": append}
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle, as it is, on a bounded sample of the same step (host cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tests.helpers import codes
+
+    rows = list(w.decode_rows)
+    src = w.src_dtype
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    res_cu, new_cu = w.cu(w.res_len), w.cu(w.new_len)
+    qc = codes(w.q, w.q_dtype)
+    done, t_total, nbytes = 0, 0.0, 0.0
+    poison = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F)}
+    pk = np.full((w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim), poison[w.cache_dtype])
+    pv = pk.copy()
+    with threadpool_limits(limits=1):
+        for s in rows:
+            if t_total >= budget_s:
+                break
+            seqs = [s]
+            if w.shared_prefix_seqs and s in w.shared_prefix_seqs[1:]:
+                seqs = [w.shared_prefix_seqs[0], s]
+            for r in seqs:                       # resident tokens: setup, not timed
+                a, b = res_cu[r], res_cu[r + 1]
+                sl = oracle.paged.slot_mapping(w.block_tables[[r]], w.res_start[[r]],
+                                               w.res_len[[r]], w.block_size)
+                oracle.paged.kv_append(pk, codes(w.res_k[a:b], src), sl, w.block_size, src,
+                                       w.cache_dtype, w.k_scale)
+                oracle.paged.kv_append(pv, codes(w.res_v[a:b], src), sl, w.block_size, src,
+                                       w.cache_dtype, w.v_scale)
+            nk = codes(w.new_k[new_cu[s]:new_cu[s + 1]], src)
+            nv = codes(w.new_v[new_cu[s]:new_cu[s + 1]], src)
+            qd = np.zeros((w.num_seqs,) + qc.shape[1:], qc.dtype)
+            qd[s] = qc[s]
+            t0 = time.perf_counter()               # timed: slot map + append + decode
+            sl = oracle.paged.slot_mapping(w.block_tables[[s]], w.new_start[[s]],
+                                           w.new_len[[s]], w.block_size)
+            oracle.paged.kv_append(pk, nk, sl, w.block_size, src, w.cache_dtype, w.k_scale)
+            oracle.paged.kv_append(pv, nv, sl, w.block_size, src, w.cache_dtype, w.v_scale)
+            oracle.paged.decode(qd, w.q_dtype, pk, pv, w.cache_dtype, w.block_tables,
+                                w.context_lens, w.block_size, w.group_size, w.scale, w.k_scale,
+                                w.v_scale, rows=[s])
+            t_total += time.perf_counter() - t0
+            nbytes += float(w.context_lens[s]) * w.n_kv_heads * w.head_dim * 2 * eb
+            done += 1
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of {len(rows)} sequences of the same step (slot map + append + "
+                      f"decode), {t_total:.1f} s, single thread, float64 NumPy; logical K/V bytes"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3-gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--pools", type=int, default=2, help="pool copies rotated across steps")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_74_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        # a copy kernel of known size: FETCH_SIZE / WRITE_SIZE per dispatch should
+        # read copy_calibration_mib MiB each; their ratio scales the counters
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration_mib} MiB x 3")
+        return
+    cfg, kv = WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    w = workloads.full(cfg, kv=kv)
+    workloads.draw_values(w, dev)
+    from tests.gpu_harness import DeviceWorkload, i32
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    pools = [(dw.k_cache, dw.v_cache)]
+    for _ in range(max(args.pools, 1) - 1):
+        pools.append((dw.k_cache.clone(), dw.v_cache.clone()))
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t0:.1f} s: {w.name}, {w.num_seqs} seqs, "
+        f"{w.num_blocks} blocks, pool {2 * dw.k_cache.numel() * dw.k_cache.element_size() / 2**30:.2f} GiB x {len(pools)}")
+
+    # step inputs, resident in HBM
+    q, tables, ctx = dw.decode_inputs()
+    B = q.shape[0]
+    maxc = int(w.context_lens[list(w.decode_rows)].max())
+    new_cu = i32(w.cu(w.new_len), dev)
+    new_start = i32(w.new_start, dev)
+    n_new = int(w.new_len.sum())
+    new_k, new_v = w.new_k.to(dev), w.new_v.to(dev)
+    slots = torch.empty(n_new, dtype=torch.int64, device=dev)
+    out = torch.empty_like(q)
+    ws = pa.workspace(pa.pa_decode_workspace_bytes(B, w.n_q_heads, w.n_kv_heads, w.head_dim, maxc,
+                                                   args.split_tokens), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        pa.pa_slot_mapping(dw.tables, new_cu, new_start, w.block_size, n_new, out=slots)
+        pa.pa_kv_append(kc, vc, new_k, new_v, slots, w.k_scale, w.v_scale)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode_partials(q, kc, vc, tables, ctx, maxc, w.scale, ws, w.k_scale,
+                              args.split_tokens)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.pa_decode_merge(out, ctx, w.n_kv_heads, maxc, ws, w.v_scale if w.cache_dtype == "fp8" else 1.0,
+                           args.split_tokens)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    split_ms = np.array([a.elapsed_time(b) for a, b in events])
+
+    bm = byte_model(w)
+    ms_step = wall * 1e3 / args.steps
+    step_gbs = bm["step"] / (ms_step * 1e-3) / 1e9
+    split_avg = float(split_ms.mean())
+    achieved = bm["split_kernel"] / (split_avg * 1e-3) / 1e9
+    ctx_tokens = float(w.context_lens[list(w.decode_rows)].sum())
+    log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s); split kernel avg {split_avg * 1e3:.1f} us "
+        f"(p10 {np.percentile(split_ms, 10) * 1e3:.1f}, p90 {np.percentile(split_ms, 90) * 1e3:.1f}) "
+        f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; "
+        f"KV unique {bm['kv_unique'] / 1e9:.3f} GB, logical {bm['kv_logical'] / 1e9:.3f} GB")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        w_host = w
+        for name in ("q", "res_k", "res_v", "new_k", "new_v"):
+            setattr(w_host, name, getattr(w, name).cpu())
+        cpu = cpu_baseline(w_host, args.cpu_seconds)
+        log(f"cpu baseline (oracle): {cpu['value']} GB/s, {cpu['sample']}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.cache_dtype == "bf16" else f"bf16-q/{w.cache_dtype}-kv",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: paged decode step (slot map + KV append + split-K decode + merge)",
+            "batch": B, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.cache_dtype,
+            "context_tokens": int(ctx_tokens), "max_context": maxc,
+            "shared_prefix_seqs": len(w.shared_prefix_seqs),
+            "shared_prefix_tokens": w.shared_prefix_blocks * w.block_size,
+            "appended_tokens": n_new, "pool_copies_rotated": len(pools),
+            "split_tokens": args.split_tokens or "auto",
+        },
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(B / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(ctx_tokens / (ms_step * 1e-3), 1),
+        "bytes_per_step": {"algorithmic_unique": bm["step"], "kv_unique": bm["kv_unique"],
+                           "kv_logical": bm["kv_logical"]},
+        "roofline": {
+            "kernel": "decode_split_kernel (pa_decode_partials)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(split_avg * 1e3, 2),
+            "algorithmic_bytes_per_launch": bm["split_kernel"],
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

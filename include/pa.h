@@ -173,6 +173,40 @@ pa_status pa_decode(void* out, const void* q, int q_dtype,
                     float scale, float k_scale, float v_scale, int32_t split_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_partials / pa_decode_merge -- the two phases of pa_decode, for
+ * callers that schedule them apart: timing the split kernel alone, or running
+ * the merge after partials from several devices (each holding a slice of a
+ * long context) have been gathered into one workspace.
+ *
+ * pa_decode_partials takes pa_decode's arguments minus `out` and `v_scale` and
+ * leaves, per (sequence, query head, split), the split's running maximum m
+ * (base-2 logarithm units of the scaled scores), its sum l and its
+ * unnormalised accumulator O in the workspace.  The workspace layout is
+ * private to this library version; only pa_decode_merge reads it.
+ *
+ * pa_decode_merge combines them (M = max m_k, out = out_scale * sum_k 2^{m_k-M} O_k /
+ * sum_k 2^{m_k-M} l_k; zeros for context 0) and writes `out` in out_dtype (F32
+ * or BF16).  out_scale is v_scale for FP8 caches and 1 otherwise.  It must be
+ * called with the num_seqs, head counts, head_dim, max_context_len,
+ * split_tokens and context_lens of the partials call it follows.
+ */
+pa_status pa_decode_partials(const void* q, int q_dtype,
+                             const void* k_cache, const void* v_cache, int cache_dtype,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t group_size,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len, float scale, float k_scale,
+                             int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, int32_t max_context_len, int32_t split_tokens,
+                          float out_scale, const void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

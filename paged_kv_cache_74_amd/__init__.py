@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PA_LIB") or os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
@@ -53,6 +54,9 @@ def lib():
         _c("pa_decode_workspace_bytes", S, I, I, I, I, I, I)
         _c("pa_decode", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I, P, I,
            P, I, I, F, F, F, I, P, S, P)
+        _c("pa_decode_partials", ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I,
+           P, I, P, I, I, F, F, I, P, S, P)
+        _c("pa_decode_merge", ctypes.c_int, P, ctypes.c_int, P, I, I, I, I, I, I, F, P, S, P)
     return _lib
 
 
@@ -167,4 +171,29 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         B, max_context_len, scale, k_scale, v_scale, split_tokens, _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+def pa_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                       ws, k_scale: float = 1.0, split_tokens: int = 0, stream=None) -> None:
+    """Phase 1 of pa_decode: per-split (m, l, O) partials into ``ws``."""
+    L = lib()
+    _dev(q, k_cache, v_cache, block_tables, context_lens)
+    B, nq, hd = q.shape
+    nb, bs, nkv, _ = k_cache.shape
+    _check("pa_decode_partials", L.pa_decode_partials(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv,
+        hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+        max_context_len, scale, k_scale, split_tokens, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def pa_decode_merge(out, context_lens, n_kv_heads: int, max_context_len, ws,
+                    out_scale: float = 1.0, split_tokens: int = 0, stream=None) -> torch.Tensor:
+    """Phase 2 of pa_decode: merge the partials in ``ws`` into ``out`` [B, n_q, hd]."""
+    L = lib()
+    _dev(out, context_lens)
+    B, nq, hd = out.shape
+    _check("pa_decode_merge", L.pa_decode_merge(
+        _ptr(out), _dtype_code(out), _ptr(context_lens), B, nq, n_kv_heads, hd, max_context_len,
+        split_tokens, out_scale, _ptr(ws), ws.numel(), _stream(stream)))
     return out

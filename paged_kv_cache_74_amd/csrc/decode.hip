@@ -52,22 +52,31 @@ struct DecodeLayout {
   static constexpr int QDW = F32 ? DPL : DPL / 2;       // q dwords per head per lane
 };
 
+#ifndef DECODE_LOAD_AUX
+#define DECODE_LOAD_AUX 2   // K/V loads are streamed once: non-temporal ("nt") cache policy
+#endif
+#ifndef DECODE_NBUF
+#define DECODE_NBUF 2   // K/V steps resident per wave: NBUF - 1 in flight during compute
+#endif
+
 struct DecodeArgs {
   const uint8_t* q;
   const uint8_t* k_cache;
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_o;      // [num_seqs][n_q][max_splits][HD]
-  float* part_ml;     // [num_seqs][n_q][max_splits][2]
+  const int32_t* cu_units;   // [num_seqs + 2] prefix sums of n_kv * steps(s), then the wave count
+  const int32_t* wave_start; // [num_waves][3] first (seq, kv head, step) of each wave
+  float* part_o;      // [slots][G][HD]   slot = wave + segment
+  float* part_ml;     // [slots][G][2]
   int64_t tok_stride; // bytes between consecutive tokens of a block (n_kv * ROW)
   int num_blocks;
   int block_size;
   int bs_log2;
   int n_kv;
   int max_blocks;
-  int max_splits;
-  int min_split;
+  int num_seqs;
+  int num_waves;
   float score_scale;  // scale * k_scale * log2(e)
 };
 
@@ -87,6 +96,31 @@ __device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[L::DW])
       d[4 * k + 0] = x.x; d[4 * k + 1] = x.y; d[4 * k + 2] = x.z; d[4 * k + 3] = x.w;
     } else {
       const uint2 x = *(const uint2*)(p + k * 8 * L::CHUNK);
+      d[2 * k + 0] = x.x; d[2 * k + 1] = x.y;
+    }
+  }
+}
+
+// Buffer loads: a wave-uniform descriptor (base address in scalar registers)
+// plus a per-lane 32-bit byte offset, so no 64-bit per-lane address is built.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  // 4th descriptor word for the gfx9 family: 32-bit data format, raw addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <class L>
+__device__ __forceinline__ void load_row_b(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff,
+                                           uint32_t (&d)[L::DW]) {
+#pragma unroll
+  for (int k = 0; k < L::NCHUNK; ++k) {
+    if constexpr (L::CHUNK == 16) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + k * 8 * L::CHUNK, soff, DECODE_LOAD_AUX);
+      d[4 * k + 0] = x.x; d[4 * k + 1] = x.y; d[4 * k + 2] = x.z; d[4 * k + 3] = x.w;
+    } else {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff + k * 8 * L::CHUNK, soff, DECODE_LOAD_AUX);
       d[2 * k + 0] = x.x; d[2 * k + 1] = x.y;
     }
   }
@@ -157,6 +191,30 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
   }
 }
 
+// Loads of one full 16-token step when block_size >= 16 (the step lies in one
+// block).  The same 4 * NCHUNK loads are issued on every path, so the number
+// of loads in flight is fixed and the compiler's waits stay tight.  A block id
+// outside the pool is never dereferenced (block 0 is read instead).
+// With live == false the loads are still issued (keeping the count in flight
+// fixed) but through an empty descriptor: they return zeros and touch no memory.
+template <class L>
+__device__ __forceinline__ void load_full_step(Frag<L>& f, const DecodeArgs& a,
+                                               const int32_t* table, int base, uint32_t lane_off,
+                                               bool live) {
+  const int j = base >> a.bs_log2;
+  int blk = j < a.max_blocks ? table[j] : 0;
+  blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+  const int64_t step_off = ((int64_t)blk * a.block_size + (base & (a.block_size - 1))) * a.tok_stride;
+  const int32_t step_bytes = live ? 16 * (int32_t)a.tok_stride : 0;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k_cache + step_off, step_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v_cache + step_off, step_bytes);
+  const int32_t half = 8 * (int32_t)a.tok_stride;
+  load_row_b<L>(kr, lane_off, 0, f.k[0]);
+  load_row_b<L>(kr, lane_off, half, f.k[1]);
+  load_row_b<L>(vr, lane_off, 0, f.v[0]);
+  load_row_b<L>(vr, lane_off, half, f.v[1]);
+}
+
 template <int CDT, int HD, int G>
 struct DecodeState {
   using L = DecodeLayout<CDT, HD>;
@@ -198,7 +256,7 @@ __device__ __forceinline__ void lane_scores(const DecodeState<CDT, HD, G>& st,
   }
 }
 
-template <int CDT, int HD, int G>
+template <int CDT, int HD, int G, bool MASKED>
 __device__ __forceinline__ void process_step(DecodeState<CDT, HD, G>& st,
                                              const Frag<DecodeLayout<CDT, HD>>& f, float c) {
   using L = DecodeLayout<CDT, HD>;
@@ -211,8 +269,8 @@ __device__ __forceinline__ void process_step(DecodeState<CDT, HD, G>& st,
   for (int h = 0; h < G; ++h) {
     const float t0 = sum8(s0[h]) * c;   // all 8 lanes of a token share ok[]
     const float t1 = sum8(s1[h]) * c;
-    s0[h] = f.ok[0] ? t0 : -INFINITY;
-    s1[h] = f.ok[1] ? t1 : -INFINITY;
+    s0[h] = (!MASKED || f.ok[0]) ? t0 : -INFINITY;
+    s1[h] = (!MASKED || f.ok[1]) ? t1 : -INFINITY;
     mn[h] = fmaxf(st.m[h], fmaxf(s0[h], s1[h]));
     grow |= mn[h] > st.m[h];
   }
@@ -282,22 +340,86 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
   return (k * 8 * L::CHUNK + c * L::CHUNK) / L::EB + w;
 }
 
-template <int CDT, int HD, int G>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+// ---------------------------------------------------------------------------
+// Work decomposition (balanced, deterministic)
+//
+// A unit is one 16-token step of one (sequence, KV head) segment; units are
+// ordered by (sequence, KV head, step).  With U units and W resident waves,
+// wave w processes units [floor(w U / W), floor((w+1) U / W)): every wave gets
+// the same amount of work, whatever the mix of context lengths.  A wave emits
+// one partial (m, l, O) for every segment piece it covers; the piece of wave w
+// in segment g is stored in slot w + g, which is unique because both wave and
+// segment boundaries are increasing along the unit order.  The merge kernel
+// finds the waves covering a segment from its unit range.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int steps_of(int ctx) { return ctx > 0 ? (ctx + 15) >> 4 : 0; }
+
+__device__ __forceinline__ int64_t wave_begin(int w, int64_t U, int W) {
+  return (int64_t)w * U / W;
+}
+// the wave whose unit range holds unit x (0 <= x < U)
+__device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
+  return (int)(((x + 1) * W - 1) / U);
+}
+
+// One workgroup: prefix sums of the units per sequence and each wave's start.
+__global__ __launch_bounds__(1024) void decode_prep_kernel(const int32_t* __restrict__ context_lens,
+                                                           int num_seqs, int n_kv, int num_waves,
+                                                           int32_t* __restrict__ cu_units,
+                                                           int32_t* __restrict__ wave_start) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (num_seqs + 1023) / 1024;
+  const int s0 = min(num_seqs, t * per), s1 = min(num_seqs, s0 + per);
+  int sum = 0;
+  for (int s = s0; s < s1; ++s) sum += n_kv * steps_of(context_lens[s]);
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {     // inclusive scan of the chunk sums
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int s = s0; s < s1; ++s) {
+    cu_units[s] = run;
+    run += n_kv * steps_of(context_lens[s]);
+  }
+  if (t == 1023) {
+    cu_units[num_seqs] = part[1023];
+    cu_units[num_seqs + 1] = num_waves;          // read back by the merge kernel
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int64_t U = part[1023];
+  for (int w = t; w < num_waves; w += 1024) {
+    const int64_t x = wave_begin(w, U, num_waves);
+    int lo = 0, hi = num_seqs;                    // last s with cu_units[s] <= x
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_units[mid] <= x) lo = mid; else hi = mid;
+    }
+    while (lo + 1 < num_seqs && cu_units[lo + 1] <= x) ++lo;   // skip empty sequences
+    const int st = steps_of(context_lens[lo]);
+    const int r = (int)(x - cu_units[lo]);
+    wave_start[3 * w + 0] = lo;
+    wave_start[3 * w + 1] = st > 0 ? r / st : 0;
+    wave_start[3 * w + 2] = st > 0 ? r % st : 0;
+  }
+}
+
+// Steps [st0, st1) of segment (s, kvh): online softmax, then the partial of
+// this piece into slot `slot`.
+template <int CDT, int HD, int G, int NBUF>
+__device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, int st0, int st1,
+                                           int slot) {
   using L = DecodeLayout<CDT, HD>;
   const int lane = threadIdx.x;
   const int lane_g = lane >> 3, lane_c = lane & 7;
-  int wid = blockIdx.x;
-  const int split = wid % a.max_splits;
-  wid /= a.max_splits;
-  const int kvh = wid % a.n_kv;
-  const int s = wid / a.n_kv;
   const int ctx = a.context_lens[s];
-  int ns, slen;
-  decode_plan(ctx, a.max_splits, a.min_split, &ns, &slen);
-  if (split >= ns) return;
-  const int begin = split * slen;
-  const int end = min(ctx, begin + slen);
+  const int begin = st0 * 16;
+  const int end = min(ctx, st1 * 16);
   const int n_q = a.n_kv * G;
 
   DecodeState<CDT, HD, G> st;
@@ -330,25 +452,62 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int lane_byte = lane_c * L::CHUNK;
   const float c = a.score_scale;
 
-  // two fragments in flight: compute one step while the next one loads
-  Frag<L> fa, fb;
-  int base = begin;
-  load_step<L>(fa, a, table, base, end, kvh, lane_g, lane_byte);
-  while (true) {
-    const int nb = base + 16;
-    if (nb < end) load_step<L>(fb, a, table, nb, end, kvh, lane_g, lane_byte);
-    process_step<CDT, HD, G>(st, fa, c);
-    if (nb >= end) break;
-    const int nn = nb + 16;
-    if (nn < end) load_step<L>(fa, a, table, nn, end, kvh, lane_g, lane_byte);
-    process_step<CDT, HD, G>(st, fb, c);
-    if (nn >= end) break;
-    base = nn;
+  if (a.block_size >= 16) {
+    const int n_full = (end - begin) >> 4;
+    const int tail = begin + (n_full << 4);
+    if (tail < end) {               // the ragged last step of the sequence, masked, first
+      Frag<L> t;
+      load_step<L>(t, a, table, tail, end, kvh, lane_g, lane_byte);
+      process_step<CDT, HD, G, true>(st, t, c);
+    }
+    if (n_full > 0) {
+      // NBUF fragments: NBUF - 1 steps in flight while one is computed.  Loads
+      // past the last step go through an empty descriptor, so the loop body
+      // always issues the same loads and the waits stay tight.
+      const uint32_t lane_off = (uint32_t)(kvh * L::ROW + lane_byte + lane_g * (int)a.tok_stride);
+      Frag<L> buf[NBUF];
+#pragma unroll
+      for (int d = 0; d < NBUF - 1; ++d)
+        load_full_step<L>(buf[d], a, table, begin + 16 * min(d, n_full - 1), lane_off, d < n_full);
+      int i = 0;
+      for (; i + NBUF <= n_full; i += NBUF) {   // every path issues NBUF step loads
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int pf = i + u + NBUF - 1;
+          load_full_step<L>(buf[(u + NBUF - 1) % NBUF], a, table, begin + 16 * min(pf, n_full - 1),
+                            lane_off, pf < n_full);
+          process_step<CDT, HD, G, false>(st, buf[u], c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NBUF - 1; ++u) {       // the last n_full % NBUF steps
+        const int pf = i + u + NBUF - 1;
+        load_full_step<L>(buf[(u + NBUF - 1) % NBUF], a, table, begin + 16 * min(pf, n_full - 1),
+                          lane_off, pf < n_full);
+        if (i + u < n_full) process_step<CDT, HD, G, false>(st, buf[u], c);
+      }
+    }
+  } else {
+    // blocks smaller than a step: per-lane table lookups, masked loads
+    Frag<L> fa, fb;
+    int base = begin;
+    load_step<L>(fa, a, table, base, end, kvh, lane_g, lane_byte);
+    while (true) {
+      const int nb = base + 16;
+      if (nb < end) load_step<L>(fb, a, table, nb, end, kvh, lane_g, lane_byte);
+      process_step<CDT, HD, G, true>(st, fa, c);
+      if (nb >= end) break;
+      const int nn = nb + 16;
+      if (nn < end) load_step<L>(fa, a, table, nn, end, kvh, lane_g, lane_byte);
+      process_step<CDT, HD, G, true>(st, fb, c);
+      if (nn >= end) break;
+      base = nn;
+    }
   }
 
   // merge the 8 lane groups (lane-local softmax states) of this wave
-  float* out_o = a.part_o + (((int64_t)s * n_q + (int64_t)kvh * G) * a.max_splits + split) * HD;
-  float* out_ml = a.part_ml + (((int64_t)s * n_q + (int64_t)kvh * G) * a.max_splits + split) * 2;
+  float* out_o = a.part_o + (int64_t)slot * G * HD;
+  float* out_ml = a.part_ml + (int64_t)slot * G * 2;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float M = max_over_groups(st.m[h]);
@@ -358,7 +517,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < L::DPL; ++e) ov[e] = sum_over_groups(st.o[h][e] * w);
     if (lane_g == h) {   // lanes of group h store head h
-      float* dst = out_o + (int64_t)h * a.max_splits * HD;
+      float* dst = out_o + h * HD;
 #pragma unroll
       for (int k = 0; k < L::NCHUNK; ++k) {
         const int d0 = lane_dim<L>(lane_c, k * L::EPC);
@@ -367,40 +526,76 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
           *(float4*)(dst + d0 + i) = make_float4(ov[k * L::EPC + i], ov[k * L::EPC + i + 1],
                                                  ov[k * L::EPC + i + 2], ov[k * L::EPC + i + 3]);
       }
-      if (lane_c == 0)
-        *(float2*)(out_ml + (int64_t)h * a.max_splits * 2) = make_float2(M, lsum);
+      if (lane_c == 0) *(float2*)(out_ml + 2 * h) = make_float2(M, lsum);
     }
   }
 }
 
-// One wave per (sequence, query head): combine the splits' (m, l, O).
-template <int HD, bool OUT_BF16>
+// One wave per workgroup; wave w walks its unit range segment by segment.
+template <int CDT, int HD, int G, int NBUF>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  const int w = blockIdx.x;
+  const int W = a.num_waves;
+  const int64_t U = a.cu_units[a.num_seqs];
+  const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
+  if (u0 >= u1) return;
+  int s = a.wave_start[3 * w + 0];
+  int kvh = a.wave_start[3 * w + 1];
+  int step = a.wave_start[3 * w + 2];
+  int64_t u = u0;
+  while (true) {
+    const int steps = steps_of(a.context_lens[s]);
+    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
+    decode_run<CDT, HD, G, NBUF>(a, s, kvh, step, run_end, w + s * a.n_kv + kvh);
+    u += run_end - step;
+    if (u >= u1) break;
+    step = 0;
+    if (++kvh == a.n_kv) {             // next sequence that has tokens
+      kvh = 0;
+      do { ++s; } while (steps_of(a.context_lens[s]) == 0);
+    }
+  }
+}
+
+// One wave per (sequence, query head): combine the pieces' (m, l, O).
+template <int HD, int G, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ context_lens, int n_q, int max_splits, int min_split,
-    float v_scale) {
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_units, int num_seqs,
+    int n_kv, float v_scale) {
   constexpr int DPT = HD / 64;   // dims per thread
+  const int n_q = n_kv * G;
   const int h = blockIdx.x % n_q;
   const int s = blockIdx.x / n_q;
+  const int kvh = h / G, hl = h % G;
   const int t = threadIdx.x;
-  int ns, slen;
-  decode_plan(context_lens[s], max_splits, min_split, &ns, &slen);
+  const int steps = steps_of(context_lens[s]);
   const int64_t row = (int64_t)s * n_q + h;
-  const float* po = part_o + row * max_splits * HD;
-  const float* pml = part_ml + row * max_splits * 2;
   float acc[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
   float inv = 0.0f;
-  if (ns > 0) {
+  if (steps > 0) {
+    const int64_t U = cu_units[num_seqs];
+    const int num_waves = cu_units[num_seqs + 1];
+    const int64_t g0 = (int64_t)cu_units[s] + (int64_t)kvh * steps;
+    const int g = s * n_kv + kvh;
+    const int w0 = wave_of(g0, U, num_waves), w1 = wave_of(g0 + steps - 1, U, num_waves);
+    // waves with an empty unit range (only when waves outnumber units) hold no piece
     float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, pml[2 * k]);
+    for (int w = w0; w <= w1; ++w) {
+      if (wave_begin(w, U, num_waves) >= wave_begin(w + 1, U, num_waves)) continue;
+      M = fmaxf(M, part_ml[((int64_t)(w + g) * G + hl) * 2]);
+    }
     float lsum = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const float w = fast_exp2(pml[2 * k] - M);
-      lsum = fmaf(w, pml[2 * k + 1], lsum);
+#pragma unroll 4
+    for (int w = w0; w <= w1; ++w) {
+      if (wave_begin(w, U, num_waves) >= wave_begin(w + 1, U, num_waves)) continue;
+      const int64_t sl = (int64_t)(w + g) * G + hl;
+      const float wt = fast_exp2(part_ml[sl * 2] - M);
+      lsum = fmaf(wt, part_ml[sl * 2 + 1], lsum);
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(w, po[(int64_t)k * HD + t * DPT + i], acc[i]);
+      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wt, part_o[sl * HD + t * DPT + i], acc[i]);
     }
     inv = v_scale / lsum;
   }
@@ -421,55 +616,112 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-struct HostPlan {
-  int max_splits;
-  int min_split;
-};
-
-static HostPlan host_plan(int max_context_len, int split_tokens) {
-  HostPlan p;
-  const int ctx = max_context_len > 0 ? max_context_len : 1;
-  if (split_tokens > 0) {
-    p.min_split = (split_tokens + 15) & ~15;
-    p.max_splits = (ctx + p.min_split - 1) / p.min_split;
-  } else {
-    p.min_split = 256;
-    p.max_splits = (ctx + p.min_split - 1) / p.min_split;
-    if (p.max_splits > 64) p.max_splits = 64;
-  }
-  if (p.max_splits < 1) p.max_splits = 1;
-  return p;
-}
-
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static size_t workspace_for(int num_seqs, int n_q, int head_dim, const HostPlan& p) {
-  const size_t rows = (size_t)num_seqs * n_q * p.max_splits;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+static int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+constexpr int MAX_WAVES_PER_CU = 32;   // upper bound used to size the workspace
+constexpr int64_t MAX_WAVES = 1 << 20;
+
+// Number of waves: the resident capacity of the device (auto), or one wave
+// per split_tokens tokens of the largest possible total context (for tests).
+static int64_t waves_bound(int num_seqs, int n_kv, int max_context_len, int split_tokens) {
+  if (split_tokens <= 0) return (int64_t)device_cu_count() * MAX_WAVES_PER_CU;
+  const int64_t units = (int64_t)num_seqs * n_kv * steps_of(max_context_len);
+  const int64_t per = (split_tokens + 15) / 16;
+  int64_t w = (units + per - 1) / per;
+  if (w < 1) w = 1;
+  if (w > MAX_WAVES) w = MAX_WAVES;
+  return w;
+}
+
+struct WsLayout {
+  size_t cu, ws, ml, o, total;
+};
+static WsLayout ws_layout(int num_seqs, int n_kv, int G, int head_dim, int64_t waves) {
+  WsLayout l;
+  const size_t slots = (size_t)waves + (size_t)num_seqs * n_kv;
+  l.cu = 0;
+  l.ws = l.cu + align256((size_t)(num_seqs + 2) * 4);
+  l.ml = l.ws + align256((size_t)waves * 3 * 4);
+  l.o = l.ml + align256(slots * G * 2 * 4);
+  l.total = l.o + align256(slots * G * head_dim * 4);
+  return l;
 }
 
 template <int CDT, int HD, int G>
-static void launch_split(const DecodeArgs& a, int num_seqs, hipStream_t st) {
-  const unsigned grid = (unsigned)((int64_t)a.max_splits * a.n_kv * num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G>), dim3(grid), dim3(64), 0, st, a);
+static int64_t resident_waves() {
+  static int64_t cached = 0;   // per instantiation; the device is assumed not to change
+  if (!cached) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_split_kernel<CDT, HD, G, DECODE_NBUF>, 64, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 8;
+    if (per_cu > MAX_WAVES_PER_CU) per_cu = MAX_WAVES_PER_CU;
+    cached = (int64_t)device_cu_count() * per_cu;
+  }
+  return cached;
+}
+
+template <int CDT, int HD, int G>
+static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
+  const int64_t bound = waves_bound(a.num_seqs, a.n_kv, max_context_len, split_tokens);
+  int64_t W = split_tokens > 0 ? bound : resident_waves<CDT, HD, G>();
+  if (W > bound) W = bound;
+  a.num_waves = (int)W;
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(1024), 0, st, a.context_lens, a.num_seqs,
+                     a.n_kv, a.num_waves, const_cast<int32_t*>(a.cu_units),
+                     const_cast<int32_t*>(a.wave_start));
+  hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W), dim3(64), 0,
+                     st, a);
 }
 
 template <int CDT, int HD>
-static bool dispatch_group(int G, const DecodeArgs& a, int num_seqs, hipStream_t st) {
+static bool dispatch_group(int G, const DecodeArgs& a, int split_tokens, int max_ctx, hipStream_t st) {
   switch (G) {
-    case 1: launch_split<CDT, HD, 1>(a, num_seqs, st); return true;
-    case 2: launch_split<CDT, HD, 2>(a, num_seqs, st); return true;
-    case 4: launch_split<CDT, HD, 4>(a, num_seqs, st); return true;
-    case 8: launch_split<CDT, HD, 8>(a, num_seqs, st); return true;
+    case 1: launch_split<CDT, HD, 1>(a, split_tokens, max_ctx, st); return true;
+    case 2: launch_split<CDT, HD, 2>(a, split_tokens, max_ctx, st); return true;
+    case 4: launch_split<CDT, HD, 4>(a, split_tokens, max_ctx, st); return true;
+    case 8: launch_split<CDT, HD, 8>(a, split_tokens, max_ctx, st); return true;
     default: return false;
   }
 }
 
 template <int CDT>
-static bool dispatch_hd(int hd, int G, const DecodeArgs& a, int num_seqs, hipStream_t st) {
-  if (hd == 128) return dispatch_group<CDT, 128>(G, a, num_seqs, st);
-  if (hd == 64) return dispatch_group<CDT, 64>(G, a, num_seqs, st);
+static bool dispatch_hd(int hd, int G, const DecodeArgs& a, int split_tokens, int max_ctx,
+                        hipStream_t st) {
+  if (hd == 128) return dispatch_group<CDT, 128>(G, a, split_tokens, max_ctx, st);
+  if (hd == 64) return dispatch_group<CDT, 64>(G, a, split_tokens, max_ctx, st);
   return false;
+}
+
+// The merge reads the wave count the split kernel used from the workspace.
+template <int HD, int G, bool BF16>
+static void launch_merge_t(void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
+                           int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+  const char* base = (const char*)ws;
+  hipLaunchKernelGGL((decode_merge_kernel<HD, G, BF16>), dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
+                     dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
+                     ctx, (const int32_t*)(base + l.cu), num_seqs, n_kv, out_scale);
+}
+
+template <int HD, bool BF16>
+static bool merge_g(int G, void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
+                    int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+  switch (G) {
+    case 1: launch_merge_t<HD, 1, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
+    case 2: launch_merge_t<HD, 2, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
+    case 4: launch_merge_t<HD, 4, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
+    case 8: launch_merge_t<HD, 8, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
+    default: return false;
+  }
 }
 
 }  // namespace pa
@@ -479,9 +731,101 @@ using namespace pa;
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                             int32_t n_kv_heads, int32_t head_dim,
                                             int32_t max_context_len, int32_t split_tokens) {
-  (void)n_kv_heads;
-  if (num_seqs <= 0 || n_q_heads <= 0 || head_dim <= 0) return 0;
-  return workspace_for(num_seqs, n_q_heads, head_dim, host_plan(max_context_len, split_tokens));
+  if (num_seqs <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      n_q_heads % n_kv_heads)
+    return 0;
+  const int G = n_q_heads / n_kv_heads;
+  const int64_t W = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
+  return ws_layout(num_seqs, n_kv_heads, G, head_dim, W).total;
+}
+
+static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int head_dim,
+                              int max_context_len, int split_tokens) {
+  if (num_seqs < 0 || n_kv_heads < 1 || group_size < 1 || max_context_len < 0 || split_tokens < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
+    return PA_ERR_UNSUPPORTED;
+  // units are counted in 32-bit integers
+  if ((int64_t)num_seqs * n_kv_heads * steps_of(max_context_len) >= (int64_t)1 << 31)
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+static pa_status launch_merge(void* out, int out_dtype, const int32_t* context_lens, int num_seqs,
+                              int n_kv, int G, int head_dim, const WsLayout& l, float out_scale,
+                              const void* workspace, hipStream_t st) {
+  bool ok;
+  if (out_dtype == PA_BF16)
+    ok = head_dim == 128 ? merge_g<128, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
+                         : merge_g<64, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
+  else
+    ok = head_dim == 128 ? merge_g<128, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
+                         : merge_g<64, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
+  if (!ok) return PA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Both phases of decode; merge == false runs the partials phase only.
+static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
+                             const void* k_cache, const void* v_cache, int cache_dtype,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t group_size, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t max_context_len, float scale,
+                             float k_scale, float v_scale, int32_t split_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len, split_tokens);
+  if (e != PA_OK) return e;
+  if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
+  const bool pair_ok = (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
+                       (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3));
+  if (!pair_ok) return PA_ERR_DTYPE;
+  if (num_seqs == 0) return PA_OK;
+  if ((merge && !out) || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL;
+  const int G = group_size;
+  const int64_t bound = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
+  const WsLayout l = ws_layout(num_seqs, n_kv_heads, G, head_dim, bound);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
+
+  char* base = (char*)workspace;
+  DecodeArgs a;
+  a.q = (const uint8_t*)q;
+  a.k_cache = (const uint8_t*)k_cache;
+  a.v_cache = (const uint8_t*)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_units = (const int32_t*)(base + l.cu);
+  a.wave_start = (const int32_t*)(base + l.ws);
+  a.part_ml = (float*)(base + l.ml);
+  a.part_o = (float*)(base + l.o);
+  const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
+  a.tok_stride = (int64_t)n_kv_heads * head_dim * eb;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  a.bs_log2 = lg;
+  a.n_kv = n_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_waves = 0;
+  a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+
+  hipStream_t st = (hipStream_t)stream;
+  bool ok = false;
+  if (cache_dtype == PA_BF16) ok = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (cache_dtype == PA_FP8_E4M3) ok = dispatch_hd<PA_FP8_E4M3>(head_dim, G, a, split_tokens, max_context_len, st);
+  else ok = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
+  if (!ok) return PA_ERR_UNSUPPORTED;
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (!merge) return PA_OK;
+  return launch_merge(out, q_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
+                      fp8 ? v_scale : 1.0f, workspace, st);
 }
 
 extern "C" pa_status pa_decode(void* out, const void* q, int q_dtype, const void* k_cache,
@@ -492,71 +836,41 @@ extern "C" pa_status pa_decode(void* out, const void* q, int q_dtype, const void
                                int32_t num_seqs, int32_t max_context_len, float scale,
                                float k_scale, float v_scale, int32_t split_tokens,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || num_blocks < 0 || n_kv_heads < 1 || group_size < 1 ||
-      max_blocks_per_seq < 0 || max_context_len < 0 || split_tokens < 0)
-    return PA_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
-  if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
-    return PA_ERR_UNSUPPORTED;
-  const bool pair_ok = (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
-                       (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3));
-  if (!pair_ok) return PA_ERR_DTYPE;
+  return decode_impl(out, true, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, n_kv_heads, head_dim, group_size, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
+                     v_scale, split_tokens, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_partials(const void* q, int q_dtype, const void* k_cache,
+                                        const void* v_cache, int cache_dtype, int32_t num_blocks,
+                                        int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                                        int32_t group_size, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t max_context_len, float scale,
+                                        float k_scale, int32_t split_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return decode_impl(nullptr, false, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, n_kv_heads, head_dim, group_size, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
+                     1.0f, split_tokens, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t max_context_len,
+                                     int32_t split_tokens, float out_scale, const void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads) return PA_ERR_SHAPE;
+  const int G = n_q_heads / n_kv_heads;
+  pa_status e = check_common(num_seqs, n_kv_heads, G, head_dim, max_context_len, split_tokens);
+  if (e != PA_OK) return e;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
-  const int n_q = n_kv_heads * group_size;
-  const HostPlan plan = host_plan(max_context_len, split_tokens);
-  const size_t need = workspace_for(num_seqs, n_q, head_dim, plan);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
-  const bool fp8 = cache_dtype == PA_FP8_E4M3;
-  if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
-
-  DecodeArgs a;
-  a.q = (const uint8_t*)q;
-  a.k_cache = (const uint8_t*)k_cache;
-  a.v_cache = (const uint8_t*)v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  const size_t rows = (size_t)num_seqs * n_q * plan.max_splits;
-  a.part_o = (float*)workspace;
-  a.part_ml = (float*)((char*)workspace + align256(rows * head_dim * sizeof(float)));
-  const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
-  a.tok_stride = (int64_t)n_kv_heads * head_dim * eb;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  int lg = 0;
-  while ((1 << lg) < block_size) ++lg;
-  a.bs_log2 = lg;
-  a.n_kv = n_kv_heads;
-  a.max_blocks = max_blocks_per_seq;
-  a.max_splits = plan.max_splits;
-  a.min_split = plan.min_split;
-  a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
-
-  hipStream_t st = (hipStream_t)stream;
-  bool ok = false;
-  if (cache_dtype == PA_BF16) ok = dispatch_hd<PA_BF16>(head_dim, group_size, a, num_seqs, st);
-  else if (cache_dtype == PA_FP8_E4M3) ok = dispatch_hd<PA_FP8_E4M3>(head_dim, group_size, a, num_seqs, st);
-  else ok = dispatch_hd<PA_F32>(head_dim, group_size, a, num_seqs, st);
-  if (!ok) return PA_ERR_UNSUPPORTED;
-  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-
-  const unsigned mgrid = (unsigned)((int64_t)num_seqs * n_q);
-  const float vs = fp8 ? v_scale : 1.0f;
-  if (q_dtype == PA_BF16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<128, true>), dim3(mgrid), dim3(64), 0, st, out,
-                         a.part_o, a.part_ml, context_lens, n_q, plan.max_splits, plan.min_split, vs);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<64, true>), dim3(mgrid), dim3(64), 0, st, out,
-                         a.part_o, a.part_ml, context_lens, n_q, plan.max_splits, plan.min_split, vs);
-  } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<128, false>), dim3(mgrid), dim3(64), 0, st, out,
-                         a.part_o, a.part_ml, context_lens, n_q, plan.max_splits, plan.min_split, vs);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<64, false>), dim3(mgrid), dim3(64), 0, st, out,
-                         a.part_o, a.part_ml, context_lens, n_q, plan.max_splits, plan.min_split, vs);
-  }
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  if (!out || !context_lens) return PA_ERR_NULL;
+  const int64_t bound = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
+  const WsLayout l = ws_layout(num_seqs, n_kv_heads, G, head_dim, bound);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
+  return launch_merge(out, out_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
+                      out_scale, workspace, (hipStream_t)stream);
 }

@@ -161,7 +161,7 @@ extern "C" const char* pa_status_string(int status) {
   }
 }
 
-extern "C" int pa_abi_version(void) { return 1; }
+extern "C" int pa_abi_version(void) { return 2; }
 
 extern "C" pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                                      int32_t max_blocks_per_seq, int32_t block_size,

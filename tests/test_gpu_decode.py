@@ -217,3 +217,21 @@ def test_full_size_decode_sampled(dev, cfg, kv):
     P = w.num_prefill_seqs
     got = to_f64(out)[[r - P for r in rows]]
     check_close(got, ref, w.q_dtype, f"full cfg{cfg}/{kv}")
+
+
+def test_decode_phases_equal_one_call(dev):
+    """pa_decode_partials + pa_decode_merge == pa_decode, bit for bit."""
+    import paged_kv_cache_74_amd as pa
+    from gpu_harness import DeviceWorkload
+    w = _small(4, "fp8")
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    one = dw.decode().clone()
+    q, tables, ctx = dw.decode_inputs()
+    maxc = int(w.context_lens.max())
+    ws = pa.workspace(pa.pa_decode_workspace_bytes(q.shape[0], w.n_q_heads, w.n_kv_heads,
+                                                   w.head_dim, maxc), dev)
+    pa.pa_decode_partials(q, dw.k_cache, dw.v_cache, tables, ctx, maxc, w.scale, ws, w.k_scale)
+    two = pa.pa_decode_merge(torch.empty_like(q), ctx, w.n_kv_heads, maxc, ws, w.v_scale)
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
