@@ -65,8 +65,7 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* cu_units;   // [num_seqs + 2] prefix sums of n_kv * steps(s), then the wave count
-  const int32_t* wave_start; // [num_waves][3] first (seq, kv head, step) of each wave
+  int32_t* header;           // the wave count, written by the split kernel for the merge
   float* part_o;      // [slots][G][HD]   slot = wave + segment
   float* part_ml;     // [slots][G][2]
   int64_t tok_stride; // bytes between consecutive tokens of a block (n_kv * ROW)
@@ -362,51 +361,50 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
   return (int)(((x + 1) * W - 1) / U);
 }
 
-// One workgroup: prefix sums of the units per sequence and each wave's start.
-__global__ __launch_bounds__(1024) void decode_prep_kernel(const int32_t* __restrict__ context_lens,
-                                                           int num_seqs, int n_kv, int num_waves,
-                                                           int32_t* __restrict__ cu_units,
-                                                           int32_t* __restrict__ wave_start) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
-  const int per = (num_seqs + 1023) / 1024;
-  const int s0 = min(num_seqs, t * per), s1 = min(num_seqs, s0 + per);
-  int sum = 0;
-  for (int s = s0; s < s1; ++s) sum += n_kv * steps_of(context_lens[s]);
-  part[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {     // inclusive scan of the chunk sums
-    const int v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+// Units of the sequences before `s` (pre) and in total (all), one pass of the
+// wave over context_lens.
+__device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int num_seqs, int n_kv,
+                                            int s, int* pre, int* all) {
+  int a = 0, b = 0;
+  for (int i = threadIdx.x; i < num_seqs; i += 64) {
+    const int v = n_kv * steps_of(ctx[i]);
+    b += v;
+    if (i < s) a += v;
   }
-  int run = part[t] - sum;
-  for (int s = s0; s < s1; ++s) {
-    cu_units[s] = run;
-    run += n_kv * steps_of(context_lens[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
   }
-  if (t == 1023) {
-    cu_units[num_seqs] = part[1023];
-    cu_units[num_seqs + 1] = num_waves;          // read back by the merge kernel
-  }
-  __threadfence_block();
-  __syncthreads();
-  const int64_t U = part[1023];
-  for (int w = t; w < num_waves; w += 1024) {
-    const int64_t x = wave_begin(w, U, num_waves);
-    int lo = 0, hi = num_seqs;                    // last s with cu_units[s] <= x
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cu_units[mid] <= x) lo = mid; else hi = mid;
+  *pre = a;
+  *all = b;
+}
+
+// The sequence holding unit x (0 <= x < U) and the units before it.
+__device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int num_seqs, int n_kv,
+                                            int x, int* seq, int* before) {
+  const int lane = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < num_seqs; base += 64) {
+    const int i = base + lane;
+    const int v = i < num_seqs ? n_kv * steps_of(ctx[i]) : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
     }
-    while (lo + 1 < num_seqs && cu_units[lo + 1] <= x) ++lo;   // skip empty sequences
-    const int st = steps_of(context_lens[lo]);
-    const int r = (int)(x - cu_units[lo]);
-    wave_start[3 * w + 0] = lo;
-    wave_start[3 * w + 1] = st > 0 ? r / st : 0;
-    wave_start[3 * w + 2] = st > 0 ? r % st : 0;
+    const uint64_t hit = __ballot(carry + incl > x);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      *seq = base + l;
+      *before = carry + __shfl(incl - v, l, 64);
+      return;
+    }
+    carry += __shfl(incl, 63, 64);
   }
+  *seq = num_seqs - 1;   // not reached for x < U
+  *before = carry;
 }
 
 // Steps [st0, st1) of segment (s, kvh): online softmax, then the partial of
@@ -536,12 +534,17 @@ template <int CDT, int HD, int G, int NBUF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int w = blockIdx.x;
   const int W = a.num_waves;
-  const int64_t U = a.cu_units[a.num_seqs];
+  int pre, U;
+  unit_counts(a.context_lens, a.num_seqs, a.n_kv, 0, &pre, &U);
+  if (w == 0 && threadIdx.x == 0) *a.header = W;   // for the merge
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
-  int s = a.wave_start[3 * w + 0];
-  int kvh = a.wave_start[3 * w + 1];
-  int step = a.wave_start[3 * w + 2];
+  int s, before;
+  locate_unit(a.context_lens, a.num_seqs, a.n_kv, (int)u0, &s, &before);
+  const int steps0 = steps_of(a.context_lens[s]);
+  const int r = (int)u0 - before;
+  int kvh = r / steps0;
+  int step = r % steps0;
   int64_t u = u0;
   while (true) {
     const int steps = steps_of(a.context_lens[s]);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 template <int HD, int G, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_units, int num_seqs,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ header, int num_seqs,
     int n_kv, float v_scale) {
   constexpr int DPT = HD / 64;   // dims per thread
   const int n_q = n_kv * G;
@@ -575,27 +578,31 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
   float inv = 0.0f;
+  int pre, Ui;
+  unit_counts(context_lens, num_seqs, n_kv, s, &pre, &Ui);
   if (steps > 0) {
-    const int64_t U = cu_units[num_seqs];
-    const int num_waves = cu_units[num_seqs + 1];
-    const int64_t g0 = (int64_t)cu_units[s] + (int64_t)kvh * steps;
+    const int64_t U = Ui;
+    const int num_waves = *header;
+    const int64_t g0 = (int64_t)pre + (int64_t)kvh * steps;
     const int g = s * n_kv + kvh;
     const int w0 = wave_of(g0, U, num_waves), w1 = wave_of(g0 + steps - 1, U, num_waves);
-    // waves with an empty unit range (only when waves outnumber units) hold no piece
-    float M = -INFINITY;
-    for (int w = w0; w <= w1; ++w) {
-      if (wave_begin(w, U, num_waves) >= wave_begin(w + 1, U, num_waves)) continue;
-      M = fmaxf(M, part_ml[((int64_t)(w + g) * G + hl) * 2]);
-    }
-    float lsum = 0.0f;
+    // one pass, online over the pieces (waves with an empty unit range, which
+    // occur only when waves outnumber units, hold no piece)
+    float M = -INFINITY, lsum = 0.0f;
 #pragma unroll 4
     for (int w = w0; w <= w1; ++w) {
       if (wave_begin(w, U, num_waves) >= wave_begin(w + 1, U, num_waves)) continue;
       const int64_t sl = (int64_t)(w + g) * G + hl;
-      const float wt = fast_exp2(part_ml[sl * 2] - M);
-      lsum = fmaf(wt, part_ml[sl * 2 + 1], lsum);
+      const float2 ml = *(const float2*)(part_ml + sl * 2);
+      float o[DPT];
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wt, part_o[sl * HD + t * DPT + i], acc[i]);
+      for (int i = 0; i < DPT; ++i) o[i] = part_o[sl * HD + t * DPT + i];
+      const float Mn = fmaxf(M, ml.x);
+      const float a = fast_exp2(M - Mn), b = fast_exp2(ml.x - Mn);
+      lsum = lsum * a + ml.y * b;
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) acc[i] = acc[i] * a + o[i] * b;
+      M = Mn;
     }
     inv = v_scale / lsum;
   }
@@ -642,14 +649,13 @@ static int64_t waves_bound(int num_seqs, int n_kv, int max_context_len, int spli
 }
 
 struct WsLayout {
-  size_t cu, ws, ml, o, total;
+  size_t hdr, ml, o, total;
 };
 static WsLayout ws_layout(int num_seqs, int n_kv, int G, int head_dim, int64_t waves) {
   WsLayout l;
   const size_t slots = (size_t)waves + (size_t)num_seqs * n_kv;
-  l.cu = 0;
-  l.ws = l.cu + align256((size_t)(num_seqs + 2) * 4);
-  l.ml = l.ws + align256((size_t)waves * 3 * 4);
+  l.hdr = 0;
+  l.ml = 256;
   l.o = l.ml + align256(slots * G * 2 * 4);
   l.total = l.o + align256(slots * G * head_dim * 4);
   return l;
@@ -676,9 +682,6 @@ static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hi
   int64_t W = split_tokens > 0 ? bound : resident_waves<CDT, HD, G>();
   if (W > bound) W = bound;
   a.num_waves = (int)W;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(1024), 0, st, a.context_lens, a.num_seqs,
-                     a.n_kv, a.num_waves, const_cast<int32_t*>(a.cu_units),
-                     const_cast<int32_t*>(a.wave_start));
   hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W), dim3(64), 0,
                      st, a);
 }
@@ -709,7 +712,7 @@ static void launch_merge_t(void* out, const WsLayout& l, const void* ws, const i
   const char* base = (const char*)ws;
   hipLaunchKernelGGL((decode_merge_kernel<HD, G, BF16>), dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
                      dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
-                     ctx, (const int32_t*)(base + l.cu), num_seqs, n_kv, out_scale);
+                     ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale);
 }
 
 template <int HD, bool BF16>
@@ -799,8 +802,7 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.v_cache = (const uint8_t*)v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.cu_units = (const int32_t*)(base + l.cu);
-  a.wave_start = (const int32_t*)(base + l.ws);
+  a.header = (int32_t*)(base + l.hdr);
   a.part_ml = (float*)(base + l.ml);
   a.part_o = (float*)(base + l.o);
   const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
