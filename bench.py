@@ -34,11 +34,22 @@ WORKLOADS = {
     "llama2": (2, "bf16"),
     "longtail": (4, "bf16"),
     "longtail-fp8": (4, "fp8"),
+    "mixed": (5, "bf16"),
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(w):
+    """4 * head_dim * n_q_heads flops per visible (query, key) pair (QK^T and PV)."""
+    pairs = 0
+    for s in range(w.num_prefill_seqs):
+        L, T = int(w.q_lens[s]), int(w.context_lens[s])
+        pairs += L * (T - L) + L * (L + 1) // 2 if w.causal else L * T
+    return 4.0 * w.head_dim * w.n_q_heads * pairs
 
 
 def byte_model(w):
@@ -212,10 +223,25 @@ def main():
                                                    args.split_tokens), dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    P = w.num_prefill_seqs
+    if P:
+        pf_cu = i32(w.cu(w.q_lens[:P]), dev)
+        pf_q = dw.q[: int(w.q_lens[:P].sum())]
+        pf_out = torch.empty_like(pf_q)
+        pf_maxq, pf_maxc = int(w.q_lens[:P].max()), int(w.context_lens[:P].max())
+
+    def step(i, ev=None, pev=None):
         kc, vc = pools[i % len(pools)]
         pa.pa_slot_mapping(dw.tables, new_cu, new_start, w.block_size, n_new, out=slots)
         pa.pa_kv_append(kc, vc, new_k, new_v, slots, w.k_scale, w.v_scale)
+        if P:
+            if pev is not None:
+                pev[0].record(stream)
+            pa.pa_prefill_chunk(pf_q, kc, vc, pf_cu, dw.tables[:P], dw.ctx[:P], pf_maxq, pf_maxc,
+                                w.scale, causal=True, k_scale=w.k_scale, v_scale=w.v_scale,
+                                out=pf_out)
+            if pev is not None:
+                pev[1].record(stream)
         if ev is not None:
             ev[0].record(stream)
         pa.pa_decode_partials(q, kc, vc, tables, ctx, maxc, w.scale, ws, w.k_scale,
@@ -238,11 +264,14 @@ def main():
     # around the split kernel -> its average launch duration (roofline)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
+    pevents = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, events[i], pevents[i])
     torch.cuda.synchronize()
     split_ms = np.array([a.elapsed_time(b) for a, b in events])
+    prefill_ms = np.array([a.elapsed_time(b) for a, b in pevents]) if P else None
 
     bm = byte_model(w)
     ms_step = wall * 1e3 / args.steps
@@ -255,8 +284,20 @@ def main():
         f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; "
         f"KV unique {bm['kv_unique'] / 1e9:.3f} GB, logical {bm['kv_logical'] / 1e9:.3f} GB")
 
+    prefill_rec = None
+    if P:
+        fl = prefill_flops(w)
+        pf_avg = float(prefill_ms.mean())
+        tf = fl / (pf_avg * 1e-3) / 1e12
+        prefill_rec = {"kernel": "prefill_kernel (pa_prefill_chunk)", "bound": "mfma",
+                       "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                       "avg_launch_us": round(pf_avg * 1e3, 2), "flops_per_launch": fl}
+        log(f"prefill avg {pf_avg * 1e3:.1f} us -> {tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
+            f"of the bf16 MFMA peak ({fl / 1e9:.1f} GFLOP)")
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not P:
         w_host = w
         for name in ("q", "res_k", "res_v", "new_k", "new_v"):
             setattr(w_host, name, getattr(w, name).cpu())
@@ -304,6 +345,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if prefill_rec:
+        rec["prefill_roofline"] = prefill_rec
     print(json.dumps(rec), flush=True)
 
 

@@ -174,6 +174,47 @@ pa_status pa_decode(void* out, const void* q, int q_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill_workspace_bytes -- scratch needed by pa_prefill_chunk (may be 0).
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len);
+
+/*
+ * pa_prefill_chunk -- attention of ragged query chunks over the paged cache.
+ *   Source: "3.3 Batching and memory management", section "Chunked prefill"
+ *   (a chunk's queries attend to a cache that already holds the earlier
+ *   chunks); "From PagedAttention to Chunked Prefill", section 3.2 (one batch
+ *   of rows with different query lengths, located by cumulative offsets) and
+ *   section 2.2 (online softmax over key blocks); addressing as in pa_decode.
+ *
+ *   Chunk s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) (L_s rows);
+ *   its cache holds T_s = context_lens[s] tokens, the chunk's own K/V included
+ *   (appended first).  Query row i of the chunk sits at position T_s - L_s + i
+ *   and attends to keys j <= T_s - L_s + i when causal != 0, to all j < T_s
+ *   otherwise:
+ *     out[row][h][:] = sum_j softmax_j(scale * q[row][h] . K_s[j][h/g]) V_s[j][h/g][:].
+ *   A decode row is the special case L_s = 1.
+ *
+ *   out, q        [total_q][n_q_heads][head_dim] bf16 (q_dtype must be BF16)
+ *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[num_seqs] == total_q
+ *   max_q_len     host-side upper bound of the L_s
+ *   cache_dtype   BF16 or FP8_E4M3 (codes times k_scale / v_scale)
+ *   head_dim      64 or 128; block_size a power of two in [1, 256];
+ *   group_size    1, 2, 4 or 8
+ *   workspace     at least pa_prefill_workspace_bytes(...) bytes (may be NULL if 0)
+ */
+pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
+                           const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                           int32_t max_q_len, const void* k_cache, const void* v_cache,
+                           int cache_dtype, int32_t num_blocks, int32_t block_size,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t group_size,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           int32_t causal, float scale, float k_scale, float v_scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_partials / pa_decode_merge -- the two phases of pa_decode, for
  * callers that schedule them apart: timing the split kernel alone, or running
  * the merge after partials from several devices (each holding a slice of a

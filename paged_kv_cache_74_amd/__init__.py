@@ -57,6 +57,9 @@ def lib():
         _c("pa_decode_partials", ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I,
            P, I, P, I, I, F, F, I, P, S, P)
         _c("pa_decode_merge", ctypes.c_int, P, ctypes.c_int, P, I, I, I, I, I, I, F, P, S, P)
+        _c("pa_prefill_workspace_bytes", S, I, I, I, I, I, I, I)
+        _c("pa_prefill_chunk", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, ctypes.c_int, I, I,
+           I, I, I, P, I, P, I, I, F, F, F, P, S, P)
     return _lib
 
 
@@ -196,4 +199,40 @@ def pa_decode_merge(out, context_lens, n_kv_heads: int, max_context_len, ws,
     _check("pa_decode_merge", L.pa_decode_merge(
         _ptr(out), _dtype_code(out), _ptr(context_lens), B, nq, n_kv_heads, hd, max_context_len,
         split_tokens, out_scale, _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def pa_prefill_workspace_bytes(num_seqs: int, total_q: int, max_q_len: int, n_q_heads: int,
+                               n_kv_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(lib().pa_prefill_workspace_bytes(num_seqs, total_q, max_q_len, n_q_heads,
+                                                n_kv_heads, head_dim, max_context_len))
+
+
+def pa_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     cu_seqlens_q: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
+                     scale: float, causal: bool = True, k_scale: float = 1.0,
+                     v_scale: float = 1.0, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Ragged chunk attention: q [total_q, n_q, hd] -> out of the same shape."""
+    L = lib()
+    _dev(q, k_cache, v_cache, cu_seqlens_q, block_tables, context_lens)
+    total_q, nq, hd = q.shape
+    nb, bs, nkv, hd2 = k_cache.shape
+    B = cu_seqlens_q.numel() - 1
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(cu_seqlens_q.dtype == block_tables.dtype == context_lens.dtype == torch.int32, "int32")
+    _need(block_tables.shape[0] >= B and context_lens.shape[0] >= B, "one table row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    need = pa_prefill_workspace_bytes(B, total_q, max_q_len, nq, nkv, hd, max_context_len)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    _check("pa_prefill_chunk", L.pa_prefill_chunk(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(cu_seqlens_q), B, total_q, max_q_len,
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv, hd, nq // nkv,
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), max_context_len,
+        1 if causal else 0, scale, k_scale, v_scale, _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
     return out

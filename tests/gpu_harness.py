@@ -80,3 +80,16 @@ class DeviceWorkload:
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def prefill(dw: DeviceWorkload, causal=None):
+    """pa_prefill_chunk over the prefill rows [0, num_prefill_seqs) of the workload."""
+    w = dw.w
+    P = w.num_prefill_seqs
+    cu = w.cu(w.q_lens[:P])
+    q = dw.q[: int(cu[-1])]
+    return pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(cu, dw.dev), dw.tables[:P],
+                               dw.ctx[:P], int(w.q_lens[:P].max()),
+                               int(w.context_lens[:P].max()), w.scale,
+                               causal=w.causal if causal is None else causal,
+                               k_scale=w.k_scale, v_scale=w.v_scale)

@@ -1,0 +1,117 @@
+"""GPU parity of the chunked-prefill kernel (MFMA) against the oracle.
+
+Bars: bf16 / fp8-KV outputs within 2e-2 absolute and 1e-2 normwise relative
+error per row; a chunk of length 1 must agree with the decode kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import oracle_pools, oracle_prefill
+from test_gpu_decode import check_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import paged_kv_cache_74_amd as pa
+    pa.lib()
+    return "cuda"
+
+
+def _run(w, dev, causal=True):
+    from gpu_harness import DeviceWorkload, prefill, to_f64
+    w.causal = causal
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    got = to_f64(prefill(dw))
+    pk, pv = oracle_pools(w)
+    ref = oracle_prefill(w, pk, pv)
+    return got, ref
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_small_config(dev, causal):
+    w = workloads.draw_values(workloads.small(5), "cpu")
+    got, ref = _run(w, dev, causal)
+    check_close(got, ref, "bf16", f"prefill causal={causal}")
+
+
+# (n_q, n_kv, head_dim, block_size): every group size, both head dims, small and large blocks
+SHAPES = [(4, 4, 128, 16), (8, 4, 64, 16), (16, 2, 128, 32), (32, 8, 64, 4), (8, 1, 128, 1)]
+
+
+@pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES)
+def test_prefill_shapes(dev, nq, nkv, hd, bs):
+    w = workloads.mixed_prefill_decode(prior=(0, 40, 300, 1), chunk_lens=(50, 130, 33, 1),
+                                       n_decode=2, dlo=1, dhi=90, seed=7, n_q=nq, n_kv=nkv,
+                                       hd=hd, bs=bs)
+    workloads.draw_values(w, "cpu")
+    got, ref = _run(w, dev)
+    check_close(got, ref, "bf16", f"prefill {nq}/{nkv}/{hd}/bs{bs}")
+
+
+def test_prefill_fp8_cache(dev):
+    w = workloads.mixed_prefill_decode(prior=(0, 77, 700), chunk_lens=(64, 100, 37), n_decode=3,
+                                       dlo=1, dhi=200, seed=2, kv="fp8")
+    workloads.draw_values(w, "cpu")
+    got, ref = _run(w, dev)
+    check_close(got, ref, "bf16", "prefill fp8")
+
+
+def test_prefill_peaked_scores(dev):
+    w = workloads.draw_values(workloads.small(5, seed=4), "cpu")
+    w.q = w.q * 16
+    got, ref = _run(w, dev)
+    check_close(got, ref, "bf16", "prefill peaked")
+
+
+def test_prefill_length_one_matches_decode(dev):
+    """Decode rows run through the chunk kernel (L = 1) agree with pa_decode."""
+    import paged_kv_cache_74_amd as pa
+    from gpu_harness import DeviceWorkload, i32, to_f64
+    w = workloads.draw_values(workloads.small(3), "cpu")
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    dec = to_f64(dw.decode())
+    B = w.num_seqs
+    pf = to_f64(pa.pa_prefill_chunk(dw.q, dw.k_cache, dw.v_cache, i32(np.arange(B + 1), dev),
+                                    dw.tables, dw.ctx, 1, int(w.context_lens.max()), w.scale))
+    assert np.abs(pf - dec).max() <= 1e-2
+    pk, pv = oracle_pools(w)
+    from helpers import oracle_decode
+    check_close(pf, oracle_decode(w, pk, pv), "bf16", "prefill L=1")
+
+
+def test_prefill_full_size_sampled(dev):
+    """The full mixed-step chunks (contexts 512 .. 33280), sampled rows of each chunk."""
+    from gpu_harness import DeviceWorkload, prefill, to_f64
+    print("full-size prefill", flush=True)
+    w = workloads.full(5)
+    workloads.draw_values(w, dev)
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    got = to_f64(prefill(dw))
+    torch.cuda.synchronize()
+    import oracle
+    from helpers import codes
+    P = w.num_prefill_seqs
+    cu = w.cu(w.q_lens[:P])
+    pk, pv = oracle_pools(w, seqs=range(P))
+    rng = np.random.default_rng(0)
+    qc = codes(w.q, "bf16")
+    for s in range(P):
+        # a few query rows of the chunk, each checked as a chunk of its own
+        for i in sorted(set([0, int(w.q_lens[s]) - 1] + list(rng.integers(0, w.q_lens[s], 2)))):
+            row = int(cu[s]) + i
+            T = int(w.context_lens[s]) - int(w.q_lens[s]) + i + 1
+            ref = oracle.paged.prefill_chunk(qc[row:row + 1], "bf16", np.array([0, 1]), pk, pv,
+                                             "bf16", w.block_tables[s:s + 1], np.array([T]),
+                                             w.block_size, w.group_size, w.scale, True)
+            check_close(got[row:row + 1], ref, "bf16", f"full prefill seq {s} row {i}")

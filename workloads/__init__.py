@@ -262,24 +262,25 @@ def long_tail_decode(batch=256, median=1024, sigma=1.0, lo=16, hi=131072, n_long
 
 
 def mixed_prefill_decode(prior=(0, 2048, 8192, 32768), chunk=512, n_decode=128,
-                         dlo=512, dhi=8192, seed=0, chunk_lens=None) -> Workload:
+                         dlo=512, dhi=8192, seed=0, chunk_lens=None, n_q=32, n_kv=8, hd=128,
+                         bs=16, kv="bf16") -> Workload:
     """Chunked-prefill step: prefill chunks (rows first) plus single-token decodes."""
     rng = np.random.default_rng(seed)
     prior = np.asarray(prior, np.int32)
     L = np.asarray(chunk_lens if chunk_lens is not None else [chunk] * len(prior), np.int32)
     dctx = rng.integers(dlo, dhi + 1, size=n_decode).astype(np.int32)
     ctx = np.concatenate([prior + L, dctx]).astype(np.int32)
-    tables, nb = _assign_blocks(rng, ctx, 16)
+    tables, nb = _assign_blocks(rng, ctx, bs)
     P = len(prior)
     rs = np.zeros(len(ctx), np.int32)
     rl = np.concatenate([prior, dctx - 1]).astype(np.int32)
     ns = rl.copy()
     nl = np.concatenate([L, np.ones(n_decode, np.int32)]).astype(np.int32)
-    return Workload(name="mixed-prefill-decode", cache_dtype="bf16", q_dtype="bf16",
-                    src_dtype="bf16", n_q_heads=32, n_kv_heads=8, head_dim=128,
-                    block_size=16, num_blocks=nb, context_lens=ctx, block_tables=tables,
+    return Workload(name="mixed-prefill-decode", cache_dtype=kv, q_dtype="bf16",
+                    src_dtype="bf16", n_q_heads=n_q, n_kv_heads=n_kv, head_dim=hd,
+                    block_size=bs, num_blocks=nb, context_lens=ctx, block_tables=tables,
                     q_lens=nl.copy(), res_start=rs, res_len=rl, new_start=ns, new_len=nl,
-                    scale=1.0 / math.sqrt(128), num_prefill_seqs=P, seed=seed)
+                    scale=1.0 / math.sqrt(hd), num_prefill_seqs=P, seed=seed)
 
 
 CONFIGS = {
