@@ -145,7 +145,7 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
   if (a.block_size >= 16) {
     // all 16 tokens of the step sit in one block: one (scalar) table read
     const int j = base >> a.bs_log2;
-    const int blk = j < a.max_blocks ? table[j] : -1;
+    const int blk = j < a.max_blocks ? uniform_load(table, j) : -1;
     const bool blk_ok = (unsigned)blk < (unsigned)a.num_blocks;
     const int64_t o0 = ((int64_t)blk * a.block_size + (base & (a.block_size - 1)) + lane_g) *
                            a.tok_stride + head_off;
@@ -201,7 +201,7 @@ __device__ __forceinline__ void load_full_step(Frag<L>& f, const DecodeArgs& a,
                                                const int32_t* table, int base, uint32_t lane_off,
                                                bool live) {
   const int j = base >> a.bs_log2;
-  int blk = j < a.max_blocks ? table[j] : 0;
+  int blk = j < a.max_blocks ? uniform_load(table, j) : 0;
   blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
   const int64_t step_off = ((int64_t)blk * a.block_size + (base & (a.block_size - 1))) * a.tok_stride;
   const int32_t step_bytes = live ? 16 * (int32_t)a.tok_stride : 0;
@@ -376,8 +376,9 @@ __device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int
     a += __shfl_xor(a, off, 64);
     b += __shfl_xor(b, off, 64);
   }
-  *pre = a;
-  *all = b;
+  // the reductions leave the same value in every lane: make it wave-uniform
+  *pre = __builtin_amdgcn_readfirstlane(a);
+  *all = __builtin_amdgcn_readfirstlane(b);
 }
 
 // The sequence holding unit x (0 <= x < U) and the units before it.
@@ -397,11 +398,11 @@ __device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int
     const uint64_t hit = __ballot(carry + incl > x);
     if (hit) {
       const int l = __ffsll((unsigned long long)hit) - 1;
-      *seq = base + l;
-      *before = carry + __shfl(incl - v, l, 64);
+      *seq = __builtin_amdgcn_readfirstlane(base + l);
+      *before = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v, l, 64));
       return;
     }
-    carry += __shfl(incl, 63, 64);
+    carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63, 64));
   }
   *seq = num_seqs - 1;   // not reached for x < U
   *before = carry;
@@ -415,7 +416,7 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
   using L = DecodeLayout<CDT, HD>;
   const int lane = threadIdx.x;
   const int lane_g = lane >> 3, lane_c = lane & 7;
-  const int ctx = a.context_lens[s];
+  const int ctx = uniform_load(a.context_lens, s);
   const int begin = st0 * 16;
   const int end = min(ctx, st1 * 16);
   const int n_q = a.n_kv * G;
@@ -541,13 +542,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   if (u0 >= u1) return;
   int s, before;
   locate_unit(a.context_lens, a.num_seqs, a.n_kv, (int)u0, &s, &before);
-  const int steps0 = steps_of(a.context_lens[s]);
+  const int steps0 = steps_of(uniform_load(a.context_lens, s));
   const int r = (int)u0 - before;
   int kvh = r / steps0;
   int step = r % steps0;
   int64_t u = u0;
   while (true) {
-    const int steps = steps_of(a.context_lens[s]);
+    const int steps = steps_of(uniform_load(a.context_lens, s));
     const int run_end = (int)min((int64_t)steps, step + (u1 - u));
     decode_run<CDT, HD, G, NBUF>(a, s, kvh, step, run_end, w + s * a.n_kv + kvh);
     u += run_end - step;
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     step = 0;
     if (++kvh == a.n_kv) {             // next sequence that has tokens
       kvh = 0;
-      do { ++s; } while (steps_of(a.context_lens[s]) == 0);
+      do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
     }
   }
 }

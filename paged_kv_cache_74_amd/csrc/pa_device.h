@@ -87,18 +87,12 @@ __device__ __forceinline__ float sum_over_groups(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Split plan of one sequence for decode: at most max_splits splits of a
-// multiple of 16 tokens, each at least min_split tokens (except the last).
-// Host and device compute it with this same function.
-__host__ __device__ __forceinline__ void decode_plan(int ctx, int max_splits, int min_split,
-                                                    int* num_splits, int* split_len) {
-  if (ctx <= 0) { *num_splits = 0; *split_len = 16; return; }
-  int ns = (ctx + min_split - 1) / min_split;
-  if (ns > max_splits) ns = max_splits;
-  int len = (ctx + ns - 1) / ns;
-  len = (len + 15) & ~15;
-  *split_len = len;
-  *num_splits = (ctx + len - 1) / len;
+// Wave-uniform read of a table that no kernel of the call writes: through the
+// constant address space, so it becomes a scalar load (counted apart from the
+// vector loads in flight) even where the kernel has stores in between.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p, int i) {
+  return ((const_i32*)p)[i];
 }
 
 }  // namespace pa

@@ -27,12 +27,25 @@
 //     permuted consistently in both operands); only V is stored transposed in
 //     LDS, written as bf16 pairs of two keys.
 //   * Rows are rescaled only when some row's running max grew (wave-uniform).
+//   * Work is balanced like the decode kernel: a unit is one 32-key tile of one
+//     segment (sequence, KV head, 128-row query tile); each resident workgroup
+//     takes an equal contiguous range of units, and segments split between
+//     workgroups are combined by a log-sum-exp merge kernel.
+//   * The next two tiles' K/V are in registers while a tile is computed; LDS
+//     is double-buffered, one barrier per tile.
 #include "pa_device.h"
 
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#ifndef PREFILL_PREFETCH
+#define PREFILL_PREFETCH 1  // K/V tiles held in registers ahead of the one computed
+#endif
+#ifndef PREFILL_MIN_WGS
+#define PREFILL_MIN_WGS 2   // workgroups per CU the register budget must allow
+#endif
 
 constexpr int PF_WAVES = 4;
 constexpr int PF_ROWS = 32 * PF_WAVES;   // query rows per workgroup
@@ -46,13 +59,18 @@ struct PrefillArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* seg_cu;     // [nseg + 1] prefix sums of key tiles per segment
+  const int32_t* wg_start;   // [num_wgs][2] first (segment, tile) of each workgroup
+  float* part_o;             // [slots][PF_ROWS][HD]   slot = workgroup + segment
+  float* part_ml;            // [slots][PF_ROWS][2]
   int64_t tok_stride;        // bytes between consecutive tokens of a block
   int num_blocks;
   int block_size;
   int bs_log2;
   int n_kv;
   int max_blocks;
-  int qtiles;                // query tiles per sequence (grid bound)
+  int qtiles;                // query tiles per sequence (segment enumeration)
+  int nseg;
   int causal;
   float score_scale;         // scale * k_scale * log2(e)
   float out_scale;           // v_scale for fp8 caches, else 1
@@ -66,87 +84,154 @@ struct PrefillLds {
   static constexpr int V_BYTES = HD * VROW;
 };
 
-// Physical address of token `key` (kv head kvh, byte `col` of the row), or
-// nullptr when the token is outside the context or its block id is invalid.
-__device__ __forceinline__ const uint8_t* token_ptr(const uint8_t* cache, const PrefillArgs& a,
-                                                    const int32_t* table, int key, int T, int kvh,
-                                                    int row_bytes, int col) {
-  if (key >= T) return nullptr;
-  const int j = key >> a.bs_log2;
-  if (j >= a.max_blocks) return nullptr;
-  const int blk = table[j];
-  if ((unsigned)blk >= (unsigned)a.num_blocks) return nullptr;
-  return cache + ((int64_t)blk * a.block_size + (key & (a.block_size - 1))) * a.tok_stride +
-         (int64_t)kvh * row_bytes + col;
+// Segment g = (sequence s, KV head kvh, query tile qt); qt varies fastest so a
+// workgroup that runs into the next segment keeps the same K/V.
+__device__ __forceinline__ void seg_decode(int g, int qtiles, int n_kv, int* s, int* kvh, int* qt) {
+  *qt = g % qtiles;
+  const int r = g / qtiles;
+  *kvh = r % n_kv;
+  *s = r / n_kv;
 }
 
-// 8 cache elements of one token row -> 4 dwords of bf16 pairs
+// Key tiles a segment needs: up to its last query's causal limit, or all of T.
+__device__ __forceinline__ int seg_tiles(const int32_t* __restrict__ cu_q,
+                                         const int32_t* __restrict__ context_lens, int s, int qt,
+                                         int QB, int causal) {
+  const int L = cu_q[s + 1] - cu_q[s];
+  if (qt * QB >= L) return 0;
+  const int T = context_lens[s];
+  const int last_q = min(L, (qt + 1) * QB) - 1;
+  const int visible = causal ? min(T, T - L + last_q + 1) : T;
+  return visible > 0 ? (visible + PF_BN - 1) / PF_BN : 0;
+}
+
+__device__ __forceinline__ int64_t pf_begin(int w, int64_t U, int W) { return (int64_t)w * U / W; }
+__device__ __forceinline__ int pf_owner(int64_t x, int64_t U, int W) {
+  return (int)(((x + 1) * W - 1) / U);
+}
+
+// One workgroup: tile prefix sums over segments and each workgroup's start.
+__global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int QB, int num_wgs,
+                                                            int32_t* __restrict__ seg_cu,
+                                                            int32_t* __restrict__ wg_start) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (a.nseg + 1023) / 1024;
+  const int g0 = min(a.nseg, t * per), g1 = min(a.nseg, g0 + per);
+  int sum = 0;
+  for (int g = g0; g < g1; ++g) {
+    int s, kvh, qt;
+    seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
+    sum += seg_tiles(a.cu_q, a.context_lens, s, qt, QB, a.causal);
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int g = g0; g < g1; ++g) {
+    seg_cu[g] = run;
+    int s, kvh, qt;
+    seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
+    run += seg_tiles(a.cu_q, a.context_lens, s, qt, QB, a.causal);
+  }
+  if (t == 1023) seg_cu[a.nseg] = part[1023];
+  __threadfence_block();
+  __syncthreads();
+  const int64_t U = part[1023];
+  for (int w = t; w < num_wgs; w += 1024) {
+    const int64_t x = pf_begin(w, U, num_wgs);
+    int lo = 0, hi = a.nseg;                 // last g with seg_cu[g] <= x < seg_cu[g+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg_cu[mid] <= x) lo = mid; else hi = mid;
+    }
+    wg_start[2 * w] = lo;
+    wg_start[2 * w + 1] = (int)(x - seg_cu[lo]);
+  }
+}
+
+// K/V element rows of one tile for this thread: keys key0, key0 + 1, chunk lc.
+struct TileRegs {
+  uint32_t k0[4], k1[4], v0[4], v1[4];
+};
+
+// Address of token `key` clamped into [0, T): every load is issued and lands
+// on a real token, so the count in flight is fixed; keys >= T are masked out
+// of the scores (their probability is 0 and the clamped V row is finite).
+__device__ __forceinline__ int64_t token_off(const PrefillArgs& a, const int32_t* table, int key,
+                                             int T) {
+  const int kc = min(key, T - 1);
+  const int j = min(kc >> a.bs_log2, a.max_blocks - 1);
+  int blk = table[j];
+  blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+  return ((int64_t)blk * a.block_size + (kc & (a.block_size - 1))) * a.tok_stride;
+}
+
 template <int CDT>
 __device__ __forceinline__ void load8(const uint8_t* p, uint32_t (&d)[4]) {
-  if (!p) { d[0] = d[1] = d[2] = d[3] = 0u; return; }
   if constexpr (CDT == PA_BF16) {
     const uint4 x = *(const uint4*)p;
     d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-  } else {   // fp8 e4m3: 8 bytes -> 4 bf16 pairs (exact)
+  } else {   // fp8 e4m3 codes: keep the raw bytes, widened when stored to LDS
     const uint2 x = *(const uint2*)p;
-    d[0] = fp8x2_to_bf16x2<false>(x.x); d[1] = fp8x2_to_bf16x2<true>(x.x);
-    d[2] = fp8x2_to_bf16x2<false>(x.y); d[3] = fp8x2_to_bf16x2<true>(x.y);
+    d[0] = x.x; d[1] = x.y; d[2] = 0u; d[3] = 0u;
+  }
+}
+
+template <int CDT>
+__device__ __forceinline__ void widen(uint32_t (&d)[4]) {
+  if constexpr (CDT == PA_FP8_E4M3) {   // 8 e4m3 codes -> 4 bf16 pairs (exact)
+    const uint32_t x = d[0], y = d[1];
+    d[0] = fp8x2_to_bf16x2<false>(x); d[1] = fp8x2_to_bf16x2<true>(x);
+    d[2] = fp8x2_to_bf16x2<false>(y); d[3] = fp8x2_to_bf16x2<true>(y);
   }
 }
 
 template <int CDT, int HD, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t0, int t1, int nt,
+                                              int wg, uint8_t* lds) {
   using LD = PrefillLds<CDT, HD>;
-  constexpr int QB = PF_ROWS / G;            // queries per workgroup
+  constexpr int QB = PF_ROWS / G;            // queries per segment
   constexpr int EB = CDT == PA_BF16 ? 2 : 1;
   constexpr int ROWB = HD * EB;              // bytes of one (token, head) row in the cache
   constexpr int NDT = HD / 32;               // 32-dim output tiles
   constexpr int NKT = HD / 16;               // 16-dim steps of the score MFMA
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[LD::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[LD::V_BYTES];
+  constexpr int CHUNKS = HD / 8;
+  constexpr int BUF = LD::K_BYTES + LD::V_BYTES;
 
-  int wid = blockIdx.x;
-  const int kvh = wid % a.n_kv;
-  wid /= a.n_kv;
-  const int qtile = wid % a.qtiles;
-  const int s = wid / a.qtiles;
+  int s, kvh, qt;
+  seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
   const int q0 = a.cu_q[s];
   const int L = a.cu_q[s + 1] - q0;
-  if (qtile * QB >= L) return;
   const int T = a.context_lens[s];
   const int n_q = a.n_kv * G;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, grp = lane >> 5;
-  // this lane's query row
-  const int rr = wave * 32 + lr;
+  const int rr = wave * 32 + lr;             // row of the segment
   const int hl = rr / QB;
-  const int qi = qtile * QB + rr % QB;
+  const int qi = qt * QB + rr % QB;
   const bool row_ok = qi < L;
   const int pos = T - L + qi;
   const int head = kvh * G + hl;
 
-  // Q operand: Q[row][16t + 8 grp + e]
   uint32_t qreg[NKT][4];
   {
-    const uint8_t* qp = a.q + ((int64_t)(q0 + qi) * n_q + head) * HD * 2 + grp * 16;
+    const int qrow = row_ok ? qi : 0;
+    const uint8_t* qp = a.q + ((int64_t)(q0 + qrow) * n_q + head) * HD * 2 + grp * 16;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      if (row_ok) {
-        const uint4 x = *(const uint4*)(qp + t * 32);
-        qreg[t][0] = x.x; qreg[t][1] = x.y; qreg[t][2] = x.z; qreg[t][3] = x.w;
-      } else {
-        qreg[t][0] = qreg[t][1] = qreg[t][2] = qreg[t][3] = 0u;
-      }
+      const uint4 x = *(const uint4*)(qp + t * 32);
+      qreg[t][0] = x.x; qreg[t][1] = x.y; qreg[t][2] = x.z; qreg[t][3] = x.w;
     }
   }
-
-  // keys this workgroup needs
-  const int last_q = min(L, (qtile + 1) * QB) - 1;
-  const int first_pos = T - L + qtile * QB;
-  const int visible = a.causal ? min(T, T - L + last_q + 1) : T;
-  const int n_tiles = (visible + PF_BN - 1) / PF_BN;
+  const int first_pos = T - L + qt * QB;
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
 
   f32x16_t acc[NDT];
@@ -157,45 +242,76 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   float m = -1e30f, lsum = 0.0f;
   const float c = a.score_scale;
 
-  // cooperative tile load: thread -> (key pair, 8-element chunk of the row)
-  constexpr int CHUNKS = HD / 8;
-  const int lp = tid / CHUNKS;               // key pair 0..15 (valid when < 16)
+  // thread -> (key pair, 8-element chunk); with head_dim 64 the upper half of
+  // the workgroup repeats the lower half's loads and (identical) LDS stores, so
+  // no branch separates loading threads and the wait counts stay exact
+  const int lp = (tid / CHUNKS) % (PF_BN / 2);
   const int lc = tid % CHUNKS;
-  const bool loader = lp < PF_BN / 2;
+  constexpr bool loader = true;
+  const int64_t col = (int64_t)kvh * ROWB + lc * 8 * EB;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int kb = kt * PF_BN;
+  const int jmax = min((T - 1) >> a.bs_log2, a.max_blocks - 1);
+  auto gload = [&](int t, TileRegs& R) {
+    // block_size >= 16: the tile spans at most two blocks; their table entries
+    // are read wave-uniformly (scalar loads, which do not wait behind the K/V
+    // loads in flight)
+    int jlo = 0, blo = 0, bhi = 0;
+    if (a.block_size >= 16) {
+      jlo = min((t * PF_BN) >> a.bs_log2, jmax);
+      const int jhi = min(jlo + 1, jmax);
+      blo = uniform_load(table, jlo);
+      bhi = uniform_load(table, jhi);
+      blo = (unsigned)blo < (unsigned)a.num_blocks ? blo : 0;
+      bhi = (unsigned)bhi < (unsigned)a.num_blocks ? bhi : 0;
+    }
     if (loader) {
-      uint32_t k0[4], k1[4], v0[4], v1[4];
-      const int key0 = kb + 2 * lp;
-      load8<CDT>(token_ptr(a.k_cache, a, table, key0, T, kvh, ROWB, lc * 8 * EB), k0);
-      load8<CDT>(token_ptr(a.k_cache, a, table, key0 + 1, T, kvh, ROWB, lc * 8 * EB), k1);
-      load8<CDT>(token_ptr(a.v_cache, a, table, key0, T, kvh, ROWB, lc * 8 * EB), v0);
-      load8<CDT>(token_ptr(a.v_cache, a, table, key0 + 1, T, kvh, ROWB, lc * 8 * EB), v1);
-      *(uint4*)(lds_k + (2 * lp) * LD::KROW + lc * 16) = make_uint4(k0[0], k0[1], k0[2], k0[3]);
-      *(uint4*)(lds_k + (2 * lp + 1) * LD::KROW + lc * 16) = make_uint4(k1[0], k1[1], k1[2], k1[3]);
-      // V^T[d][key0, key0 + 1] as one bf16 pair per dim
+      const int key0 = t * PF_BN + 2 * lp;
+      int64_t o0, o1;
+      if (a.block_size >= 16) {
+        const int k0c = min(key0, T - 1), k1c = min(key0 + 1, T - 1);
+        const int b0 = (k0c >> a.bs_log2) == jlo ? blo : bhi;
+        const int b1 = (k1c >> a.bs_log2) == jlo ? blo : bhi;
+        o0 = ((int64_t)b0 * a.block_size + (k0c & (a.block_size - 1))) * a.tok_stride + col;
+        o1 = ((int64_t)b1 * a.block_size + (k1c & (a.block_size - 1))) * a.tok_stride + col;
+      } else {
+        o0 = token_off(a, table, key0, T) + col;
+        o1 = token_off(a, table, key0 + 1, T) + col;
+      }
+      load8<CDT>(a.k_cache + o0, R.k0);
+      load8<CDT>(a.k_cache + o1, R.k1);
+      load8<CDT>(a.v_cache + o0, R.v0);
+      load8<CDT>(a.v_cache + o1, R.v1);
+    }
+  };
+  auto sstore = [&](TileRegs& R, uint8_t* buf) {
+    if (loader) {
+      widen<CDT>(R.k0); widen<CDT>(R.k1); widen<CDT>(R.v0); widen<CDT>(R.v1);
+      uint8_t* lk = buf;
+      uint8_t* lv = buf + LD::K_BYTES;
+      *(uint4*)(lk + (2 * lp) * LD::KROW + lc * 16) = make_uint4(R.k0[0], R.k0[1], R.k0[2], R.k0[3]);
+      *(uint4*)(lk + (2 * lp + 1) * LD::KROW + lc * 16) = make_uint4(R.k1[0], R.k1[1], R.k1[2], R.k1[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {   // V^T[d][key0, key0 + 1] as bf16 pairs
         const int d = lc * 8 + 2 * i;
-        *(uint32_t*)(lds_v + d * LD::VROW + 4 * lp) = pair_lo(v0[i], v1[i]);
-        *(uint32_t*)(lds_v + (d + 1) * LD::VROW + 4 * lp) = pair_hi(v0[i], v1[i]);
+        *(uint32_t*)(lv + d * LD::VROW + 4 * lp) = pair_lo(R.v0[i], R.v1[i]);
+        *(uint32_t*)(lv + (d + 1) * LD::VROW + 4 * lp) = pair_hi(R.v0[i], R.v1[i]);
       }
     }
-    __syncthreads();
-
-    // S^T tile (32 keys x 32 rows of this wave)
+  };
+  auto compute = [&](const uint8_t* buf, int kt) {
+    const uint8_t* lk = buf;
+    const uint8_t* lv = buf + LD::K_BYTES;
+    const int kb = kt * PF_BN;
     f32x16_t sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const uint4 kx = *(const uint4*)(lds_k + lr * LD::KROW + (16 * t + 8 * grp) * 2);
+      const uint4 kx = *(const uint4*)(lk + lr * LD::KROW + (16 * t + 8 * grp) * 2);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, kx);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(qreg[t][0], qreg[t][1], qreg[t][2], qreg[t][3]));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, sc, 0, 0, 0);
     }
-    // mask (ragged end, causal diagonal) and scale into the log2 domain
     const bool full_tile = kb + PF_BN <= T && (!a.causal || kb + PF_BN - 1 <= first_pos);
     float tmax = -INFINITY;
 #pragma unroll
@@ -220,7 +336,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       m = mn;
     }
-    // probabilities as bf16 pairs: slice t = registers 8t .. 8t+7
     uint32_t P[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -232,7 +347,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // O^T += V^T P^T; k index (grp, e) of slice t <-> key 16t + 8(e/4) + 4 grp + e%4
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint8_t* vrow = lds_v + (32 * dt + lr) * LD::VROW;
+      const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint2 lo = *(const uint2*)(vrow + (16 * t + 4 * grp) * 2);
@@ -242,35 +357,215 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[dt], 0, 0, 0);
       }
     }
-    __syncthreads();
-  }
+  };
 
-  // normalise and store: lane holds dims 32dt + 8(r/4) + 4grp + (0..3) of its row
+#if PREFILL_PREFETCH == 2
+  // two tiles in registers ahead of the one being computed, two LDS buffers
+  TileRegs R0, R1;
+  gload(t0, R0);
+  gload(min(t0 + 1, t1 - 1), R1);
+  for (int t = t0; t < t1; t += 2) {
+    sstore(R0, lds);
+    gload(min(t + 2, t1 - 1), R0);
+    __syncthreads();
+    compute(lds, t);
+    if (t + 1 >= t1) break;
+    sstore(R1, lds + BUF);
+    gload(min(t + 3, t1 - 1), R1);
+    __syncthreads();
+    compute(lds + BUF, t + 1);
+  }
+#else
+  // the next tile in registers while one is computed, two LDS buffers
+  TileRegs R0;
+  gload(t0, R0);
+  for (int t = t0; t < t1; t += 2) {
+    sstore(R0, lds);
+    gload(min(t + 1, t1 - 1), R0);
+    __syncthreads();
+    compute(lds, t);
+    if (t + 1 >= t1) break;
+    sstore(R0, lds + BUF);
+    gload(min(t + 2, t1 - 1), R0);
+    __syncthreads();
+    compute(lds + BUF, t + 1);
+  }
+#endif
+  __syncthreads();   // the next piece reuses the LDS buffers
+
   const float ltot = lsum + shfl_xor(lsum, 32);
-  if (row_ok) {
-    const float inv = ltot > 0.0f ? a.out_scale / ltot : 0.0f;
-    uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + head) * HD;
+  if (t0 == 0 && t1 == nt) {
+    // the whole segment: normalise and store the output rows
+    if (row_ok) {
+      const float inv = ltot > 0.0f ? a.out_scale / ltot : 0.0f;
+      uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + head) * HD;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * dt + 8 * r4 + 4 * grp;
+          const uint32_t w0 = pack_bf16(acc[dt][4 * r4 + 0] * inv, acc[dt][4 * r4 + 1] * inv);
+          const uint32_t w1 = pack_bf16(acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv);
+          *(uint2*)(orow + d) = make_uint2(w0, w1);
+        }
+    }
+  } else {
+    // a piece: unnormalised (m, l, O) of every row into slot wg + g
+    const int64_t slot = (int64_t)wg + g;
+    float* po = a.part_o + (slot * PF_ROWS + rr) * HD;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * dt + 8 * r4 + 4 * grp;
-        const uint32_t w0 = pack_bf16(acc[dt][4 * r4 + 0] * inv, acc[dt][4 * r4 + 1] * inv);
-        const uint32_t w1 = pack_bf16(acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv);
-        *(uint2*)(orow + d) = make_uint2(w0, w1);
+        *(float4*)(po + d) = make_float4(acc[dt][4 * r4 + 0], acc[dt][4 * r4 + 1],
+                                         acc[dt][4 * r4 + 2], acc[dt][4 * r4 + 3]);
       }
+    if (grp == 0) *(float2*)(a.part_ml + (slot * PF_ROWS + rr) * 2) = make_float2(m, ltot);
   }
 }
 
+template <int CDT, int HD, int G>
+__global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillArgs a) {
+  using LD = PrefillLds<CDT, HD>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (LD::K_BYTES + LD::V_BYTES)];
+  const int wg = blockIdx.x, W = gridDim.x;
+  const int64_t U = a.seg_cu[a.nseg];
+  const int64_t u0 = pf_begin(wg, U, W), u1 = pf_begin(wg + 1, U, W);
+  if (u0 >= u1) return;
+  int g = a.wg_start[2 * wg];
+  int tile = a.wg_start[2 * wg + 1];
+  int64_t u = u0;
+  while (true) {
+    const int nt = uniform_load(a.seg_cu, g + 1) - uniform_load(a.seg_cu, g);
+    const int end = (int)min((int64_t)nt, tile + (u1 - u));
+    prefill_piece<CDT, HD, G>(a, g, tile, end, nt, wg, lds);
+    u += end - tile;
+    if (u >= u1) break;
+    do { ++g; } while (uniform_load(a.seg_cu, g + 1) == uniform_load(a.seg_cu, g));
+    tile = 0;
+  }
+}
+
+// One workgroup per segment: combine the pieces of segments split between
+// workgroups (segments done by one workgroup were written directly).
+template <int HD, int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int num_wgs) {
+  constexpr int QB = PF_ROWS / G;
+  constexpr int DPT = HD / 2;                  // dims per thread: 2 threads per row
+  const int g = blockIdx.x;
+  const int64_t c0 = a.seg_cu[g], c1 = a.seg_cu[g + 1];
+  if (c1 <= c0) return;
+  const int64_t U = a.seg_cu[a.nseg];
+  const int w0 = pf_owner(c0, U, num_wgs), w1 = pf_owner(c1 - 1, U, num_wgs);
+  if (w0 == w1) return;
+  int s, kvh, qt;
+  seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
+  const int q0 = a.cu_q[s];
+  const int L = a.cu_q[s + 1] - q0;
+  const int n_q = a.n_kv * G;
+  const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int hl = rr / QB;
+  const int qi = qt * QB + rr % QB;
+  if (qi >= L) return;
+  float acc[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
+  float M = -INFINITY, lsum = 0.0f;
+  for (int w = w0; w <= w1; ++w) {
+    if (pf_begin(w, U, num_wgs) >= pf_begin(w + 1, U, num_wgs)) continue;   // empty workgroup
+    const int64_t slot = (int64_t)w + g;
+    const float2 ml = *(const float2*)(a.part_ml + (slot * PF_ROWS + rr) * 2);
+    const float* po = a.part_o + (slot * PF_ROWS + rr) * HD + half * DPT;
+    const float Mn = fmaxf(M, ml.x);
+    const float x = fast_exp2(M - Mn), y = fast_exp2(ml.x - Mn);
+    lsum = lsum * x + ml.y * y;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) {
+      const float4 o = *(const float4*)(po + i);
+      acc[i] = acc[i] * x + o.x * y;
+      acc[i + 1] = acc[i + 1] * x + o.y * y;
+      acc[i + 2] = acc[i + 2] * x + o.z * y;
+      acc[i + 3] = acc[i + 3] * x + o.w * y;
+    }
+    M = Mn;
+  }
+  const float inv = lsum > 0.0f ? a.out_scale / lsum : 0.0f;
+  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + kvh * G + hl) * HD + half * DPT;
+#pragma unroll
+  for (int i = 0; i < DPT; i += 2) *(uint32_t*)(orow + i) = pack_bf16(acc[i] * inv, acc[i + 1] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static size_t pf_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int pf_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+constexpr int PF_MAX_WGS_PER_CU = 4;   // bounds the workspace (LDS allows at most 4)
+
+struct PfLayout {
+  size_t seg, wgs, ml, o, total;
+};
+static PfLayout pf_layout(int64_t nseg, int64_t wgs, int head_dim) {
+  PfLayout l;
+  const size_t slots = (size_t)(wgs + nseg);
+  l.seg = 0;
+  l.wgs = pf_align((size_t)(nseg + 1) * 4);
+  l.ml = l.wgs + pf_align((size_t)wgs * 2 * 4);
+  l.o = l.ml + pf_align(slots * PF_ROWS * 2 * 4);
+  l.total = l.o + pf_align(slots * PF_ROWS * head_dim * 4);
+  return l;
+}
+
+template <int CDT, int HD, int G>
+static int pf_resident_wgs() {
+  static int cached = 0;   // per instantiation; the device is assumed not to change
+  if (!cached) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<CDT, HD, G>, 256, 0) !=
+            hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    if (per_cu > PF_MAX_WGS_PER_CU) per_cu = PF_MAX_WGS_PER_CU;
+    cached = pf_cu_count() * per_cu;
+  }
+  return cached;
+}
+
+template <int CDT, int HD, int G>
+static void pf_launch(PrefillArgs a, const PfLayout& l, char* ws, hipStream_t st) {
+  const int W = pf_resident_wgs<CDT, HD, G>();
+  a.seg_cu = (const int32_t*)(ws + l.seg);
+  a.wg_start = (const int32_t*)(ws + l.wgs);
+  a.part_ml = (float*)(ws + l.ml);
+  a.part_o = (float*)(ws + l.o);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, PF_ROWS / G, W,
+                     (int32_t*)(ws + l.seg), (int32_t*)(ws + l.wgs));
+  hipLaunchKernelGGL((prefill_kernel<CDT, HD, G>), dim3(W), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_merge_kernel<HD, G>), dim3(a.nseg), dim3(256), 0, st, a, W);
+}
+
 template <int CDT, int HD>
-static bool prefill_dispatch_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t st) {
+static bool pf_dispatch_g(int G, const PrefillArgs& a, const PfLayout& l, char* ws, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<CDT, HD, 1>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 2: hipLaunchKernelGGL((prefill_kernel<CDT, HD, 2>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 4: hipLaunchKernelGGL((prefill_kernel<CDT, HD, 4>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 8: hipLaunchKernelGGL((prefill_kernel<CDT, HD, 8>), dim3(grid), dim3(256), 0, st, a); return true;
+    case 1: pf_launch<CDT, HD, 1>(a, l, ws, st); return true;
+    case 2: pf_launch<CDT, HD, 2>(a, l, ws, st); return true;
+    case 4: pf_launch<CDT, HD, 4>(a, l, ws, st); return true;
+    case 8: pf_launch<CDT, HD, 8>(a, l, ws, st); return true;
     default: return false;
   }
+}
+
+static int64_t pf_nseg(int num_seqs, int max_q_len, int n_kv, int G) {
+  const int QB = PF_ROWS / G;
+  return (int64_t)num_seqs * n_kv * ((max_q_len + QB - 1) / QB);
 }
 
 }  // namespace pa
@@ -280,9 +575,12 @@ using namespace pa;
 extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                              int32_t n_q_heads, int32_t n_kv_heads,
                                              int32_t head_dim, int32_t max_context_len) {
-  (void)num_seqs; (void)total_q; (void)max_q_len; (void)n_q_heads; (void)n_kv_heads;
-  (void)head_dim; (void)max_context_len;
-  return 0;
+  (void)total_q; (void)max_context_len;
+  if (num_seqs <= 0 || max_q_len <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || head_dim <= 0)
+    return 0;
+  const int G = n_q_heads / n_kv_heads;
+  return pf_layout(pf_nseg(num_seqs, max_q_len, n_kv_heads, G),
+                   (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
 }
 
 extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
@@ -295,9 +593,8 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
                                       int32_t max_context_len, int32_t causal, float scale,
                                       float k_scale, float v_scale, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes; (void)max_context_len;
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || n_kv_heads < 1 ||
-      max_blocks_per_seq < 0)
+      max_blocks_per_seq < 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
@@ -310,6 +607,13 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
     return PA_ERR_NULL;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
+  const int64_t nseg = pf_nseg(num_seqs, max_q_len, n_kv_heads, group_size);
+  // key tiles are counted in 32-bit integers
+  if (nseg >= ((int64_t)1 << 31) ||
+      nseg * ((int64_t)max_context_len / PF_BN + 1) >= ((int64_t)1 << 31))
+    return PA_ERR_SHAPE;
+  const PfLayout l = pf_layout(nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   PrefillArgs a;
   a.q = (const uint8_t*)q;
   a.out = out;
@@ -328,19 +632,19 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   a.max_blocks = max_blocks_per_seq;
   const int QB = PF_ROWS / group_size;
   a.qtiles = (max_q_len + QB - 1) / QB;
+  a.nseg = (int)nseg;
   a.causal = causal != 0;
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.out_scale = fp8 ? v_scale : 1.0f;
-  const int64_t grid = (int64_t)num_seqs * a.qtiles * n_kv_heads;
-  if (grid >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
   bool ok;
   if (cache_dtype == PA_BF16)
-    ok = head_dim == 128 ? prefill_dispatch_g<PA_BF16, 128>(group_size, a, (unsigned)grid, st)
-                         : prefill_dispatch_g<PA_BF16, 64>(group_size, a, (unsigned)grid, st);
+    ok = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128>(group_size, a, l, ws, st)
+                         : pf_dispatch_g<PA_BF16, 64>(group_size, a, l, ws, st);
   else
-    ok = head_dim == 128 ? prefill_dispatch_g<PA_FP8_E4M3, 128>(group_size, a, (unsigned)grid, st)
-                         : prefill_dispatch_g<PA_FP8_E4M3, 64>(group_size, a, (unsigned)grid, st);
+    ok = head_dim == 128 ? pf_dispatch_g<PA_FP8_E4M3, 128>(group_size, a, l, ws, st)
+                         : pf_dispatch_g<PA_FP8_E4M3, 64>(group_size, a, l, ws, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
