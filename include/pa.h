@@ -202,6 +202,7 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *   cache_dtype   BF16 or FP8_E4M3 (codes times k_scale / v_scale)
  *   head_dim      64 or 128; block_size a power of two in [1, 256];
  *   group_size    1, 2, 4 or 8
+ *   scale         positive and finite, else PA_ERR_SHAPE
  *   workspace     at least pa_prefill_workspace_bytes(...) bytes (may be NULL if 0)
  */
 pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,

@@ -25,14 +25,19 @@
 //   * O^T = V^T P^T: the probability registers of the score tile are already
 //     the B operand of the PV MFMA (the key order inside a 16-key slice is
 //     permuted consistently in both operands); only V is stored transposed in
-//     LDS, written as bf16 pairs of two keys.
-//   * Rows are rescaled only when some row's running max grew (wave-uniform).
+//     LDS, written as bf16 pairs of two keys.  The row paddings of the K and
+//     V^T buffers, with loader lanes ordered key pair first, keep the LDS
+//     stores and operand reads free of bank conflicts.
+//   * The scale multiplies the scores inside the exponent (one FMA); row maxima
+//     are taken on the raw scores.  The running max moves only when a row's
+//     tile max exceeds it by more than PF_SLACK (base-2 units), so O is
+//     rescaled rarely; the result does not depend on which max is used.
 //   * Work is balanced like the decode kernel: a unit is one 32-key tile of one
 //     segment (sequence, KV head, 128-row query tile); each resident workgroup
 //     takes an equal contiguous range of units, and segments split between
 //     workgroups are combined by a log-sum-exp merge kernel.
-//   * The next two tiles' K/V are in registers while a tile is computed; LDS
-//     is double-buffered, one barrier per tile.
+//   * The next tile's K/V is in registers while a tile is computed; LDS is
+//     double-buffered, one barrier per tile; three workgroups share a CU.
 #include "pa_device.h"
 
 namespace pa {
@@ -40,16 +45,14 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-#ifndef PREFILL_PREFETCH
-#define PREFILL_PREFETCH 1  // K/V tiles held in registers ahead of the one computed
-#endif
 #ifndef PREFILL_MIN_WGS
-#define PREFILL_MIN_WGS 2   // workgroups per CU the register budget must allow
+#define PREFILL_MIN_WGS 3   // workgroups per CU the register budget must allow
 #endif
 
 constexpr int PF_WAVES = 4;
 constexpr int PF_ROWS = 32 * PF_WAVES;   // query rows per workgroup
 constexpr int PF_BN = 32;                // keys per tile
+constexpr float PF_SLACK = 8.0f;
 
 struct PrefillArgs {
   const uint8_t* q;          // [total_q][n_q][HD] bf16
@@ -79,7 +82,7 @@ struct PrefillArgs {
 template <int CDT, int HD>
 struct PrefillLds {
   static constexpr int KROW = HD * 2 + 16;        // bytes per key row of K (padded)
-  static constexpr int VROW = PF_BN * 2 + 16;     // bytes per dim row of V^T (padded)
+  static constexpr int VROW = PF_BN * 2 + 8;      // bytes per dim row of V^T (padded)
   static constexpr int K_BYTES = PF_BN * KROW;
   static constexpr int V_BYTES = HD * VROW;
 };
@@ -242,11 +245,14 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   float m = -1e30f, lsum = 0.0f;
   const float c = a.score_scale;
 
-  // thread -> (key pair, 8-element chunk); with head_dim 64 the upper half of
-  // the workgroup repeats the lower half's loads and (identical) LDS stores, so
-  // no branch separates loading threads and the wait counts stay exact
-  const int lp = (tid / CHUNKS) % (PF_BN / 2);
-  const int lc = tid % CHUNKS;
+  // thread -> (key pair, 8-element chunk), key pair fastest: the 16 lanes that
+  // share a chunk write 16 different key pairs of the same V^T rows, which
+  // with the row paddings above keeps every LDS store and operand read free of
+  // bank conflicts.  With head_dim 64 the upper half of the workgroup repeats
+  // the lower half's loads and (identical) LDS stores, so no branch separates
+  // loading threads and the wait counts stay exact
+  const int lp = tid % (PF_BN / 2);
+  const int lc = (tid / (PF_BN / 2)) % CHUNKS;
   constexpr bool loader = true;
   const int64_t col = (int64_t)kvh * ROWB + lc * 8 * EB;
 
@@ -312,85 +318,66 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(qreg[t][0], qreg[t][1], qreg[t][2], qreg[t][3]));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, sc, 0, 0, 0);
     }
+    // raw scores; the positive scale c is applied inside the exponent below
     const bool full_tile = kb + PF_BN <= T && (!a.causal || kb + PF_BN - 1 <= first_pos);
+    if (!full_tile) {
+      // score r holds key kb + 4 grp + 8(r/4) + r%4; keys above the row's last
+      // visible key are masked
+      const int lim = (a.causal ? min(pos, T - 1) : T - 1) - kb - 4 * grp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) <= lim ? sc[r] : -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = sc[r] * c;
-      if (!full_tile) {
-        const int key = kb + 8 * (r >> 2) + 4 * grp + (r & 3);
-        const bool ok = key < T && (!a.causal || key <= pos);
-        v = ok ? v : -INFINITY;
-      }
-      sc[r] = v;
-      tmax = fmaxf(tmax, v);
-    }
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[r]);
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    if (__any(mn > m)) {
+    // The running max only moves when some row's tile max exceeds it by more
+    // than PF_SLACK (base-2 units): the weights 2^(s - m) then stay below
+    // 2^PF_SLACK, exact in bf16 and fp32, and the rescale of O is rare.
+    const float mt = tmax * c;
+    if (__any(mt > m + PF_SLACK)) {
+      const float mn = fmaxf(m, mt);
       const float alpha = fast_exp2(m - mn);
       lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
       m = mn;
     }
-    uint32_t P[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        P[t][i] = pack_bf16(fast_exp2(sc[8 * t + 2 * i] - m), fast_exp2(sc[8 * t + 2 * i + 1] - m));
-        lsum = dot2_bf16(P[t][i], 0x3F803F80u, lsum);
-      }
     // O^T += V^T P^T; k index (grp, e) of slice t <-> key 16t + 8(e/4) + 4 grp + e%4
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW;
+    for (int t = 0; t < 2; ++t) {
+      uint32_t P[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int i = 0; i < 4; ++i) {
+        P[i] = pack_bf16(fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i], c, -m)),
+                         fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i + 1], c, -m)));
+        lsum = dot2_bf16(P[i], 0x3F803F80u, lsum);
+      }
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(P[0], P[1], P[2], P[3]));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW;
         const uint2 lo = *(const uint2*)(vrow + (16 * t + 4 * grp) * 2);
         const uint2 hi = *(const uint2*)(vrow + (16 * t + 8 + 4 * grp) * 2);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(P[t][0], P[t][1], P[t][2], P[t][3]));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[dt], 0, 0, 0);
       }
     }
   };
 
-#if PREFILL_PREFETCH == 2
-  // two tiles in registers ahead of the one being computed, two LDS buffers
-  TileRegs R0, R1;
-  gload(t0, R0);
-  gload(min(t0 + 1, t1 - 1), R1);
-  for (int t = t0; t < t1; t += 2) {
-    sstore(R0, lds);
-    gload(min(t + 2, t1 - 1), R0);
-    __syncthreads();
-    compute(lds, t);
-    if (t + 1 >= t1) break;
-    sstore(R1, lds + BUF);
-    gload(min(t + 3, t1 - 1), R1);
-    __syncthreads();
-    compute(lds + BUF, t + 1);
-  }
-#else
-  // the next tile in registers while one is computed, two LDS buffers
+  // the next tile in registers while one is computed, two LDS buffers.  One
+  // loop body per tile (the buffer offset alternates at run time) keeps the
+  // accumulators in the same registers from tile to tile.
   TileRegs R0;
   gload(t0, R0);
-  for (int t = t0; t < t1; t += 2) {
-    sstore(R0, lds);
+  int boff = 0;
+  for (int t = t0; t < t1; ++t) {
+    sstore(R0, lds + boff);
     gload(min(t + 1, t1 - 1), R0);
     __syncthreads();
-    compute(lds, t);
-    if (t + 1 >= t1) break;
-    sstore(R0, lds + BUF);
-    gload(min(t + 2, t1 - 1), R0);
-    __syncthreads();
-    compute(lds + BUF, t + 1);
+    compute(lds + boff, t);
+    boff ^= BUF;
   }
-#endif
   __syncthreads();   // the next piece reuses the LDS buffers
 
   const float ltot = lsum + shfl_xor(lsum, 32);
@@ -607,6 +594,8 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
     return PA_ERR_NULL;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
+  // the kernel takes row maxima of the unscaled scores
+  if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
   const int64_t nseg = pf_nseg(num_seqs, max_q_len, n_kv_heads, group_size);
   // key tiles are counted in 32-bit integers
   if (nseg >= ((int64_t)1 << 31) ||
