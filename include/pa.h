@@ -40,8 +40,10 @@
  *   checked on the device: block ids must lie in [0, num_blocks) for the
  *   positions that are read, context_lens[s] <= max_blocks_per_seq*block_size,
  *   context_lens[s] <= max_context_len, append slots must be distinct.  As a
- *   guard against memory faults only, a block id or slot outside the pool is
- *   skipped (its tokens contribute nothing / are not written).
+ *   guard against memory faults only, an append slot outside the pool is not
+ *   written, and attention reads through a block id outside the pool go to
+ *   block 0 instead: the output rows of such a sequence are unspecified, but
+ *   no access leaves the pools.
  */
 #ifndef PA_H_
 #define PA_H_

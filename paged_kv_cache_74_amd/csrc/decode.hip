@@ -17,6 +17,10 @@
 // How it maps to CDNA4 (gfx950, wave64):
 //   * One wave = one (sequence, KV head, split).  It owns all group_size query
 //     heads of that KV head, so every K/V byte is fetched from HBM exactly once.
+//     The waves of a workgroup take consecutive KV heads of the same sequence
+//     and steps: together they read whole token rows of each block (all heads
+//     of a token are adjacent in the pool), so HBM sees long contiguous runs
+//     instead of one 256-byte row per token.
 //   * Lane l works on token slot g = l >> 3 (and g + 8) of each 16-token step and
 //     on the dims of lane column c = l & 7.  One 16-byte load per lane covers 8
 //     tokens x 128 contiguous bytes: whole cache lines, fully coalesced, with no
@@ -58,6 +62,18 @@ struct DecodeLayout {
 #ifndef DECODE_NBUF
 #define DECODE_NBUF 2   // K/V steps resident per wave: NBUF - 1 in flight during compute
 #endif
+#ifndef DECODE_MAX_HW
+#define DECODE_MAX_HW 8   // most KV heads (waves) per workgroup
+#endif
+// With 8 query heads per KV head (4 for fp32 caches) a wave needs more than 256
+// registers: at most 4 waves per workgroup then, so that a workgroup fits the
+// register file.
+__host__ __device__ constexpr int max_hw(int CDT, int G) {
+  return (G >= 8 || (CDT == PA_F32 && G >= 4)) ? 4 : DECODE_MAX_HW;
+}
+#ifndef DECODE_WAVES_PER_CU
+#define DECODE_WAVES_PER_CU 16   // resident waves per CU the split kernel is launched with
+#endif
 
 struct DecodeArgs {
   const uint8_t* q;
@@ -65,9 +81,9 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  int32_t* header;           // the wave count, written by the split kernel for the merge
-  float* part_o;      // [slots][G][HD]   slot = wave + segment
-  float* part_ml;     // [slots][G][2]
+  int32_t* header;           // {workgroups, waves per workgroup}, written for the merge
+  float* part_o;      // [slots][HW][G][HD]   slot = workgroup + segment
+  float* part_ml;     // [slots][HW][G][2]
   int64_t tok_stride; // bytes between consecutive tokens of a block (n_kv * ROW)
   int num_blocks;
   int block_size;
@@ -75,7 +91,9 @@ struct DecodeArgs {
   int n_kv;
   int max_blocks;
   int num_seqs;
-  int num_waves;
+  int num_wgs;
+  int hw;             // waves (KV heads) per workgroup; n_kv = hw * nhg
+  int nhg;            // KV head groups
   float score_scale;  // scale * k_scale * log2(e)
 };
 
@@ -342,14 +360,16 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
 // ---------------------------------------------------------------------------
 // Work decomposition (balanced, deterministic)
 //
-// A unit is one 16-token step of one (sequence, KV head) segment; units are
-// ordered by (sequence, KV head, step).  With U units and W resident waves,
-// wave w processes units [floor(w U / W), floor((w+1) U / W)): every wave gets
-// the same amount of work, whatever the mix of context lengths.  A wave emits
-// one partial (m, l, O) for every segment piece it covers; the piece of wave w
-// in segment g is stored in slot w + g, which is unique because both wave and
-// segment boundaries are increasing along the unit order.  The merge kernel
-// finds the waves covering a segment from its unit range.
+// A unit is one 16-token step of one (sequence, KV head group) segment, a
+// group being the hw consecutive KV heads that the hw waves of a workgroup
+// take; units are ordered by (sequence, head group, step).  With U units and W
+// resident workgroups, workgroup w processes units [floor(w U / W),
+// floor((w+1) U / W)): every workgroup gets the same amount of work, whatever
+// the mix of context lengths.  Each wave emits one partial (m, l, O) for every
+// segment piece it covers; the piece of workgroup w in segment g is stored in
+// slot w + g (one entry per wave of the group), which is unique because both
+// workgroup and segment boundaries are increasing along the unit order.  The
+// merge kernel finds the workgroups covering a segment from its unit range.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int steps_of(int ctx) { return ctx > 0 ? (ctx + 15) >> 4 : 0; }
 
@@ -362,12 +382,12 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
 }
 
 // Units of the sequences before `s` (pre) and in total (all), one pass of the
-// wave over context_lens.
-__device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int num_seqs, int n_kv,
+// wave over context_lens (nhg = head groups per sequence).
+__device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int num_seqs, int nhg,
                                             int s, int* pre, int* all) {
   int a = 0, b = 0;
-  for (int i = threadIdx.x; i < num_seqs; i += 64) {
-    const int v = n_kv * steps_of(ctx[i]);
+  for (int i = threadIdx.x & 63; i < num_seqs; i += 64) {
+    const int v = nhg * steps_of(ctx[i]);
     b += v;
     if (i < s) a += v;
   }
@@ -382,13 +402,13 @@ __device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int
 }
 
 // The sequence holding unit x (0 <= x < U) and the units before it.
-__device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int num_seqs, int n_kv,
+__device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int num_seqs, int nhg,
                                             int x, int* seq, int* before) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int base = 0; base < num_seqs; base += 64) {
     const int i = base + lane;
-    const int v = i < num_seqs ? n_kv * steps_of(ctx[i]) : 0;
+    const int v = i < num_seqs ? nhg * steps_of(ctx[i]) : 0;
     int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -409,12 +429,12 @@ __device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int
 }
 
 // Steps [st0, st1) of segment (s, kvh): online softmax, then the partial of
-// this piece into slot `slot`.
+// this piece into entry `slot` of the partial arrays.
 template <int CDT, int HD, int G, int NBUF>
 __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, int st0, int st1,
-                                           int slot) {
+                                           int64_t slot) {
   using L = DecodeLayout<CDT, HD>;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int lane_g = lane >> 3, lane_c = lane & 7;
   const int ctx = uniform_load(a.context_lens, s);
   const int begin = st0 * 16;
@@ -505,8 +525,8 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
   }
 
   // merge the 8 lane groups (lane-local softmax states) of this wave
-  float* out_o = a.part_o + (int64_t)slot * G * HD;
-  float* out_ml = a.part_ml + (int64_t)slot * G * 2;
+  float* out_o = a.part_o + slot * G * HD;
+  float* out_ml = a.part_ml + slot * G * 2;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float M = max_over_groups(st.m[h]);
@@ -530,32 +550,35 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
   }
 }
 
-// One wave per workgroup; wave w walks its unit range segment by segment.
+// hw waves per workgroup; workgroup w walks its unit range segment by
+// segment, wave i of the group on KV head hg * hw + i of head group hg.
 template <int CDT, int HD, int G, int NBUF>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(DecodeArgs a) {
   const int w = blockIdx.x;
-  const int W = a.num_waves;
+  const int W = a.num_wgs;
+  const int wv = threadIdx.x >> 6;
   int pre, U;
-  unit_counts(a.context_lens, a.num_seqs, a.n_kv, 0, &pre, &U);
-  if (w == 0 && threadIdx.x == 0) *a.header = W;   // for the merge
+  unit_counts(a.context_lens, a.num_seqs, a.nhg, 0, &pre, &U);
+  if (w == 0 && threadIdx.x == 0) *(int2*)a.header = make_int2(W, a.hw);   // for the merge
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
   int s, before;
-  locate_unit(a.context_lens, a.num_seqs, a.n_kv, (int)u0, &s, &before);
+  locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
   const int steps0 = steps_of(uniform_load(a.context_lens, s));
   const int r = (int)u0 - before;
-  int kvh = r / steps0;
+  int hg = r / steps0;
   int step = r % steps0;
   int64_t u = u0;
   while (true) {
     const int steps = steps_of(uniform_load(a.context_lens, s));
     const int run_end = (int)min((int64_t)steps, step + (u1 - u));
-    decode_run<CDT, HD, G, NBUF>(a, s, kvh, step, run_end, w + s * a.n_kv + kvh);
+    const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
+    decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv);
     u += run_end - step;
     if (u >= u1) break;
     step = 0;
-    if (++kvh == a.n_kv) {             // next sequence that has tokens
-      kvh = 0;
+    if (++hg == a.nhg) {               // next sequence that has tokens
+      hg = 0;
       do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
     }
   }
@@ -569,9 +592,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     int n_kv, float v_scale) {
   constexpr int DPT = HD / 64;   // dims per thread
   const int n_q = n_kv * G;
+  const int hw = header[1];
+  const int nhg = n_kv / hw;
   const int h = blockIdx.x % n_q;
   const int s = blockIdx.x / n_q;
   const int kvh = h / G, hl = h % G;
+  const int hg = kvh / hw, wv = kvh % hw;
   const int t = threadIdx.x;
   const int steps = steps_of(context_lens[s]);
   const int64_t row = (int64_t)s * n_q + h;
@@ -580,20 +606,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
   float inv = 0.0f;
   int pre, Ui;
-  unit_counts(context_lens, num_seqs, n_kv, s, &pre, &Ui);
+  unit_counts(context_lens, num_seqs, nhg, s, &pre, &Ui);
   if (steps > 0) {
     const int64_t U = Ui;
-    const int num_waves = *header;
-    const int64_t g0 = (int64_t)pre + (int64_t)kvh * steps;
-    const int g = s * n_kv + kvh;
-    const int w0 = wave_of(g0, U, num_waves), w1 = wave_of(g0 + steps - 1, U, num_waves);
-    // one pass, online over the pieces (waves with an empty unit range, which
-    // occur only when waves outnumber units, hold no piece)
+    const int num_wgs = header[0];
+    const int64_t g0 = (int64_t)pre + (int64_t)hg * steps;
+    const int g = s * nhg + hg;
+    const int w0 = wave_of(g0, U, num_wgs), w1 = wave_of(g0 + steps - 1, U, num_wgs);
+    // one pass, online over the pieces (workgroups with an empty unit range,
+    // which occur only when they outnumber units, hold no piece)
     float M = -INFINITY, lsum = 0.0f;
 #pragma unroll 4
     for (int w = w0; w <= w1; ++w) {
-      if (wave_begin(w, U, num_waves) >= wave_begin(w + 1, U, num_waves)) continue;
-      const int64_t sl = (int64_t)(w + g) * G + hl;
+      if (wave_begin(w, U, num_wgs) >= wave_begin(w + 1, U, num_wgs)) continue;
+      const int64_t sl = (((int64_t)w + g) * hw + wv) * G + hl;
       const float2 ml = *(const float2*)(part_ml + sl * 2);
       float o[DPT];
 #pragma unroll
@@ -635,56 +661,82 @@ static int device_cu_count() {
 }
 
 constexpr int MAX_WAVES_PER_CU = 32;   // upper bound used to size the workspace
-constexpr int64_t MAX_WAVES = 1 << 20;
+constexpr int64_t MAX_WGS = 1 << 20;
 
-// Number of waves: the resident capacity of the device (auto), or one wave
-// per split_tokens tokens of the largest possible total context (for tests).
-static int64_t waves_bound(int num_seqs, int n_kv, int max_context_len, int split_tokens) {
-  if (split_tokens <= 0) return (int64_t)device_cu_count() * MAX_WAVES_PER_CU;
-  const int64_t units = (int64_t)num_seqs * n_kv * steps_of(max_context_len);
+// KV heads (waves) per workgroup: the largest power of two up to max_hw
+// dividing n_kv.
+static int heads_per_wg(int cache_dtype, int n_kv, int G) {
+  int hw = max_hw(cache_dtype, G);
+  while (hw > 1 && n_kv % hw) hw >>= 1;
+  return hw;
+}
+
+// Number of workgroups of hw waves: the resident capacity of the device
+// (auto), or one workgroup per split_tokens tokens of the largest possible
+// total context (for tests).
+static int64_t wgs_bound(int hw, int num_seqs, int n_kv, int max_context_len, int split_tokens) {
+  if (split_tokens <= 0) return ((int64_t)device_cu_count() * MAX_WAVES_PER_CU + hw - 1) / hw;
+  const int64_t units = (int64_t)num_seqs * (n_kv / hw) * steps_of(max_context_len);
   const int64_t per = (split_tokens + 15) / 16;
   int64_t w = (units + per - 1) / per;
   if (w < 1) w = 1;
-  if (w > MAX_WAVES) w = MAX_WAVES;
+  if (w > MAX_WGS) w = MAX_WGS;
   return w;
+}
+
+// Partial entries (one per wave and segment piece): slots = workgroups +
+// segments, hw entries per slot.  The bound covers every cache dtype, so the
+// workspace size does not depend on it.
+static int64_t entries_bound(int num_seqs, int n_kv, int G, int max_context_len, int split_tokens) {
+  int64_t e = 0;
+  for (int cdt : {(int)PA_F32, (int)PA_BF16}) {
+    const int hw = heads_per_wg(cdt, n_kv, G);
+    const int64_t n = (wgs_bound(hw, num_seqs, n_kv, max_context_len, split_tokens) +
+                       (int64_t)num_seqs * (n_kv / hw)) * hw;
+    if (n > e) e = n;
+  }
+  return e;
 }
 
 struct WsLayout {
   size_t hdr, ml, o, total;
 };
-static WsLayout ws_layout(int num_seqs, int n_kv, int G, int head_dim, int64_t waves) {
+static WsLayout ws_layout(int64_t entries, int G, int head_dim) {
   WsLayout l;
-  const size_t slots = (size_t)waves + (size_t)num_seqs * n_kv;
   l.hdr = 0;
   l.ml = 256;
-  l.o = l.ml + align256(slots * G * 2 * 4);
-  l.total = l.o + align256(slots * G * head_dim * 4);
+  l.o = l.ml + align256((size_t)entries * G * 2 * 4);
+  l.total = l.o + align256((size_t)entries * G * head_dim * 4);
   return l;
 }
 
 template <int CDT, int HD, int G>
-static int64_t resident_waves() {
-  static int64_t cached = 0;   // per instantiation; the device is assumed not to change
-  if (!cached) {
+static int64_t resident_wgs(int hw) {
+  static int64_t cached[DECODE_MAX_HW + 1] = {};   // per instantiation and group size
+  if (!cached[hw]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_split_kernel<CDT, HD, G, DECODE_NBUF>, 64, 0) != hipSuccess ||
+            &per_cu, decode_split_kernel<CDT, HD, G, DECODE_NBUF>, 64 * hw, 0) != hipSuccess ||
         per_cu <= 0)
-      per_cu = 8;
-    if (per_cu > MAX_WAVES_PER_CU) per_cu = MAX_WAVES_PER_CU;
-    cached = (int64_t)device_cu_count() * per_cu;
+      per_cu = 1;
+    const int target = (DECODE_WAVES_PER_CU + hw - 1) / hw;
+    if (per_cu > target) per_cu = target;
+    cached[hw] = (int64_t)device_cu_count() * per_cu;
   }
-  return cached;
+  return cached[hw];
 }
 
 template <int CDT, int HD, int G>
 static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
-  const int64_t bound = waves_bound(a.num_seqs, a.n_kv, max_context_len, split_tokens);
-  int64_t W = split_tokens > 0 ? bound : resident_waves<CDT, HD, G>();
+  const int hw = heads_per_wg(CDT, a.n_kv, G);
+  const int64_t bound = wgs_bound(hw, a.num_seqs, a.n_kv, max_context_len, split_tokens);
+  int64_t W = split_tokens > 0 ? bound : resident_wgs<CDT, HD, G>(hw);
   if (W > bound) W = bound;
-  a.num_waves = (int)W;
-  hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W), dim3(64), 0,
-                     st, a);
+  a.num_wgs = (int)W;
+  a.hw = hw;
+  a.nhg = a.n_kv / hw;
+  hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W),
+                     dim3(64 * hw), 0, st, a);
 }
 
 template <int CDT, int HD>
@@ -739,8 +791,8 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
       n_q_heads % n_kv_heads)
     return 0;
   const int G = n_q_heads / n_kv_heads;
-  const int64_t W = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
-  return ws_layout(num_seqs, n_kv_heads, G, head_dim, W).total;
+  return ws_layout(entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G,
+                   head_dim).total;
 }
 
 static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int head_dim,
@@ -790,8 +842,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   if ((merge && !out) || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
   const int G = group_size;
-  const int64_t bound = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
-  const WsLayout l = ws_layout(num_seqs, n_kv_heads, G, head_dim, bound);
+  const WsLayout l = ws_layout(
+      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
@@ -816,7 +868,9 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.n_kv = n_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
-  a.num_waves = 0;
+  a.num_wgs = 0;
+  a.hw = 1;
+  a.nhg = n_kv_heads;
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
 
   hipStream_t st = (hipStream_t)stream;
@@ -871,8 +925,8 @@ extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* co
   if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !context_lens) return PA_ERR_NULL;
-  const int64_t bound = waves_bound(num_seqs, n_kv_heads, max_context_len, split_tokens);
-  const WsLayout l = ws_layout(num_seqs, n_kv_heads, G, head_dim, bound);
+  const WsLayout l = ws_layout(
+      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   return launch_merge(out, out_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
                       out_scale, workspace, (hipStream_t)stream);

@@ -1,0 +1,93 @@
+"""The fp8 (OCP e4m3fn) encoder of pa_kv_append against the oracle's, bit for bit.
+
+bf16 sources: every one of the 65536 bit patterns.  fp32 sources: every
+rounding boundary of the format (each midpoint between neighbouring codes and
+its two neighbouring binary32 values, the saturation and underflow edges),
+plus 2^22 uniformly drawn bit patterns.  The oracle encoder is pinned to the
+format definition and to torch's own cast in tests/test_oracle_codecs.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_74_amd as pa
+from oracle import codecs
+from oracle.paged import encode_tokens
+
+pytestmark = pytest.mark.gpu
+
+HD, NKV, BS = 128, 1, 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+    return torch.device("cuda")
+
+
+def _encode_on_gpu(dev, src_codes: np.ndarray, src: str, scale: float) -> np.ndarray:
+    """Append the values as K rows of an fp8 pool; return the pool bytes in order."""
+    n = src_codes.size
+    pad = (-n) % HD
+    codes = np.concatenate([src_codes, np.zeros(pad, src_codes.dtype)])
+    T = codes.size // HD
+    nb = (T + BS - 1) // BS
+    if src == "bf16":
+        x = torch.from_numpy(codes.astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(codes.astype(np.uint32).view(np.int32)).view(torch.float32)
+    x = x.reshape(T, NKV, HD).to(dev)
+    k = torch.zeros((nb, BS, NKV, HD), dtype=torch.uint8, device=dev)
+    v = torch.zeros_like(k)
+    slots = torch.arange(T, dtype=torch.int64, device=dev)
+    pa.pa_kv_append(k, v, x, x, slots, scale, scale)
+    torch.cuda.synchronize()
+    out = k.reshape(-1)[: T * HD].cpu().numpy()
+    assert np.array_equal(out, v.reshape(-1)[: T * HD].cpu().numpy())
+    return out[:n]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 3.0e-3, 11.0])
+def test_fp8_encode_every_bf16_pattern(dev, scale):
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    got = _encode_on_gpu(dev, codes, "bf16", scale)
+    want = encode_tokens(codes, "bf16", "fp8", scale)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+def _boundary_f32() -> np.ndarray:
+    """Every midpoint between adjacent e4m3 magnitudes, its binary32 neighbours, and the edges."""
+    mags = np.sort(np.unique(np.abs(codecs.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))))
+    mids = ((mags[:-1].astype(np.float64) + mags[1:]) / 2).astype(np.float32)
+    edges = np.array([448.0, 464.0, 480.0, 1e30, np.inf, 2.0 ** -10, 2.0 ** -11, 2.0 ** -12,
+                      1e-30, 1e-45, 0.0], np.float32)
+    pts = np.concatenate([mids, mags.astype(np.float32), edges])
+    bits = pts.view(np.uint32).astype(np.int64)
+    around = np.concatenate([bits - 1, bits, bits + 1])
+    around = around[(around >= 0) & (around < 0x7F800001)].astype(np.uint32)
+    both = np.concatenate([around, around | np.uint32(0x80000000)])
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32)
+    return np.concatenate([both, nans])
+
+
+def test_fp8_encode_f32_rounding_boundaries(dev):
+    codes = _boundary_f32()
+    got = _encode_on_gpu(dev, codes, "f32", 1.0)
+    want = encode_tokens(codes, "f32", "fp8", 1.0)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37])
+def test_fp8_encode_f32_random_patterns(dev, scale):
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    got = _encode_on_gpu(dev, codes, "f32", scale)
+    want = encode_tokens(codes, "f32", "fp8", scale)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
