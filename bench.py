@@ -75,29 +75,30 @@ def byte_model(w):
             "step": split + out_bytes + append + slots, "append": append}
 
 
-KERNEL_SOURCES = ("paged_kv_cache_74_amd/csrc/decode.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_split_hbm_traffic.json")
+DECODE_SOURCES = ("paged_kv_cache_74_amd/csrc/decode.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
+PREFILL_SOURCES = ("paged_kv_cache_74_amd/csrc/prefill.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_hash() -> str:
+def source_hash(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per split-kernel launch from the committed counter record, or
-    None when the record is for another workload or the kernel sources changed."""
+def measured_traffic(workload: str, kernel: str, sources):
+    """HBM bytes per launch of `kernel` from the committed counter record, or
+    None when there is no record for this workload or the kernel sources changed."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    r = rec.get(workload)
-    if not r or r.get("source_sha256") != kernel_source_hash():
+    r = rec.get(f"{workload}:{kernel}")
+    if not r or r.get("source_sha256") != source_hash(sources):
         return None
     return r["fetch_kib"] * r["fetch_scale"] * 1024 + r["write_kib"] * r["write_scale"] * 1024
 
@@ -120,39 +121,47 @@ def cpu_baseline(w, budget_s: float):
     pk = np.full((w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim), poison[w.cache_dtype])
     pv = pk.copy()
     with threadpool_limits(limits=1):
-        for s in rows:
-            if t_total >= budget_s:
-                break
-            seqs = [s]
-            if w.shared_prefix_seqs and s in w.shared_prefix_seqs[1:]:
-                seqs = [w.shared_prefix_seqs[0], s]
-            for r in seqs:                       # resident tokens: setup, not timed
-                a, b = res_cu[r], res_cu[r + 1]
-                sl = oracle.paged.slot_mapping(w.block_tables[[r]], w.res_start[[r]],
-                                               w.res_len[[r]], w.block_size)
-                oracle.paged.kv_append(pk, codes(w.res_k[a:b], src), sl, w.block_size, src,
-                                       w.cache_dtype, w.k_scale)
-                oracle.paged.kv_append(pv, codes(w.res_v[a:b], src), sl, w.block_size, src,
-                                       w.cache_dtype, w.v_scale)
-            nk = codes(w.new_k[new_cu[s]:new_cu[s + 1]], src)
-            nv = codes(w.new_v[new_cu[s]:new_cu[s + 1]], src)
-            qd = np.zeros((w.num_seqs,) + qc.shape[1:], qc.dtype)
-            qd[s] = qc[s]
-            t0 = time.perf_counter()               # timed: slot map + append + decode
-            sl = oracle.paged.slot_mapping(w.block_tables[[s]], w.new_start[[s]],
-                                           w.new_len[[s]], w.block_size)
-            oracle.paged.kv_append(pk, nk, sl, w.block_size, src, w.cache_dtype, w.k_scale)
-            oracle.paged.kv_append(pv, nv, sl, w.block_size, src, w.cache_dtype, w.v_scale)
-            oracle.paged.decode(qd, w.q_dtype, pk, pv, w.cache_dtype, w.block_tables,
-                                w.context_lens, w.block_size, w.group_size, w.scale, w.k_scale,
-                                w.v_scale, rows=[s])
-            t_total += time.perf_counter() - t0
-            nbytes += float(w.context_lens[s]) * w.n_kv_heads * w.head_dim * 2 * eb
-            done += 1
+        ready = set()
+        passes = 0
+        while t_total < budget_s:          # whole passes over the step's sequences
+            for s in rows:
+                if passes and t_total >= budget_s:
+                    break
+                seqs = [s]
+                if w.shared_prefix_seqs and s in w.shared_prefix_seqs[1:]:
+                    seqs = [w.shared_prefix_seqs[0], s]
+                for r in seqs:                   # resident tokens: setup, not timed
+                    if r in ready:
+                        continue
+                    ready.add(r)
+                    a, b = res_cu[r], res_cu[r + 1]
+                    sl = oracle.paged.slot_mapping(w.block_tables[[r]], w.res_start[[r]],
+                                                   w.res_len[[r]], w.block_size)
+                    oracle.paged.kv_append(pk, codes(w.res_k[a:b], src), sl, w.block_size, src,
+                                           w.cache_dtype, w.k_scale)
+                    oracle.paged.kv_append(pv, codes(w.res_v[a:b], src), sl, w.block_size, src,
+                                           w.cache_dtype, w.v_scale)
+                nk = codes(w.new_k[new_cu[s]:new_cu[s + 1]], src)
+                nv = codes(w.new_v[new_cu[s]:new_cu[s + 1]], src)
+                qd = np.zeros((w.num_seqs,) + qc.shape[1:], qc.dtype)
+                qd[s] = qc[s]
+                t0 = time.perf_counter()           # timed: slot map + append + decode
+                sl = oracle.paged.slot_mapping(w.block_tables[[s]], w.new_start[[s]],
+                                               w.new_len[[s]], w.block_size)
+                oracle.paged.kv_append(pk, nk, sl, w.block_size, src, w.cache_dtype, w.k_scale)
+                oracle.paged.kv_append(pv, nv, sl, w.block_size, src, w.cache_dtype, w.v_scale)
+                oracle.paged.decode(qd, w.q_dtype, pk, pv, w.cache_dtype, w.block_tables,
+                                    w.context_lens, w.block_size, w.group_size, w.scale,
+                                    w.k_scale, w.v_scale, rows=[s])
+                t_total += time.perf_counter() - t0
+                nbytes += float(w.context_lens[s]) * w.n_kv_heads * w.head_dim * 2 * eb
+                done += 1
+            passes += 1
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{done} of {len(rows)} sequences of the same step (slot map + append + "
-                      f"decode), {t_total:.1f} s, single thread, float64 NumPy; logical K/V bytes"}
+            "sample": f"{done} sequence decodes ({passes} pass(es) over the {len(rows)} sequences "
+                      f"of the same step: slot map + append + decode), {t_total:.1f} s, single "
+                      f"thread, float64 NumPy; logical K/V bytes"}
 
 
 def main():
@@ -291,7 +300,8 @@ def main():
         tf = fl / (pf_avg * 1e-3) / 1e12
         prefill_rec = {"kernel": "prefill_kernel (pa_prefill_chunk)", "bound": "mfma",
                        "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "traffic": measured_traffic(args.workload, "prefill_kernel", PREFILL_SOURCES),
                        "avg_launch_us": round(pf_avg * 1e3, 2), "flops_per_launch": fl}
         log(f"prefill avg {pf_avg * 1e3:.1f} us -> {tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
             f"of the bf16 MFMA peak ({fl / 1e9:.1f} GFLOP)")
@@ -339,7 +349,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload, "decode_split_kernel", DECODE_SOURCES),
             "avg_launch_us": round(split_avg * 1e3, 2),
             "algorithmic_bytes_per_launch": bm["split_kernel"],
         },

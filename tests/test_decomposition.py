@@ -1,0 +1,156 @@
+"""The balanced work split of the decode and prefill kernels, replayed on the CPU.
+
+Host logic only: these functions restate, in Python, the index formulas the
+kernels use (unit ranges per workgroup, the slot of each piece, the pieces the
+merge reads back), and check over many random shapes that every unit is
+processed exactly once, that every slot is unique and inside the workspace the
+host sizes, and that each merge reads exactly the pieces written for its
+segment.  A mistake in the scheme (an off-by-one in the owner formula, a slot
+collision, a merge that skips or double-counts a piece) fails here without a GPU.
+"""
+from __future__ import annotations
+
+import random
+
+import pytest
+
+
+def steps_of(c):
+    return (c + 15) >> 4 if c > 0 else 0
+
+
+def begin(w, U, W):
+    return w * U // W
+
+
+def owner(x, U, W):
+    return ((x + 1) * W - 1) // U
+
+
+def replay_decode(ctx, n_kv, hw, W):
+    """Decode: units (sequence, head group, 16-token step), hw waves per workgroup."""
+    B, nhg = len(ctx), n_kv // hw
+    cu = [0]
+    for c in ctx:
+        cu.append(cu[-1] + nhg * steps_of(c))
+    U = cu[-1]
+    entries = (W + B * nhg) * hw
+    written, covered = {}, [0] * (U * hw)
+    for w in range(W):
+        u0, u1 = begin(w, U, W), begin(w + 1, U, W)
+        if u0 >= u1:
+            continue
+        s = next(i for i in range(B) if cu[i + 1] > u0)
+        st = steps_of(ctx[s])
+        hg, step = (u0 - cu[s]) // st, (u0 - cu[s]) % st
+        u = u0
+        while True:
+            steps = steps_of(ctx[s])
+            end = min(steps, step + (u1 - u))
+            assert end > step
+            slot = w + s * nhg + hg
+            for wv in range(hw):
+                e = slot * hw + wv
+                assert 0 <= e < entries and e not in written
+                written[e] = (s, hg * hw + wv, step, end)
+                for t in range(step, end):
+                    covered[(cu[s] + hg * steps + t) * hw + wv] += 1
+            u += end - step
+            if u >= u1:
+                break
+            step, hg = 0, hg + 1
+            if hg == nhg:
+                hg, s = 0, s + 1
+                while steps_of(ctx[s]) == 0:
+                    s += 1
+    assert all(c == 1 for c in covered)
+    read = set()
+    for s in range(B):
+        st = steps_of(ctx[s])
+        if st == 0:
+            continue
+        for kvh in range(n_kv):
+            hg, wv = kvh // hw, kvh % hw
+            g0, g = cu[s] + hg * st, s * nhg + hg
+            got = 0
+            for w in range(owner(g0, U, W), owner(g0 + st - 1, U, W) + 1):
+                if begin(w, U, W) >= begin(w + 1, U, W):
+                    continue                       # an empty workgroup holds no piece
+                e = (w + g) * hw + wv
+                assert e in written and written[e][:2] == (s, kvh)
+                got += written[e][3] - written[e][2]
+                read.add(e)
+            assert got == st
+    assert read == set(written)
+
+
+def replay_prefill(tiles, W):
+    """Prefill: units (segment, 32-key tile); a piece of workgroup w in segment g -> slot w + g."""
+    cu = [0]
+    for t in tiles:
+        cu.append(cu[-1] + t)
+    U, nseg = cu[-1], len(tiles)
+    written, covered = {}, [0] * U
+    for w in range(W):
+        u0, u1 = begin(w, U, W), begin(w + 1, U, W)
+        if u0 >= u1:
+            continue
+        g = next(i for i in range(nseg) if cu[i + 1] > u0)
+        tile, u = u0 - cu[g], u0
+        while True:
+            end = min(tiles[g], tile + (u1 - u))
+            whole = tile == 0 and end == tiles[g]
+            if not whole:
+                slot = w + g
+                assert slot < W + nseg and slot not in written
+                written[slot] = (g, tile, end)
+            for t in range(tile, end):
+                covered[cu[g] + t] += 1
+            u += end - tile
+            if u >= u1:
+                break
+            tile, g = 0, g + 1
+            while tiles[g] == 0:
+                g += 1
+    assert all(c == 1 for c in covered)
+    read = set()
+    for g in range(nseg):
+        if tiles[g] == 0:
+            continue
+        w0, w1 = owner(cu[g], U, W), owner(cu[g + 1] - 1, U, W)
+        if w0 == w1:
+            continue                               # written whole by one workgroup
+        got = 0
+        for w in range(w0, w1 + 1):
+            if begin(w, U, W) >= begin(w + 1, U, W):
+                continue
+            assert (w + g) in written and written[w + g][0] == g
+            got += written[w + g][2] - written[w + g][1]
+            read.add(w + g)
+        assert got == tiles[g]
+    assert read == set(written)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_split_covers_every_unit_once(seed):
+    rng = random.Random(seed)
+    for _ in range(300):
+        B = rng.randint(1, 12)
+        n_kv = rng.choice([1, 2, 4, 8, 16, 32])
+        hw = rng.choice([h for h in (1, 2, 4, 8) if n_kv % h == 0])
+        ctx = [rng.choice([0, 0, 1, 15, 16, 17, rng.randint(1, 300)]) for _ in range(B)]
+        if sum(ctx) == 0:
+            continue
+        for W in (1, 2, 3, 7, 64, 1000):
+            replay_decode(ctx, n_kv, hw, W)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_split_covers_every_tile_once(seed):
+    rng = random.Random(100 + seed)
+    for _ in range(300):
+        tiles = [rng.choice([0, 1, 2, 5, rng.randint(1, 40)]) for _ in range(rng.randint(1, 10))]
+        if sum(tiles) == 0:
+            continue
+        for W in (1, 2, 3, 5, 17, 256):
+            replay_prefill(tiles, W)
