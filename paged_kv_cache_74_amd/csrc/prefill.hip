@@ -87,6 +87,19 @@ struct PrefillLds {
   static constexpr int V_BYTES = HD * VROW;
 };
 
+// Workgroups are dispatched to the chip's 8 XCDs round robin (workgroup b on
+// XCD b % 8), each XCD with its own L2.  Renumbering them so that every XCD
+// holds a contiguous range of the work order puts the query tiles of one
+// (sequence, KV head) -- which read the same K/V tiles at about the same time
+// -- on one XCD, where they share its L2 instead of each fetching from HBM.
+// The renumbering is a bijection of [0, W), so correctness never depends on
+// the dispatch order.
+constexpr int PF_XCDS = 8;
+__device__ __forceinline__ int xcd_local_order(int b, int W) {
+  const int x = b % PF_XCDS, j = b / PF_XCDS;
+  return x * (W / PF_XCDS) + min(x, W % PF_XCDS) + j;
+}
+
 // Segment g = (sequence s, KV head kvh, query tile qt); qt varies fastest so a
 // workgroup that runs into the next segment keeps the same K/V.
 __device__ __forceinline__ void seg_decode(int g, int qtiles, int n_kv, int* s, int* kvh, int* qt) {
@@ -416,7 +429,8 @@ template <int CDT, int HD, int G>
 __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillArgs a) {
   using LD = PrefillLds<CDT, HD>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (LD::K_BYTES + LD::V_BYTES)];
-  const int wg = blockIdx.x, W = gridDim.x;
+  const int W = gridDim.x;
+  const int wg = xcd_local_order(blockIdx.x, W);
   const int64_t U = a.seg_cu[a.nseg];
   const int64_t u0 = pf_begin(wg, U, W), u1 = pf_begin(wg + 1, U, W);
   if (u0 >= u1) return;
@@ -434,13 +448,24 @@ __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillAr
   }
 }
 
-// One workgroup per segment: combine the pieces of segments split between
-// workgroups (segments done by one workgroup were written directly).
+// Combine the pieces of segments split between workgroups (segments done by
+// one workgroup were written directly).  Workgroup (g, part) takes 256 / (HD / 4)
+// rows of segment g; each row is read by HD / 4 consecutive lanes (four dims
+// each), so every load and store of a wave covers whole rows, and each
+// thread merges one row slice in a single online pass over the pieces.
+template <int HD>
+struct MergeShape {
+  static constexpr int LPR = HD / 4;            // lanes per row
+  static constexpr int ROWS = 256 / LPR;        // rows per workgroup
+};
 template <int HD, int G>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int num_wgs) {
   constexpr int QB = PF_ROWS / G;
-  constexpr int DPT = HD / 2;                  // dims per thread: 2 threads per row
-  const int g = blockIdx.x;
+  constexpr int LPR = MergeShape<HD>::LPR;
+  constexpr int ROWS = MergeShape<HD>::ROWS;
+  static_assert(PF_ROWS % ROWS == 0, "merge tiling");
+  const int g = blockIdx.x / (PF_ROWS / ROWS);
+  const int part = blockIdx.x % (PF_ROWS / ROWS);
   const int64_t c0 = a.seg_cu[g], c1 = a.seg_cu[g + 1];
   if (c1 <= c0) return;
   const int64_t U = a.seg_cu[a.nseg];
@@ -451,36 +476,28 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
   const int q0 = a.cu_q[s];
   const int L = a.cu_q[s + 1] - q0;
   const int n_q = a.n_kv * G;
-  const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int hl = rr / QB;
+  const int d0 = (threadIdx.x % LPR) * 4;
+  const int rr = part * ROWS + threadIdx.x / LPR;
   const int qi = qt * QB + rr % QB;
   if (qi >= L) return;
-  float acc[DPT];
-#pragma unroll
-  for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float M = -INFINITY, lsum = 0.0f;
+#pragma unroll 4
   for (int w = w0; w <= w1; ++w) {
     if (pf_begin(w, U, num_wgs) >= pf_begin(w + 1, U, num_wgs)) continue;   // empty workgroup
-    const int64_t slot = (int64_t)w + g;
-    const float2 ml = *(const float2*)(a.part_ml + (slot * PF_ROWS + rr) * 2);
-    const float* po = a.part_o + (slot * PF_ROWS + rr) * HD + half * DPT;
+    const int64_t row = ((int64_t)w + g) * PF_ROWS + rr;
+    const float2 ml = *(const float2*)(a.part_ml + row * 2);
+    const float4 o = *(const float4*)(a.part_o + row * HD + d0);
     const float Mn = fmaxf(M, ml.x);
     const float x = fast_exp2(M - Mn), y = fast_exp2(ml.x - Mn);
     lsum = lsum * x + ml.y * y;
-#pragma unroll
-    for (int i = 0; i < DPT; i += 4) {
-      const float4 o = *(const float4*)(po + i);
-      acc[i] = acc[i] * x + o.x * y;
-      acc[i + 1] = acc[i + 1] * x + o.y * y;
-      acc[i + 2] = acc[i + 2] * x + o.z * y;
-      acc[i + 3] = acc[i + 3] * x + o.w * y;
-    }
+    acc.x = acc.x * x + o.x * y; acc.y = acc.y * x + o.y * y;
+    acc.z = acc.z * x + o.z * y; acc.w = acc.w * x + o.w * y;
     M = Mn;
   }
   const float inv = lsum > 0.0f ? a.out_scale / lsum : 0.0f;
-  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + kvh * G + hl) * HD + half * DPT;
-#pragma unroll
-  for (int i = 0; i < DPT; i += 2) *(uint32_t*)(orow + i) = pack_bf16(acc[i] * inv, acc[i + 1] * inv);
+  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + kvh * G + rr / QB) * HD + d0;
+  *(uint2*)orow = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -536,7 +553,8 @@ static void pf_launch(PrefillArgs a, const PfLayout& l, char* ws, hipStream_t st
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, PF_ROWS / G, W,
                      (int32_t*)(ws + l.seg), (int32_t*)(ws + l.wgs));
   hipLaunchKernelGGL((prefill_kernel<CDT, HD, G>), dim3(W), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((prefill_merge_kernel<HD, G>), dim3(a.nseg), dim3(256), 0, st, a, W);
+  hipLaunchKernelGGL((prefill_merge_kernel<HD, G>),
+                     dim3(a.nseg * (PF_ROWS / MergeShape<HD>::ROWS)), dim3(256), 0, st, a, W);
 }
 
 template <int CDT, int HD>
@@ -598,7 +616,8 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
   const int64_t nseg = pf_nseg(num_seqs, max_q_len, n_kv_heads, group_size);
   // key tiles are counted in 32-bit integers
-  if (nseg >= ((int64_t)1 << 31) ||
+  // (the merge launches PF_ROWS / 4 workgroups per segment at head_dim 64)
+  if (nseg * (PF_ROWS / 4) >= ((int64_t)1 << 31) ||
       nseg * ((int64_t)max_context_len / PF_BN + 1) >= ((int64_t)1 << 31))
     return PA_ERR_SHAPE;
   const PfLayout l = pf_layout(nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
