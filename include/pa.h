@@ -119,7 +119,8 @@ pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
  *
  *   k_new, v_new  [num_tokens][n_kv_heads][head_dim] of src_dtype (contiguous)
  *   slot_mapping  int64 [num_tokens], distinct non-negative entries
- *   head_dim      a multiple of 8
+ *   head_dim      a multiple of 8; num_tokens * n_kv_heads * head_dim / 8 < 2^31
+ *                 (else PA_ERR_SHAPE)
  */
 pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
                        int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,

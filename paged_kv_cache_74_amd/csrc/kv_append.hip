@@ -129,12 +129,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int64_t* __restrict__ slots, int64_t num_slots_in_pool, int lanes_per_token,
-    int64_t total_lanes, float k_inv, float v_inv) {
-  const int64_t lane = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int total_lanes, float k_inv, float v_inv) {
+  // 32-bit index arithmetic (the host keeps total_lanes below 2^31)
+  const int lane = blockIdx.x * blockDim.x + threadIdx.x;
   if (lane >= total_lanes) return;
   const bool is_v = blockIdx.y != 0;
-  const int64_t tok = lane / lanes_per_token;
-  const int64_t within = lane - tok * lanes_per_token;   // which 8-element piece of the token
+  const int tok = (int)((unsigned)lane / (unsigned)lanes_per_token);
+  const int within = lane - tok * lanes_per_token;   // which 8-element piece of the token
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= num_slots_in_pool) return;
   constexpr int SB = elem_bytes(SRC), DB = elem_bytes(DST);
@@ -187,8 +188,10 @@ extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
   if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
-  const int lanes_per_token = n_kv_heads * head_dim / 8;
-  const int64_t total = (int64_t)num_tokens * lanes_per_token;
+  const int64_t lanes = (int64_t)n_kv_heads * head_dim / 8;
+  if (lanes * num_tokens >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
+  const int lanes_per_token = (int)lanes;
+  const int total = (int)(lanes * num_tokens);
   const int64_t pool_slots = (int64_t)num_blocks * block_size;
   const dim3 grid((unsigned)((total + 255) / 256), 2);
   hipStream_t st = (hipStream_t)stream;
