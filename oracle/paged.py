@@ -97,6 +97,25 @@ def kv_append(pool, new_codes, slots, block_size: int, src_dtype: str, cache_dty
     return pool
 
 
+def copy_blocks(dst_pool, src_pool, pairs):
+    """Whole-block copies: dst_pool[d] = src_pool[s] for every pair (s, d).
+
+    [Batching] "Sharing and copy-on-write": before a sequence writes into a
+    block that other sequences still reference (refcount > 1), the block is
+    copied to a fresh one and the writer's table entry is pointed at the copy;
+    section "Scheduling policy and preemption": a preempted sequence's blocks
+    are copied out to host memory and copied back (to any free blocks) when it
+    resumes.  Both are this operation, within one pool or between a device
+    pool and a host pool.  Pairs whose source or destination lies outside its
+    pool are skipped; ``dst_pool`` is modified in place and returned, and no
+    block that is not a destination changes.
+    """
+    for s_blk, d_blk in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= s_blk < src_pool.shape[0] and 0 <= d_blk < dst_pool.shape[0]:
+            dst_pool[d_blk] = src_pool[s_blk].copy()
+    return dst_pool
+
+
 def materialise(pool, table_row, ctx: int, block_size: int):
     """Contiguous [ctx, n_kv, hd] codes of one sequence, gathered block by block."""
     n_blocks = -(-int(ctx) // block_size)
