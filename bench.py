@@ -164,12 +164,89 @@ def cpu_baseline(w, budget_s: float):
                       f"thread, float64 NumPy; logical K/V bytes"}
 
 
+# Block copies on the Llama-3-8B-shaped pool (block 16, 8 KV heads, 128 dims, bf16:
+# 32 KiB of K and 32 KiB of V per block): copy-on-write of 4096 blocks within the
+# device pool, and a swap of 4096 blocks out to pinned host memory and back in.
+BLOCK_WORKLOADS = {"cow": 4096, "swap": 4096}
+HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16, one direction
+
+
+def block_copy_bench(args, torch, np, pa):
+    """K copy calls of n block pairs; algorithmic bytes = pairs * 2 (K, V) * block bytes
+    * 2 (read + write)."""
+    dev = "cuda"
+    nb, bs, nkv, hd = 19850, 16, 8, 128
+    n = BLOCK_WORKLOADS[args.workload]
+    block_bytes = bs * nkv * hd * 2
+    gen = torch.Generator(device=dev).manual_seed(0)
+    k = torch.empty((nb, bs, nkv, hd), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    k.view(torch.int16).random_(generator=gen)
+    v.view(torch.int16).random_(generator=gen)
+    perm = np.random.default_rng(0).permutation(nb)
+    if args.workload == "cow":
+        pairs = torch.as_tensor(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64), device=dev)
+        calls = [lambda: pa.pa_copy_blocks(k, v, k, v, pairs)]
+        bound, peak = "hbm", HBM_PEAK_GBS
+        what = f"copy-on-write of {n} blocks within the device pool"
+    else:
+        hk = torch.empty((n, bs, nkv, hd), dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty_like(hk, pin_memory=True)
+        out_pairs = torch.as_tensor(np.stack([perm[:n], np.arange(n)], 1).astype(np.int64), device=dev)
+        in_pairs = torch.as_tensor(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64),
+                                   device=dev)
+        calls = [lambda: pa.pa_copy_blocks(hk, hv, k, v, out_pairs),
+                 lambda: pa.pa_copy_blocks(k, v, hk, hv, in_pairs)]
+        bound, peak = "host-link", HOST_LINK_PEAK_GBS
+        what = f"swap of {n} blocks out to pinned host memory and back in"
+    nbytes = n * 2 * block_bytes            # bytes copied per call (K and V)
+    # bytes the bound resource carries per call: HBM reads and writes them (copy-on-write);
+    # the host link carries them once (swap)
+    moved = 2 * nbytes if bound == "hbm" else nbytes
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * len(calls))]
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for j, c in enumerate(calls):
+            e = ev[i * len(calls) + j]
+            e[0].record(stream)
+            c()
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    per_call = float(ms.mean())
+    gbs = moved / (per_call * 1e-3) / 1e9
+    step_ms = wall * 1e3 / args.steps
+    log(f"{what}: {per_call * 1e3:.1f} us per call -> {gbs:.1f} GB/s through the {bound} "
+        f"({gbs / peak:.1%} of {peak:.0f} GB/s)")
+    rec = {"metric": f"block copy GB/s ({args.workload})", "value": round(moved * len(calls) /
+           (step_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": what, "blocks": n, "block_bytes_k": block_bytes,
+                      "pool_blocks": nb},
+           "roofline": {"kernel": "copy_blocks_kernel (pa_copy_blocks)", "bound": bound,
+                        "achieved": round(gbs, 2), "peak": peak, "unit": "GB/s",
+                        "frac": round(gbs / peak, 4), "traffic": None,
+                        "avg_launch_us": round(per_call * 1e3, 2),
+                        "algorithmic_bytes_per_launch": moved},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3-gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama3-gqa",
+                    choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--pools", type=int, default=2, help="pool copies rotated across steps")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -204,6 +281,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration_mib} MiB x 3")
         return
+    if args.workload in BLOCK_WORKLOADS:
+        return block_copy_bench(args, torch, np, pa)
     cfg, kv = WORKLOADS[args.workload]
     t0 = time.perf_counter()
     w = workloads.full(cfg, kv=kv)

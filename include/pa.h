@@ -252,6 +252,39 @@ pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
                           float out_scale, const void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * pa_copy_blocks -- whole-block copies between paged pools: copy-on-write
+ *   within one pool, and swap-out / swap-in between a device pool and a pool
+ *   in pinned host memory.
+ *   Source: "3.3 Batching and memory management", section "Sharing and
+ *   copy-on-write" (a block that other sequences still reference is copied
+ *   to a fresh block before one of them writes into it) and section
+ *   "Scheduling policy and preemption" (a preempted sequence's blocks are
+ *   copied out to host memory and copied back when it resumes).
+ *
+ *   For every pair i with 0 <= src < src_num_blocks and 0 <= dst < dst_num_blocks
+ *   (block_pairs[2i] = src, block_pairs[2i+1] = dst):
+ *     dst_k[dst][:][:][:] = src_k[src][:][:][:],  dst_v[dst] = src_v[src]
+ *   byte for byte; other pairs are skipped and no other block is written.
+ *
+ *   dst_k, dst_v  [dst_num_blocks][block_size][n_kv_heads][head_dim] of cache_dtype
+ *   src_k, src_v  [src_num_blocks][block_size][n_kv_heads][head_dim] of cache_dtype;
+ *                 either pair of pools may be device memory or pinned host memory
+ *                 (hipHostMalloc), which the kernel accesses directly; the src and
+ *                 dst pools may be the same pools.
+ *   block_pairs   int64 [num_pairs][2] in device memory.  Destinations distinct,
+ *                 and no block is both a source and a destination in one call
+ *                 (else which copy lands is unspecified).
+ *   Pool bases 16-byte aligned (8 when a block's byte size is not a multiple
+ *   of 16; a block's byte size must be a multiple of 8), else PA_ERR_SHAPE /
+ *   PA_ERR_UNSUPPORTED.
+ */
+pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                         const void* src_k, const void* src_v, int32_t src_num_blocks,
+                         int cache_dtype, int32_t block_size, int32_t n_kv_heads,
+                         int32_t head_dim, const int64_t* block_pairs, int32_t num_pairs,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,7 @@ def lib():
         _c("pa_decode_partials", ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I,
            P, I, P, I, I, F, F, I, P, S, P)
         _c("pa_decode_merge", ctypes.c_int, P, ctypes.c_int, P, I, I, I, I, I, I, F, P, S, P)
+        _c("pa_copy_blocks", ctypes.c_int, P, P, I, P, P, I, ctypes.c_int, I, I, I, P, I, P)
         _c("pa_prefill_workspace_bytes", S, I, I, I, I, I, I, I)
         _c("pa_prefill_chunk", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, ctypes.c_int, I, I,
            I, I, I, P, I, P, I, I, F, F, F, P, S, P)
@@ -236,3 +237,26 @@ def pa_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         1 if causal else 0, scale, k_scale, v_scale, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
     return out
+
+
+def pa_copy_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                   src_v: torch.Tensor, block_pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks src -> dst for every (src, dst) row of ``block_pairs`` (int64 [n, 2],
+    on the GPU).  The pools are [num_blocks, bs, n_kv, hd]; either side may live in pinned
+    host memory (swap) or both be the same device pools (copy-on-write)."""
+    L = lib()
+    for t in (dst_k, dst_v, src_k, src_v):
+        _need(t.is_contiguous() and (t.is_cuda or t.is_pinned()),
+              "pools: contiguous, on the GPU or in pinned host memory")
+    _dev(block_pairs)
+    _need(dst_k.shape == dst_v.shape and src_k.shape == src_v.shape and dst_k.dim() == 4,
+          "pools: [num_blocks, bs, n_kv, hd], K and V alike")
+    _need(dst_k.shape[1:] == src_k.shape[1:] and dst_k.dtype == src_k.dtype ==
+          dst_v.dtype == src_v.dtype, "source and destination pools of one block shape and dtype")
+    _need(block_pairs.dtype == torch.int64 and block_pairs.dim() == 2 and
+          block_pairs.shape[1] == 2, "block_pairs: int64 [n, 2]")
+    _, bs, nkv, hd = dst_k.shape
+    _check("pa_copy_blocks", L.pa_copy_blocks(
+        _ptr(dst_k), _ptr(dst_v), dst_k.shape[0], _ptr(src_k), _ptr(src_v), src_k.shape[0],
+        _dtype_code(dst_k), bs, nkv, hd, _ptr(block_pairs), block_pairs.shape[0],
+        _stream(stream)))

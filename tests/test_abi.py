@@ -164,3 +164,27 @@ def test_prefill_scale_checks(lib):
     assert _prefill(lib, scale=-0.1, **d) == PA_ERR_SHAPE
     assert _prefill(lib, scale=float("inf"), **d) == PA_ERR_SHAPE
     assert _prefill(lib, scale=float("nan"), **d) == PA_ERR_SHAPE
+
+
+def _copy(lib, **kw):
+    a = dict(dk=None, dv=None, dn=8, sk=None, sv=None, sn=8, cdt=BF16, bs=16, nkv=2, hd=64,
+             pairs=None, n=4)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["dk"], a["dv"], a["dn"], a["sk"], a["sv"], a["sn"], a["cdt"],
+                              a["bs"], a["nkv"], a["hd"], a["pairs"], a["n"], None)
+
+
+def test_copy_blocks_argument_checks(lib):
+    assert _copy(lib, n=0) == PA_OK
+    assert _copy(lib, dn=-1) == PA_ERR_SHAPE
+    assert _copy(lib, bs=0) == PA_ERR_SHAPE
+    assert _copy(lib, n=-2) == PA_ERR_SHAPE
+    assert _copy(lib, cdt=7) == PA_ERR_DTYPE
+    assert _copy(lib, cdt=FP8, bs=1, nkv=1, hd=4) == PA_ERR_UNSUPPORTED   # 4-byte blocks
+    assert _copy(lib) == PA_ERR_NULL
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="dummy pointers are passed only where no GPU is visible")
+def test_copy_blocks_alignment_check(lib):
+    d = dict(dk=0x1000, dv=0x1000, sk=0x1000, sv=0x1008, pairs=0x1000)
+    assert _copy(lib, **d) == PA_ERR_SHAPE                                 # 16-byte blocks need 16
