@@ -15,6 +15,13 @@ Encoding rule (the reading used by the whole path): multiply by the
 per-tensor inverse scale in float32, clamp the magnitude to 448 (saturate
 finite; infinities saturate too), then round to the nearest representable
 value with ties to even.  NaN encodes as 0x7F whatever its sign.
+
+INT8: the KV-quantisation section of "From PagedAttention to Chunked
+Prefill" (5.4) names FP16 -> INT8 as the standard step; the reading taken
+is symmetric 8-bit integers with a per-tensor scale, like FP8 above: the
+code is the float32 product x * (1 / scale) rounded to the nearest integer
+(ties to even) and clamped to [-127, 127]; NaN encodes as 0; the value of a
+code is code * scale.
 """
 from __future__ import annotations
 
@@ -84,6 +91,20 @@ def e4m3_encode(x) -> np.ndarray:
     return out
 
 
+def int8_decode(codes) -> np.ndarray:
+    """Signed 8-bit codes (stored as uint8 bytes) -> float64 integers."""
+    return np.asarray(codes, dtype=np.uint8).view(np.int8).astype(np.float64)
+
+
+def int8_encode(x) -> np.ndarray:
+    """float32 values -> uint8 bytes of int8 codes: rint (ties to even), clamp to
+    [-127, 127], NaN -> 0."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    c = np.clip(np.rint(np.where(nan, 0.0, x)), -127.0, 127.0)   # +-inf clamp too
+    return c.astype(np.int8).view(np.uint8)
+
+
 def f32_inverse(scale: float) -> np.float32:
     """Per-tensor inverse scale, one IEEE binary32 division."""
     return np.float32(1.0) / np.float32(scale)
@@ -97,4 +118,6 @@ def decode(codes, dtype: str, scale: float = 1.0) -> np.ndarray:
         return bf16_decode(codes)
     if dtype == "fp8":
         return e4m3_decode(codes) * np.float64(np.float32(scale))
+    if dtype == "int8":
+        return int8_decode(codes) * np.float64(np.float32(scale))
     raise ValueError(dtype)

@@ -70,15 +70,16 @@ def encode_tokens(new_codes, src_dtype: str, cache_dtype: str, scale: float = 1.
     """What a cache slot stores for a token: a bit copy, or e4m3(x * (1/scale))."""
     if cache_dtype == src_dtype:
         return np.array(new_codes, copy=True)
-    if cache_dtype == "fp8":
+    if cache_dtype in ("fp8", "int8"):
         if src_dtype == "bf16":
             x = codecs.bf16_decode(new_codes).astype(np.float32)
         elif src_dtype == "f32":
             x = np.asarray(new_codes, dtype=np.uint32).view(np.float32)
         else:
             raise ValueError(src_dtype)
-        y = x * codecs.f32_inverse(scale)           # one float32 product
-        return codecs.e4m3_encode(y.astype(np.float32))
+        with np.errstate(over="ignore", invalid="ignore"):
+            y = (x * codecs.f32_inverse(scale)).astype(np.float32)   # one float32 product
+        return codecs.e4m3_encode(y) if cache_dtype == "fp8" else codecs.int8_encode(y)
     raise ValueError((src_dtype, cache_dtype))
 
 

@@ -12,15 +12,16 @@ import torch
 import paged_kv_cache_74_amd as pa
 from workloads import POISON, Workload
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
-INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+               "int8": torch.int8}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8}
 
 
 def poison_pool(w: Workload, dev) -> torch.Tensor:
     shape = (w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim)
     t = torch.empty(shape, dtype=TORCH_DTYPE[w.cache_dtype], device=dev)
     p = int(POISON[w.cache_dtype])
-    bits = {"f32": 32, "bf16": 16, "fp8": 8}[w.cache_dtype]
+    bits = {"f32": 32, "bf16": 16, "fp8": 8, "int8": 8}[w.cache_dtype]
     if w.cache_dtype != "fp8" and p >= 1 << (bits - 1):
         p -= 1 << bits            # as the signed integer of the same bits
     t.view(INT_VIEW[w.cache_dtype]).fill_(p)

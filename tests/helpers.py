@@ -21,7 +21,7 @@ def codes(t, dtype: str) -> np.ndarray:
         return t.contiguous().view(torch.int32).numpy().view(np.uint32)
     if dtype == "bf16":
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    if dtype == "fp8":
+    if dtype in ("fp8", "int8"):
         return t.contiguous().view(torch.uint8).numpy()
     raise ValueError(dtype)
 

@@ -95,3 +95,49 @@ def test_bf16_decode_matches_torch():
     np.testing.assert_array_equal(tv[ok], got[ok])
     assert codecs.bf16_decode(np.uint16(0x3F80)) == 1.0
     assert codecs.bf16_decode(np.uint16(0xC000)) == -2.0
+
+
+# ---- INT8 (symmetric, per-tensor scale) --------------------------------------------
+
+def test_int8_decode_is_twos_complement():
+    b = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(b.copy()).view(torch.int8).numpy().astype(np.float64)
+    assert np.array_equal(codecs.int8_decode(b), want)
+
+
+def test_int8_integers_round_trip():
+    x = np.arange(-127, 128, dtype=np.float32)
+    assert np.array_equal(codecs.int8_decode(codecs.int8_encode(x)), x.astype(np.float64))
+
+
+def test_int8_ties_to_even_and_saturation():
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.49, 127.5, 1e9, -1e9,
+                  np.inf, -np.inf, np.nan, -0.0], np.float32)
+    want = np.array([0, 2, 2, 0, -2, -2, 126, 127, 127, 127, -127, 127, -127, 0, 0], np.float64)
+    assert np.array_equal(codecs.int8_decode(codecs.int8_encode(x)), want)
+
+
+def test_int8_encode_matches_torch_round_and_clamp():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(100000) * 80).astype(np.float32)
+    t = torch.from_numpy(x).round().clamp(-127, 127).to(torch.int8).view(torch.uint8).numpy()
+    assert np.array_equal(codecs.int8_encode(x), t)
+
+
+def test_int8_cache_decodes_like_its_dequantised_f32_cache():
+    """Attention over an int8 cache with scale 2^-4 equals attention over the f32 cache
+    holding code * 2^-4 (exact in f32), through the oracle's decode path."""
+    from oracle import paged
+    rng = np.random.default_rng(4)
+    bs, nkv, hd, nb = 4, 2, 8, 6
+    kc = rng.integers(-127, 128, size=(nb, bs, nkv, hd)).astype(np.int8).view(np.uint8)
+    vc = rng.integers(-127, 128, size=(nb, bs, nkv, hd)).astype(np.int8).view(np.uint8)
+    sc = 2.0 ** -4
+    kf = (kc.view(np.int8).astype(np.float32) * np.float32(sc)).view(np.uint32)
+    vf = (vc.view(np.int8).astype(np.float32) * np.float32(sc)).view(np.uint32)
+    q = rng.standard_normal((2, 2 * nkv, hd)).astype(np.float32).view(np.uint32)
+    tables = np.array([[3, 0, 5], [1, 4, -1]])
+    ctx = np.array([11, 6])
+    a = paged.decode(q, "f32", kc, vc, "int8", tables, ctx, bs, 2, 0.3, sc, sc)
+    b = paged.decode(q, "f32", kf, vf, "f32", tables, ctx, bs, 2, 0.3)
+    assert np.array_equal(a, b)

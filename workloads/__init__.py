@@ -34,14 +34,15 @@ import numpy as np
 
 # Bit patterns used to fill the pool before anything is appended.  They are
 # NaNs, so any read of a slot that no token owns shows up in the results.
-POISON = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F)}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+POISON = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F),
+          "int8": np.uint8(0x80)}       # int8: -128, outside the code range [-127, 127]
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 @dataclasses.dataclass
 class Workload:
     name: str
-    cache_dtype: str            # "f32" | "bf16" | "fp8"
+    cache_dtype: str            # "f32" | "bf16" | "fp8" | "int8"
     q_dtype: str                # "f32" | "bf16"   (output dtype == q dtype)
     src_dtype: str              # dtype of K/V handed to the append call
     n_q_heads: int
@@ -175,13 +176,14 @@ def draw_values(w: Workload, device: str = "cpu") -> Workload:
     w.res_v = _draw(g, (int(w.res_len.sum()), nkv, hd), w.src_dtype, w.value_std, device)
     w.new_k = _draw(g, (int(w.new_len.sum()), nkv, hd), w.src_dtype, w.value_std, device)
     w.new_v = _draw(g, (int(w.new_len.sum()), nkv, hd), w.src_dtype, w.value_std, device)
-    if w.cache_dtype == "fp8":
-        # per-tensor scales: amax / 448 (largest finite e4m3 magnitude), fp32
+    if w.cache_dtype in ("fp8", "int8"):
+        # per-tensor scales: amax / 448 (largest finite e4m3 magnitude) or amax / 127, fp32
         import torch
+        top = np.float32(448.0 if w.cache_dtype == "fp8" else 127.0)
         ka = torch.maximum(w.res_k.float().abs().amax(), w.new_k.float().abs().amax()) if w.new_k.numel() else w.res_k.float().abs().amax()
         va = torch.maximum(w.res_v.float().abs().amax(), w.new_v.float().abs().amax()) if w.new_v.numel() else w.res_v.float().abs().amax()
-        w.k_scale = float(np.float32(float(ka)) / np.float32(448.0))
-        w.v_scale = float(np.float32(float(va)) / np.float32(448.0))
+        w.k_scale = float(np.float32(float(ka)) / top)
+        w.v_scale = float(np.float32(float(va)) / top)
     return w
 
 
