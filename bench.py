@@ -12,7 +12,7 @@ Inputs are resident in HBM before timing.  Several copies of the pool are
 rotated so a step never finds the previous step's K/V in L2 or the MALL.
 Prints ONE JSON line on stdout (human-readable detail goes to stderr).
 
-    python bench.py [--steps K] [--warmup W] [--workload llama3-gqa|llama2|longtail|longtail-fp8]
+    python bench.py [--steps K] [--warmup W] [--workload llama3-gqa|llama2|longtail|longtail-fp8|...]
 """
 from __future__ import annotations
 
@@ -34,6 +34,7 @@ WORKLOADS = {
     "llama2": (2, "bf16"),
     "longtail": (4, "bf16"),
     "longtail-fp8": (4, "fp8"),
+    "longtail-int8": (4, "int8"),
     "mixed": (5, "bf16"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -54,7 +55,7 @@ def prefill_flops(w):
 
 def byte_model(w):
     """Algorithmic bytes of one step (what the method must move)."""
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.cache_dtype]
     qb = {"f32": 4, "bf16": 2}[w.q_dtype]
     sb = {"f32": 4, "bf16": 2}[w.src_dtype]
     nkv, hd, bs = w.n_kv_heads, w.head_dim, w.block_size
@@ -113,11 +114,12 @@ def cpu_baseline(w, budget_s: float):
 
     rows = list(w.decode_rows)
     src = w.src_dtype
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.cache_dtype]
     res_cu, new_cu = w.cu(w.res_len), w.cu(w.new_len)
     qc = codes(w.q, w.q_dtype)
     done, t_total, nbytes = 0, 0.0, 0.0
-    poison = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F)}
+    poison = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F),
+              "int8": np.uint8(0x80)}
     pk = np.full((w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim), poison[w.cache_dtype])
     pv = pk.copy()
     with threadpool_limits(limits=1):
@@ -336,7 +338,7 @@ def main():
                               args.split_tokens)
         if ev is not None:
             ev[1].record(stream)
-        pa.pa_decode_merge(out, ctx, w.n_kv_heads, maxc, ws, w.v_scale if w.cache_dtype == "fp8" else 1.0,
+        pa.pa_decode_merge(out, ctx, w.n_kv_heads, maxc, ws, w.v_scale if w.cache_dtype in ("fp8", "int8") else 1.0,
                            args.split_tokens)
 
     for i in range(args.warmup):

@@ -68,7 +68,8 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_F32 = 0,              /* IEEE binary32 */
   PA_BF16 = 1,             /* bfloat16 */
-  PA_FP8_E4M3 = 2          /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF) */
+  PA_FP8_E4M3 = 2,         /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF) */
+  PA_INT8 = 3              /* symmetric int8 codes in [-127, 127] (cache only) */
 } pa_dtype;
 
 /* Human-readable name of a status code.  Never NULL. */
@@ -114,8 +115,13 @@ pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
  *   (F32 or BF16); for an FP8_E4M3 cache (src F32 or BF16) it is
  *     e4m3_satfinite_rne( float(x) * (1.0f / scale) )
  *   with the inverse computed once in binary32 on the host, the magnitude
- *   clamped to 448 (infinities too), ties rounded to even, NaN -> 0x7F.
- *   k_scale / v_scale are the per-tensor scales (read only for FP8 caches).
+ *   clamped to 448 (infinities too), ties rounded to even, NaN -> 0x7F; for
+ *   an INT8 cache (src F32 or BF16; the 8-bit step of "From PagedAttention to
+ *   Chunked Prefill", section 5.4) it is
+ *     clamp(rint_ties_even( float(x) * (1.0f / scale) ), -127, 127)
+ *   with NaN -> 0.
+ *   k_scale / v_scale are the per-tensor scales (read only for FP8 and INT8
+ *   caches).
  *
  *   k_new, v_new  [num_tokens][n_kv_heads][head_dim] of src_dtype (contiguous)
  *   slot_mapping  int64 [num_tokens], distinct non-negative entries
@@ -151,13 +157,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads, int32_t n_
  *   M = max m_k, O = sum_k e^{m_k - M} O_k / sum_k e^{m_k - M} l_k.
  *
  *   out[s][h][:] = sum_j softmax_j(scale * q[s][h] . K_s[j][h/g]) V_s[j][h/g][:],
- *   j < context_lens[s]; a sequence with context 0 gets zeros.  For FP8 caches
- *   the stored codes are multiplied by k_scale / v_scale.
+ *   j < context_lens[s]; a sequence with context 0 gets zeros.  For FP8 and
+ *   INT8 caches the stored codes are multiplied by k_scale / v_scale.
  *
  *   out           [num_seqs][n_q_heads][head_dim], dtype = q_dtype (bf16 output is
  *                 rounded to nearest even)
  *   q             [num_seqs][n_q_heads][head_dim] of q_dtype
- *   dtype pairs   (q, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}
+ *   dtype pairs   (q, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ *                 (BF16, INT8)}
  *   head_dim      64 or 128;  block_size a power of two in [1, 256];
  *   group_size    1, 2, 4 or 8
  *   max_context_len  host-side upper bound of context_lens (sizes the plan)
@@ -202,7 +209,7 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *   out, q        [total_q][n_q_heads][head_dim] bf16 (q_dtype must be BF16)
  *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[num_seqs] == total_q
  *   max_q_len     host-side upper bound of the L_s
- *   cache_dtype   BF16 or FP8_E4M3 (codes times k_scale / v_scale)
+ *   cache_dtype   BF16, FP8_E4M3 or INT8 (codes times k_scale / v_scale)
  *   head_dim      64 or 128; block_size a power of two in [1, 256];
  *   group_size    1, 2, 4 or 8
  *   scale         positive and finite, else PA_ERR_SHAPE
@@ -232,7 +239,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
  *
  * pa_decode_merge combines them (M = max m_k, out = out_scale * sum_k 2^{m_k-M} O_k /
  * sum_k 2^{m_k-M} l_k; zeros for context 0) and writes `out` in out_dtype (F32
- * or BF16).  out_scale is v_scale for FP8 caches and 1 otherwise.  It must be
+ * or BF16).  out_scale is v_scale for FP8 and INT8 caches and 1 otherwise.  It must be
  * called with the num_seqs, head counts, head_dim, max_context_len,
  * split_tokens and context_lens of the partials call it follows.
  */

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # PA_LIB may name another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIB") or os.path.join(_HERE, "libpa.so")
 
-PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
            4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
 
@@ -71,6 +71,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PA_BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return PA_FP8_E4M3
+    if t.dtype == torch.int8:
+        return PA_INT8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -63,7 +63,8 @@ extern "C" pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_bl
   if (dst_num_blocks < 0 || src_num_blocks < 0 || block_size < 1 || n_kv_heads < 1 ||
       head_dim < 1 || num_pairs < 0)
     return PA_ERR_SHAPE;
-  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3)
+  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 &&
+      cache_dtype != PA_INT8)
     return PA_ERR_DTYPE;
   const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
   const int64_t block_bytes = (int64_t)block_size * n_kv_heads * head_dim * eb;

@@ -25,7 +25,7 @@
 //     on the dims of lane column c = l & 7.  One 16-byte load per lane covers 8
 //     tokens x 128 contiguous bytes: whole cache lines, fully coalesced, with no
 //     LDS round trip (each byte is used by exactly one lane).
-//   * Scores: v_dot2_f32_bf16 over bf16 pairs (fp8 codes are widened to bf16
+//   * Scores: v_dot2_f32_bf16 over bf16 pairs (fp8 and int8 codes are widened to bf16
 //     pairs exactly with the gfx950 pair converter), then a 3-step DPP sum over
 //     the 8 lanes of the token.
 //   * Softmax is lane-local: each group of 8 lanes keeps its own running max,
@@ -254,11 +254,11 @@ __device__ __forceinline__ void lane_scores(const DecodeState<CDT, HD, G>& st,
     for (int i = 0; i < L::DW; ++i)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = dot2_bf16(st.q[h][i], kd[i], s[h]);
-  } else if constexpr (CDT == PA_FP8_E4M3) {
+  } else if constexpr (CDT == PA_FP8_E4M3 || CDT == PA_INT8) {
 #pragma unroll
     for (int i = 0; i < L::DW; ++i) {
-      const uint32_t lo = fp8x2_to_bf16x2<false>(kd[i]);
-      const uint32_t hi = fp8x2_to_bf16x2<true>(kd[i]);
+      const uint32_t lo = code8x2_to_bf16x2<CDT, false>(kd[i]);
+      const uint32_t hi = code8x2_to_bf16x2<CDT, true>(kd[i]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         s[h] = dot2_bf16(st.q[h][2 * i], lo, s[h]);
@@ -332,10 +332,10 @@ __device__ __forceinline__ void process_step(DecodeState<CDT, HD, G>& st,
     } else {
 #pragma unroll
       for (int i = 0; i < L::DW; ++i) {
-        const uint32_t a0 = fp8x2_to_bf16x2<false>(f.v[0][i]);
-        const uint32_t b0 = fp8x2_to_bf16x2<false>(f.v[1][i]);
-        const uint32_t a1 = fp8x2_to_bf16x2<true>(f.v[0][i]);
-        const uint32_t b1 = fp8x2_to_bf16x2<true>(f.v[1][i]);
+        const uint32_t a0 = code8x2_to_bf16x2<CDT, false>(f.v[0][i]);
+        const uint32_t b0 = code8x2_to_bf16x2<CDT, false>(f.v[1][i]);
+        const uint32_t a1 = code8x2_to_bf16x2<CDT, true>(f.v[0][i]);
+        const uint32_t b1 = code8x2_to_bf16x2<CDT, true>(f.v[1][i]);
         const uint32_t d0 = pair_lo(a0, b0), d1 = pair_hi(a0, b0);
         const uint32_t d2 = pair_lo(a1, b1), d3 = pair_hi(a1, b1);
 #pragma unroll
@@ -836,7 +836,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
   if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
   const bool pair_ok = (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
-                       (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3));
+                       (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3 ||
+                                                 cache_dtype == PA_INT8));
   if (!pair_ok) return PA_ERR_DTYPE;
   if (num_seqs == 0) return PA_OK;
   if ((merge && !out) || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -845,7 +846,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   const WsLayout l = ws_layout(
       entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
-  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  // 8-bit caches (fp8 or int8) carry per-tensor scales
+  const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
 
   char* base = (char*)workspace;
@@ -877,6 +879,7 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   bool ok = false;
   if (cache_dtype == PA_BF16) ok = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
   else if (cache_dtype == PA_FP8_E4M3) ok = dispatch_hd<PA_FP8_E4M3>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (cache_dtype == PA_INT8) ok = dispatch_hd<PA_INT8>(head_dim, G, a, split_tokens, max_context_len, st);
   else ok = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;

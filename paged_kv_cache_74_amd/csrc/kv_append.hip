@@ -64,6 +64,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// int8 encoder: round half to even, clamp to [-127, 127], NaN -> 0.  (The
+// clamp before the rounding changes no result: every value beyond +-127 ends
+// at +-127 either way.)
+__device__ __forceinline__ uint32_t f32_to_int8(float x) {
+  if (!(x == x)) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
+template <int DST>
+__device__ __forceinline__ uint32_t encode8(float x) {
+  if constexpr (DST == PA_FP8_E4M3) return f32_to_e4m3(x);
+  else return f32_to_int8(x);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming 16-byte read of source rows (read once, not kept in cache).
@@ -91,31 +106,31 @@ struct AppendIO<PA_F32, PA_F32> {
     ((uint4*)dst)[1] = b;
   }
 };
-// Encodes: 8 elements in, 8 bytes out.
-template <>
-struct AppendIO<PA_BF16, PA_FP8_E4M3> {
+// Encodes (FP8_E4M3 or INT8): 8 elements in, 8 bytes out.
+template <int DST>
+struct AppendIO<PA_BF16, DST> {
   static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float inv) {
     const uint4 a = ld_stream(src);
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f32_to_e4m3(bf16lo_f32(w[i]) * inv);
-      const uint32_t hi = f32_to_e4m3(bf16hi_f32(w[i]) * inv);
+      const uint32_t lo = encode8<DST>(bf16lo_f32(w[i]) * inv);
+      const uint32_t hi = encode8<DST>(bf16hi_f32(w[i]) * inv);
       out[i >> 1] |= (lo | (hi << 8)) << ((i & 1) * 16);
     }
     *(uint2*)dst = make_uint2(out[0], out[1]);
   }
 };
-template <>
-struct AppendIO<PA_F32, PA_FP8_E4M3> {
+template <int DST>
+struct AppendIO<PA_F32, DST> {
   static __device__ __forceinline__ void run(const uint8_t* src, uint8_t* dst, float inv) {
     const uint4 a = ld_stream(src);
     const uint4 b = ld_stream(src + 16);
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t out[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[i >> 2] |= f32_to_e4m3(bits_f32(w[i]) * inv) << ((i & 3) * 8);
+    for (int i = 0; i < 8; ++i) out[i >> 2] |= encode8<DST>(bits_f32(w[i]) * inv) << ((i & 3) * 8);
     *(uint2*)dst = make_uint2(out[0], out[1]);
   }
 };
@@ -205,17 +220,17 @@ extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
   } else if (cache_dtype == src_dtype && cache_dtype == PA_F32) {
     hipLaunchKernelGGL((kv_append_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc, kn,
                        vn, slot_mapping, pool_slots, lanes_per_token, total, 1.0f, 1.0f);
-  } else if (cache_dtype == PA_FP8_E4M3 && (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
+  } else if ((cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8) &&
+             (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
     if (!(k_scale > 0.0f) || !(v_scale > 0.0f)) return PA_ERR_SHAPE;
     const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;   // one binary32 division each
-    if (src_dtype == PA_BF16)
-      hipLaunchKernelGGL((kv_append_kernel<PA_BF16, PA_FP8_E4M3>), grid, dim3(256), 0, st, kc,
-                         vc, kn, vn, slot_mapping, pool_slots, lanes_per_token, total, k_inv,
-                         v_inv);
-    else
-      hipLaunchKernelGGL((kv_append_kernel<PA_F32, PA_FP8_E4M3>), grid, dim3(256), 0, st, kc,
-                         vc, kn, vn, slot_mapping, pool_slots, lanes_per_token, total, k_inv,
-                         v_inv);
+    const bool i8 = cache_dtype == PA_INT8;
+    auto kernel = src_dtype == PA_BF16 ? (i8 ? kv_append_kernel<PA_BF16, PA_INT8>
+                                             : kv_append_kernel<PA_BF16, PA_FP8_E4M3>)
+                                       : (i8 ? kv_append_kernel<PA_F32, PA_INT8>
+                                             : kv_append_kernel<PA_F32, PA_FP8_E4M3>);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, slot_mapping, pool_slots,
+                       lanes_per_token, total, k_inv, v_inv);
   } else {
     return PA_ERR_DTYPE;
   }

@@ -40,6 +40,23 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Two int8 codes (bytes 0, 1 of `src`, or 2, 3 when HI) -> a bf16 pair.  Every
+// integer in [-128, 127] is exact in bf16, so the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t src) {
+  const int32_t x = (int32_t)src;
+  const float a = (float)((x << (HI ? 8 : 24)) >> 24);
+  const float b = (float)((x << (HI ? 0 : 16)) >> 24);
+  return pack_bf16(a, b);
+}
+
+// Two 8-bit cache codes (fp8 e4m3 or int8) -> a bf16 pair, exactly.
+template <int CDT, bool HI>
+__device__ __forceinline__ uint32_t code8x2_to_bf16x2(uint32_t src) {
+  if constexpr (CDT == PA_INT8) return i8x2_to_bf16x2<HI>(src);
+  else return fp8x2_to_bf16x2<HI>(src);
+}
+
 // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

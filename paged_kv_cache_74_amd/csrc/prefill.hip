@@ -76,7 +76,7 @@ struct PrefillArgs {
   int nseg;
   int causal;
   float score_scale;         // scale * k_scale * log2(e)
-  float out_scale;           // v_scale for fp8 caches, else 1
+  float out_scale;           // v_scale for 8-bit caches, else 1
 };
 
 template <int CDT, int HD>
@@ -193,7 +193,7 @@ __device__ __forceinline__ void load8(const uint8_t* p, uint32_t (&d)[4]) {
   if constexpr (CDT == PA_BF16) {
     const uint4 x = *(const uint4*)p;
     d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-  } else {   // fp8 e4m3 codes: keep the raw bytes, widened when stored to LDS
+  } else {   // 8-bit codes: keep the raw bytes, widened when stored to LDS
     const uint2 x = *(const uint2*)p;
     d[0] = x.x; d[1] = x.y; d[2] = 0u; d[3] = 0u;
   }
@@ -201,10 +201,10 @@ __device__ __forceinline__ void load8(const uint8_t* p, uint32_t (&d)[4]) {
 
 template <int CDT>
 __device__ __forceinline__ void widen(uint32_t (&d)[4]) {
-  if constexpr (CDT == PA_FP8_E4M3) {   // 8 e4m3 codes -> 4 bf16 pairs (exact)
+  if constexpr (CDT == PA_FP8_E4M3 || CDT == PA_INT8) {   // 8 codes -> 4 bf16 pairs (exact)
     const uint32_t x = d[0], y = d[1];
-    d[0] = fp8x2_to_bf16x2<false>(x); d[1] = fp8x2_to_bf16x2<true>(x);
-    d[2] = fp8x2_to_bf16x2<false>(y); d[3] = fp8x2_to_bf16x2<true>(y);
+    d[0] = code8x2_to_bf16x2<CDT, false>(x); d[1] = code8x2_to_bf16x2<CDT, true>(x);
+    d[2] = code8x2_to_bf16x2<CDT, false>(y); d[3] = code8x2_to_bf16x2<CDT, true>(y);
   }
 }
 
@@ -605,12 +605,14 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
   if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
     return PA_ERR_UNSUPPORTED;
-  if (q_dtype != PA_BF16 || (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3))
+  if (q_dtype != PA_BF16 ||
+      (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_INT8))
     return PA_ERR_DTYPE;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
-  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  // 8-bit caches (fp8 or int8) carry per-tensor scales
+  const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
   // the kernel takes row maxima of the unscaled scores
   if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
@@ -650,9 +652,12 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   if (cache_dtype == PA_BF16)
     ok = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128>(group_size, a, l, ws, st)
                          : pf_dispatch_g<PA_BF16, 64>(group_size, a, l, ws, st);
-  else
+  else if (cache_dtype == PA_FP8_E4M3)
     ok = head_dim == 128 ? pf_dispatch_g<PA_FP8_E4M3, 128>(group_size, a, l, ws, st)
                          : pf_dispatch_g<PA_FP8_E4M3, 64>(group_size, a, l, ws, st);
+  else
+    ok = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128>(group_size, a, l, ws, st)
+                         : pf_dispatch_g<PA_INT8, 64>(group_size, a, l, ws, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

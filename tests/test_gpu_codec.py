@@ -1,4 +1,4 @@
-"""The fp8 (OCP e4m3fn) encoder of pa_kv_append against the oracle's, bit for bit.
+"""The fp8 (OCP e4m3fn) and int8 encoders of pa_kv_append against the oracle's, bit for bit.
 
 bf16 sources: every one of the 65536 bit patterns.  fp32 sources: every
 rounding boundary of the format (each midpoint between neighbouring codes and
@@ -29,8 +29,9 @@ def dev():
     return torch.device("cuda")
 
 
-def _encode_on_gpu(dev, src_codes: np.ndarray, src: str, scale: float) -> np.ndarray:
-    """Append the values as K rows of an fp8 pool; return the pool bytes in order."""
+def _encode_on_gpu(dev, src_codes: np.ndarray, src: str, scale: float,
+                   cache=torch.uint8) -> np.ndarray:
+    """Append the values as K rows of an 8-bit pool; return the pool bytes in order."""
     n = src_codes.size
     pad = (-n) % HD
     codes = np.concatenate([src_codes, np.zeros(pad, src_codes.dtype)])
@@ -41,13 +42,13 @@ def _encode_on_gpu(dev, src_codes: np.ndarray, src: str, scale: float) -> np.nda
     else:
         x = torch.from_numpy(codes.astype(np.uint32).view(np.int32)).view(torch.float32)
     x = x.reshape(T, NKV, HD).to(dev)
-    k = torch.zeros((nb, BS, NKV, HD), dtype=torch.uint8, device=dev)
+    k = torch.zeros((nb, BS, NKV, HD), dtype=cache, device=dev)
     v = torch.zeros_like(k)
     slots = torch.arange(T, dtype=torch.int64, device=dev)
     pa.pa_kv_append(k, v, x, x, slots, scale, scale)
     torch.cuda.synchronize()
-    out = k.reshape(-1)[: T * HD].cpu().numpy()
-    assert np.array_equal(out, v.reshape(-1)[: T * HD].cpu().numpy())
+    out = k.view(torch.uint8).reshape(-1)[: T * HD].cpu().numpy()
+    assert np.array_equal(out, v.view(torch.uint8).reshape(-1)[: T * HD].cpu().numpy())
     return out[:n]
 
 
@@ -89,5 +90,26 @@ def test_fp8_encode_f32_random_patterns(dev, scale):
     codes = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
     got = _encode_on_gpu(dev, codes, "f32", scale)
     want = encode_tokens(codes, "f32", "fp8", scale)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 3.0e-3, 11.0])
+def test_int8_encode_every_bf16_pattern(dev, scale):
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    got = _encode_on_gpu(dev, codes, "bf16", scale, torch.int8)
+    want = encode_tokens(codes, "bf16", "int8", scale)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+def test_int8_encode_f32_ties_and_random_patterns(dev):
+    halves = (np.arange(-130, 130) + 0.5).astype(np.float32).view(np.uint32)
+    around = np.concatenate([halves - 1, halves, halves + 1]).astype(np.uint32)
+    rng = np.random.default_rng(6)
+    codes = np.concatenate([around, rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64)
+                            .astype(np.uint32)])
+    got = _encode_on_gpu(dev, codes, "f32", 1.0, torch.int8)
+    want = encode_tokens(codes, "f32", "int8", 1.0)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(hex(int(codes[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]

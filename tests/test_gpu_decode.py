@@ -6,7 +6,7 @@ compared in full; the full-size configurations in the launch configuration the
 benchmark times are compared on sampled sequences.
 
 Bars: integer and byte results bit-exact; fp32 outputs within 1e-5 normwise
-relative error per row (max|g - r| / max|r|); bf16 / fp8-KV outputs within
+relative error per row (max|g - r| / max|r|); bf16 / fp8- and int8-KV outputs within
 2e-2 absolute AND 1e-2 normwise relative error per row.
 """
 import numpy as np
@@ -18,7 +18,8 @@ from helpers import (blocks_of, codes, normwise_rel, oracle_decode, oracle_pools
 
 pytestmark = pytest.mark.gpu
 
-DECODE_CASES = [(1, "f32"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (4, "fp8"), (5, "bf16")]
+DECODE_CASES = [(1, "f32"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (4, "fp8"), (4, "int8"),
+                (5, "bf16")]
 
 
 def _small(cfg, kv="bf16", seed=0):
@@ -97,7 +98,7 @@ def test_decode_matches_oracle(dev, cfg, kv, split):
     check_close(out, ref, w.q_dtype, f"cfg{cfg}/{kv}/split{split}")
 
 
-@pytest.mark.parametrize("cfg,kv", [(2, "bf16"), (3, "bf16"), (4, "fp8")])
+@pytest.mark.parametrize("cfg,kv", [(2, "bf16"), (3, "bf16"), (4, "fp8"), (4, "int8")])
 def test_decode_peaked_scores(dev, cfg, kv):
     """q scaled by 16 (exact in bf16): sharper softmax, larger dynamic range."""
     from gpu_harness import DeviceWorkload, to_f64
@@ -195,7 +196,8 @@ def _sample_rows(w, k=4, seed=0):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("cfg,kv", [(2, "bf16"), (3, "bf16"), (4, "bf16"), (4, "fp8"), (5, "bf16")])
+@pytest.mark.parametrize("cfg,kv", [(2, "bf16"), (3, "bf16"), (4, "bf16"), (4, "fp8"), (4, "int8"),
+                                    (5, "bf16")])
 def test_full_size_decode_sampled(dev, cfg, kv):
     from gpu_harness import DeviceWorkload, to_f64
     print(f"full-size decode cfg{cfg} {kv}", flush=True)

@@ -1,6 +1,6 @@
 """GPU parity of the chunked-prefill kernel (MFMA) against the oracle.
 
-Bars: bf16 / fp8-KV outputs within 2e-2 absolute and 1e-2 normwise relative
+Bars: bf16 / fp8- and int8-KV outputs within 2e-2 absolute and 1e-2 normwise relative
 error per row; a chunk of length 1 must agree with the decode kernel.
 """
 import numpy as np
@@ -55,12 +55,13 @@ def test_prefill_shapes(dev, nq, nkv, hd, bs):
     check_close(got, ref, "bf16", f"prefill {nq}/{nkv}/{hd}/bs{bs}")
 
 
-def test_prefill_fp8_cache(dev):
+@pytest.mark.parametrize("kv", ["fp8", "int8"])
+def test_prefill_8bit_cache(dev, kv):
     w = workloads.mixed_prefill_decode(prior=(0, 77, 700), chunk_lens=(64, 100, 37), n_decode=3,
-                                       dlo=1, dhi=200, seed=2, kv="fp8")
+                                       dlo=1, dhi=200, seed=2, kv=kv)
     workloads.draw_values(w, "cpu")
     got, ref = _run(w, dev)
-    check_close(got, ref, "bf16", "prefill fp8")
+    check_close(got, ref, "bf16", f"prefill {kv}")
 
 
 def test_prefill_peaked_scores(dev):
