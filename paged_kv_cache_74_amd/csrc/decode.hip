@@ -613,24 +613,55 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     const int64_t g0 = (int64_t)pre + (int64_t)hg * steps;
     const int g = s * nhg + hg;
     const int w0 = wave_of(g0, U, num_wgs), w1 = wave_of(g0 + steps - 1, U, num_wgs);
-    // one pass, online over the pieces (workgroups with an empty unit range,
-    // which occur only when they outnumber units, hold no piece)
-    float M = -INFINITY, lsum = 0.0f;
-#pragma unroll 4
-    for (int w = w0; w <= w1; ++w) {
-      if (wave_begin(w, U, num_wgs) >= wave_begin(w + 1, U, num_wgs)) continue;
-      const int64_t sl = (((int64_t)w + g) * hw + wv) * G + hl;
-      const float2 ml = *(const float2*)(part_ml + sl * 2);
-      float o[DPT];
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) o[i] = part_o[sl * HD + t * DPT + i];
-      const float Mn = fmaxf(M, ml.x);
-      const float a = fast_exp2(M - Mn), b = fast_exp2(ml.x - Mn);
-      lsum = lsum * a + ml.y * b;
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = acc[i] * a + o[i] * b;
-      M = Mn;
+    const int npc = w1 - w0 + 1;
+    // Lane k holds piece w0 + b + k of a sweep over 64 pieces: first the max M
+    // of the pieces' m, then each piece's weight 2^(m_k - M), broadcast while
+    // every lane sums its dims of the weighted O.  A workgroup with an empty
+    // unit range (only when workgroups outnumber units) holds no piece; it and
+    // the lanes past the last piece get weight 0 and read piece w0's O, which
+    // always exists, so the O loads go out four at a time with no tail loop.
+    // Most rows have at most 64 pieces: their m and l are loaded once.
+    auto entry = [&](int w) -> int64_t { return (((int64_t)w + g) * hw + wv) * G + hl; };
+    auto piece_ml = [&](int b, bool* has) -> float2 {
+      const int w = w0 + b + t;
+      *has = w <= w1 && wave_begin(w, U, num_wgs) < wave_begin(w + 1, U, num_wgs);
+      return *has ? *(const float2*)(part_ml + entry(w) * 2) : make_float2(-INFINITY, 0.0f);
+    };
+    bool has0;
+    const float2 ml0 = piece_ml(0, &has0);
+    float M = ml0.x;
+    for (int b = 64; b < npc; b += 64) {
+      bool has;
+      M = fmaxf(M, piece_ml(b, &has).x);
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float lsum = 0.0f;
+    for (int b = 0; b < npc; b += 64) {
+      bool has = has0;
+      const float2 ml = b == 0 ? ml0 : piece_ml(b, &has);
+      const uint64_t present = __ballot(has);
+      const float wk = has ? fast_exp2(ml.x - M) : 0.0f;
+      lsum += ml.y * wk;
+      const int n = min(64, npc - b);
+      for (int j = 0; j < n; j += 4) {
+        float o[4][DPT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t sl = entry((present >> (j + u)) & 1 ? w0 + b + j + u : w0);
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) o[u][i] = part_o[sl * HD + t * DPT + i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wj = __shfl(wk, j + u, 64);
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) acc[i] += wj * o[u][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
     inv = v_scale / lsum;
   }
   if constexpr (OUT_BF16) {
