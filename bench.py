@@ -44,10 +44,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_flops(w):
+def prefill_flops(w, seqs=None):
     """4 * head_dim * n_q_heads flops per visible (query, key) pair (QK^T and PV)."""
     pairs = 0
-    for s in range(w.num_prefill_seqs):
+    for s in range(w.num_prefill_seqs) if seqs is None else seqs:
         L, T = int(w.q_lens[s]), int(w.context_lens[s])
         pairs += L * (T - L) + L * (L + 1) // 2 if w.causal else L * T
     return 4.0 * w.head_dim * w.n_q_heads * pairs
@@ -253,6 +253,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="mixed workload: chunks and decode rows in one pa_prefill_chunk call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for scaling HBM counters)")
     args = ap.parse_args()
@@ -314,11 +316,20 @@ def main():
     stream = torch.cuda.current_stream()
 
     P = w.num_prefill_seqs
+    one = args.one_launch
+    if one and not P:
+        log("--one-launch needs a workload with prefill chunks (mixed)")
+        sys.exit(2)
     if P:
-        pf_cu = i32(w.cu(w.q_lens[:P]), dev)
-        pf_q = dw.q[: int(w.q_lens[:P].sum())]
+        # one launch: the whole batch (chunks, then the decode rows as chunks of
+        # one query); else the chunks only, the decode rows going to pa_decode
+        PB = w.num_seqs if one else P
+        pf_cu = i32(w.cu(w.q_lens[:PB]), dev)
+        pf_q = dw.q[: int(w.q_lens[:PB].sum())]
         pf_out = torch.empty_like(pf_q)
-        pf_maxq, pf_maxc = int(w.q_lens[:P].max()), int(w.context_lens[:P].max())
+        pf_maxq, pf_maxc = int(w.q_lens[:PB].max()), int(w.context_lens[:PB].max())
+        pf_ws = pa.workspace(pa.pa_prefill_workspace_bytes(
+            PB, pf_q.shape[0], pf_maxq, w.n_q_heads, w.n_kv_heads, w.head_dim, pf_maxc), dev)
 
     def step(i, ev=None, pev=None):
         kc, vc = pools[i % len(pools)]
@@ -327,11 +338,13 @@ def main():
         if P:
             if pev is not None:
                 pev[0].record(stream)
-            pa.pa_prefill_chunk(pf_q, kc, vc, pf_cu, dw.tables[:P], dw.ctx[:P], pf_maxq, pf_maxc,
+            pa.pa_prefill_chunk(pf_q, kc, vc, pf_cu, dw.tables[:PB], dw.ctx[:PB], pf_maxq, pf_maxc,
                                 w.scale, causal=True, k_scale=w.k_scale, v_scale=w.v_scale,
-                                out=pf_out)
+                                out=pf_out, ws=pf_ws)
             if pev is not None:
                 pev[1].record(stream)
+        if one:
+            return
         if ev is not None:
             ev[0].record(stream)
         pa.pa_decode_partials(q, kc, vc, tables, ctx, maxc, w.scale, ws, w.k_scale,
@@ -360,32 +373,46 @@ def main():
     for i in range(args.steps):
         step(i, events[i], pevents[i])
     torch.cuda.synchronize()
-    split_ms = np.array([a.elapsed_time(b) for a, b in events])
+    split_ms = np.array([a.elapsed_time(b) for a, b in events]) if not one else None
     prefill_ms = np.array([a.elapsed_time(b) for a, b in pevents]) if P else None
 
     bm = byte_model(w)
     ms_step = wall * 1e3 / args.steps
     step_gbs = bm["step"] / (ms_step * 1e-3) / 1e9
-    split_avg = float(split_ms.mean())
-    achieved = bm["split_kernel"] / (split_avg * 1e-3) / 1e9
     ctx_tokens = float(w.context_lens[list(w.decode_rows)].sum())
-    log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s); split kernel avg {split_avg * 1e3:.1f} us "
-        f"(p10 {np.percentile(split_ms, 10) * 1e3:.1f}, p90 {np.percentile(split_ms, 90) * 1e3:.1f}) "
-        f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; "
-        f"KV unique {bm['kv_unique'] / 1e9:.3f} GB, logical {bm['kv_logical'] / 1e9:.3f} GB")
+    if not one:
+        split_avg = float(split_ms.mean())
+        achieved = bm["split_kernel"] / (split_avg * 1e-3) / 1e9
+        log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s); split kernel avg {split_avg * 1e3:.1f} us "
+            f"(p10 {np.percentile(split_ms, 10) * 1e3:.1f}, p90 {np.percentile(split_ms, 90) * 1e3:.1f}) "
+            f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; "
+            f"KV unique {bm['kv_unique'] / 1e9:.3f} GB, logical {bm['kv_logical'] / 1e9:.3f} GB")
 
     prefill_rec = None
     if P:
-        fl = prefill_flops(w)
+        fl = prefill_flops(w, range(PB))
         pf_avg = float(prefill_ms.mean())
         tf = fl / (pf_avg * 1e-3) / 1e12
-        prefill_rec = {"kernel": "prefill_kernel (pa_prefill_chunk)", "bound": "mfma",
+        what = ("pa_prefill_chunk: chunks and decode rows, one launch" if one
+                else "pa_prefill_chunk")
+        prefill_rec = {"kernel": f"prefill_kernel ({what})", "bound": "mfma",
                        "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "traffic": measured_traffic(args.workload, "prefill_kernel", PREFILL_SOURCES),
+                       "traffic": measured_traffic(args.workload + ("-one" if one else ""),
+                                                   "prefill_kernel", PREFILL_SOURCES),
                        "avg_launch_us": round(pf_avg * 1e3, 2), "flops_per_launch": fl}
         log(f"prefill avg {pf_avg * 1e3:.1f} us -> {tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
             f"of the bf16 MFMA peak ({fl / 1e9:.1f} GFLOP)")
+        if one:
+            # lower bound of the one launch: the chunks' flops at the MFMA peak
+            # plus the decode rows' bytes at the HBM peak
+            t_min = (prefill_flops(w) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                     + bm["split_kernel"] / (HBM_PEAK_GBS * 1e9))
+            prefill_rec["serial_bound_us"] = round(t_min * 1e6, 2)
+            prefill_rec["frac_of_serial_bound"] = round(t_min / (pf_avg * 1e-3), 4)
+            log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s), one launch; bound "
+                f"{t_min * 1e6:.1f} us (chunk flops at the MFMA peak + decode bytes at the HBM peak) "
+                f"= {t_min / (pf_avg * 1e-3):.1%} of the launch")
 
     cpu = None
     if not args.no_cpu_baseline and not P:
@@ -409,7 +436,9 @@ def main():
         "dtype": "bf16" if w.cache_dtype == "bf16" else f"bf16-q/{w.cache_dtype}-kv",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: paged decode step (slot map + KV append + split-K decode + merge)",
+            "workload": f"{w.name}: " + ("paged step, one attention launch (slot map + KV append + "
+                                         "chunks and decode rows in pa_prefill_chunk)" if one else
+                                         "paged decode step (slot map + KV append + split-K decode + merge)"),
             "batch": B, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.cache_dtype,
             "context_tokens": int(ctx_tokens), "max_context": maxc,
@@ -423,7 +452,7 @@ def main():
         "context_tokens_per_s": round(ctx_tokens / (ms_step * 1e-3), 1),
         "bytes_per_step": {"algorithmic_unique": bm["step"], "kv_unique": bm["kv_unique"],
                            "kv_logical": bm["kv_logical"]},
-        "roofline": {
+        "roofline": prefill_rec if one else {
             "kernel": "decode_split_kernel (pa_decode_partials)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -436,7 +465,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
-    if prefill_rec:
+    if prefill_rec and not one:
         rec["prefill_roofline"] = prefill_rec
     print(json.dumps(rec), flush=True)
 

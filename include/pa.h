@@ -184,7 +184,11 @@ pa_status pa_decode(void* out, const void* q, int q_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_prefill_workspace_bytes -- scratch needed by pa_prefill_chunk (may be 0).
+ * pa_prefill_workspace_bytes -- scratch needed by pa_prefill_chunk (0 for an
+ * empty batch or unsupported head counts).  It grows with num_seqs and
+ * total_q, not with num_seqs times max_q_len: a batch of many decode rows
+ * beside a few long chunks needs little.  The call must pass the same
+ * num_seqs, total_q and max_q_len.
  */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -204,11 +208,19 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *   and attends to keys j <= T_s - L_s + i when causal != 0, to all j < T_s
  *   otherwise:
  *     out[row][h][:] = sum_j softmax_j(scale * q[row][h] . K_s[j][h/g]) V_s[j][h/g][:].
- *   A decode row is the special case L_s = 1.
+ *   A decode row is the special case L_s = 1, so one call (one attention
+ *   launch, plus a small planning launch and a merge launch) serves a mixed
+ *   step: prefill chunks and decode rows side by side, in any order -- the
+ *   engine's view in "From PagedAttention to Chunked Prefill", section 3.2.
+ *   Work is spread over the device in equal shares of 32-key tiles; a short
+ *   chunk occupies only the matrix-core rows it needs.
  *
  *   out, q        [total_q][n_q_heads][head_dim] bf16 (q_dtype must be BF16)
  *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[num_seqs] == total_q
- *   max_q_len     host-side upper bound of the L_s
+ *   max_q_len     host-side upper bound of the L_s.  A cu_seqlens_q that
+ *                 needs more query tiles than total_q and max_q_len allow
+ *                 (the device-side planner checks) is not computed: out is
+ *                 left unwritten and nothing outside the arguments is touched.
  *   cache_dtype   BF16, FP8_E4M3 or INT8 (codes times k_scale / v_scale)
  *   head_dim      64 or 128; block_size a power of two in [1, 256];
  *   group_size    1, 2, 4 or 8

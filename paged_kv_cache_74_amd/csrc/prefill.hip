@@ -62,7 +62,9 @@ struct PrefillArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* seg_cu;     // [nseg + 1] prefix sums of key tiles per segment
+  const int32_t* hdr;        // {segments, key tiles in all}, written by the prep kernel
+  const int32_t* seg_cu;     // [segments + 1] prefix sums of key tiles per segment
+  const int4* seg_desc;      // [segments] {sequence, KV head, query tile, key tiles}
   const int32_t* wg_start;   // [num_wgs][2] first (segment, tile) of each workgroup
   float* part_o;             // [slots][PF_ROWS][HD]   slot = workgroup + segment
   float* part_ml;            // [slots][PF_ROWS][2]
@@ -72,8 +74,7 @@ struct PrefillArgs {
   int bs_log2;
   int n_kv;
   int max_blocks;
-  int qtiles;                // query tiles per sequence (segment enumeration)
-  int nseg;
+  int nseg_max;              // bound on the segments of the batch (workspace size)
   int causal;
   float score_scale;         // scale * k_scale * log2(e)
   float out_scale;           // v_scale for 8-bit caches, else 1
@@ -94,28 +95,19 @@ struct PrefillLds {
 // -- on one XCD, where they share its L2 instead of each fetching from HBM.
 // The renumbering is a bijection of [0, W), so correctness never depends on
 // the dispatch order.
+#ifndef PREFILL_XCD_LOCAL
+#define PREFILL_XCD_LOCAL 1   // 0: workgroup b takes the b-th range of the work order
+#endif
 constexpr int PF_XCDS = 8;
 __device__ __forceinline__ int xcd_local_order(int b, int W) {
+  if (!PREFILL_XCD_LOCAL) return b;
   const int x = b % PF_XCDS, j = b / PF_XCDS;
   return x * (W / PF_XCDS) + min(x, W % PF_XCDS) + j;
 }
 
-// Segment g = (sequence s, KV head kvh, query tile qt); qt varies fastest so a
-// workgroup that runs into the next segment keeps the same K/V.
-__device__ __forceinline__ void seg_decode(int g, int qtiles, int n_kv, int* s, int* kvh, int* qt) {
-  *qt = g % qtiles;
-  const int r = g / qtiles;
-  *kvh = r % n_kv;
-  *s = r / n_kv;
-}
-
 // Key tiles a segment needs: up to its last query's causal limit, or all of T.
-__device__ __forceinline__ int seg_tiles(const int32_t* __restrict__ cu_q,
-                                         const int32_t* __restrict__ context_lens, int s, int qt,
-                                         int QB, int causal) {
-  const int L = cu_q[s + 1] - cu_q[s];
+__device__ __forceinline__ int seg_tiles(int L, int T, int qt, int QB, int causal) {
   if (qt * QB >= L) return 0;
-  const int T = context_lens[s];
   const int last_q = min(L, (qt + 1) * QB) - 1;
   const int visible = causal ? min(T, T - L + last_q + 1) : T;
   return visible > 0 ? (visible + PF_BN - 1) / PF_BN : 0;
@@ -126,48 +118,131 @@ __device__ __forceinline__ int pf_owner(int64_t x, int64_t U, int W) {
   return (int)(((x + 1) * W - 1) / U);
 }
 
-// One workgroup: tile prefix sums over segments and each workgroup's start.
-__global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int QB, int num_wgs,
-                                                            int32_t* __restrict__ seg_cu,
-                                                            int32_t* __restrict__ wg_start) {
-  __shared__ int32_t part[1024];
+// Segments of the ragged batch, in order: for each sequence s, for each KV
+// head, its ceil(L_s / QB) query tiles (query tile fastest, so a workgroup
+// that runs into the next segment keeps the same K/V).  A sequence with L_s = 1
+// (a decode row) has one segment per KV head, a chunk of 512 queries 512 / QB
+// per head: the segment count follows the batch, not num_seqs times its
+// longest chunk.
+
+// Inclusive scan of one int64 per thread over the 1024 threads of the block.
+__device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t* buf) {
   const int t = threadIdx.x;
-  const int per = (a.nseg + 1023) / 1024;
-  const int g0 = min(a.nseg, t * per), g1 = min(a.nseg, g0 + per);
-  int sum = 0;
-  for (int g = g0; g < g1; ++g) {
-    int s, kvh, qt;
-    seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
-    sum += seg_tiles(a.cu_q, a.context_lens, s, qt, QB, a.causal);
-  }
-  part[t] = sum;
+  buf[t] = v;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int v = t >= off ? part[t - off] : 0;
+    const int64_t x = t >= off ? buf[t - off] : 0;
     __syncthreads();
-    part[t] += v;
+    buf[t] += x;
     __syncthreads();
   }
-  int run = part[t] - sum;
-  for (int g = g0; g < g1; ++g) {
-    seg_cu[g] = run;
-    int s, kvh, qt;
-    seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
-    run += seg_tiles(a.cu_q, a.context_lens, s, qt, QB, a.causal);
+  const int64_t r = buf[t];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup builds the work list:
+//   1. each thread counts the segments of a contiguous range of sequences; a
+//      scan gives every sequence its first segment (seq_seg0);
+//   2. each thread takes a contiguous range of segments, writes their
+//      descriptors {sequence, KV head, query tile, key tiles} and sums the
+//      tiles; a scan gives the tile prefix sums seg_cu;
+//   3. each workgroup of the attention kernel gets its first (segment, tile)
+//      by binary search over seg_cu.
+// A batch whose offsets disagree with total_q and max_q_len (an offset
+// outside [0, total_q], a decreasing offset or a chunk longer than max_q_len),
+// which could need more segments than the workspace was sized for or reach
+// rows outside q and out, or one with 2^31 key tiles or more, is given no
+// work: {0, 0} in the header.
+__global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int num_seqs, int total_q,
+                                                            int max_q_len, int QB,
+                                                            int num_wgs, int32_t* __restrict__ hdr,
+                                                            int32_t* __restrict__ seq_seg0,
+                                                            int32_t* __restrict__ seg_cu,
+                                                            int4* __restrict__ seg_desc,
+                                                            int32_t* __restrict__ wg_start) {
+  __shared__ int64_t buf[1024];
+  __shared__ int32_t ok;
+  const int t = threadIdx.x;
+  auto qtiles = [&](int s) {
+    const int L = max(0, a.cu_q[s + 1] - a.cu_q[s]);
+    return (int)(((int64_t)L + QB - 1) / QB);
+  };
+  // 1. segments per sequence
+  const int per_s = (num_seqs + 1023) / 1024;
+  const int s0 = min(num_seqs, t * per_s), s1 = min(num_seqs, s0 + per_s);
+  int64_t cs = 0;
+  int bad = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1];
+    bad |= c0 < 0 || c1 < c0 || c1 > total_q || c1 - c0 > max_q_len;
+    cs += (int64_t)a.n_kv * qtiles(s);
   }
-  if (t == 1023) seg_cu[a.nseg] = part[1023];
+  bad = __syncthreads_or(bad);
+  const int64_t cs_end = block_scan_1024(cs, buf);
+  const int64_t nseg_all = bad ? a.nseg_max + (int64_t)1 : buf[1023];
+  if (nseg_all <= a.nseg_max) {
+    int64_t g = cs_end - cs;
+    for (int s = s0; s < s1; ++s) {
+      seq_seg0[s] = (int)g;
+      g += (int64_t)a.n_kv * qtiles(s);
+    }
+    if (t == 1023) seq_seg0[num_seqs] = (int)g;
+  }
+  const int nseg = nseg_all <= a.nseg_max ? (int)nseg_all : 0;
   __threadfence_block();
   __syncthreads();
-  const int64_t U = part[1023];
+  // 2. descriptors and tile counts, then their prefix sums
+  const int per_g = (nseg + 1023) / 1024;
+  const int g0 = min(nseg, t * per_g), g1 = min(nseg, g0 + per_g);
+  int64_t ct = 0;
+  if (g0 < g1) {
+    int lo = 0, hi = num_seqs;               // last s with seq_seg0[s] <= g0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seq_seg0[mid] <= g0) lo = mid; else hi = mid;
+    }
+    int s = lo;
+    for (int g = g0; g < g1; ++g) {
+      while (seq_seg0[s + 1] <= g) ++s;      // skips sequences without segments
+      const int L = max(0, a.cu_q[s + 1] - a.cu_q[s]);
+      const int nq = qtiles(s);
+      const int local = g - seq_seg0[s];
+      const int kvh = local / nq, qt = local % nq;
+      const int n = seg_tiles(L, a.context_lens[s], qt, QB, a.causal);
+      seg_desc[g] = make_int4(s, kvh, qt, n);
+      ct += n;
+    }
+  }
+  const int64_t ct_end = block_scan_1024(ct, buf);
+  if (t == 0) ok = buf[1023] < ((int64_t)1 << 31);
+  __syncthreads();
+  const int64_t U = ok ? buf[1023] : 0;
+  if (ok) {
+    int run = (int)(ct_end - ct);
+    for (int g = g0; g < g1; ++g) {
+      seg_cu[g] = run;
+      run += seg_desc[g].w;
+    }
+  }
+  const int nseg_used = ok ? nseg : 0;
+  if (t == 0) {
+    seg_cu[nseg_used] = (int)U;
+    hdr[0] = nseg_used;
+    hdr[1] = (int)U;
+  }
+  __threadfence_block();
+  __syncthreads();
+  // 3. each workgroup's first (segment, tile)
   for (int w = t; w < num_wgs; w += 1024) {
     const int64_t x = pf_begin(w, U, num_wgs);
-    int lo = 0, hi = a.nseg;                 // last g with seg_cu[g] <= x < seg_cu[g+1]
+    int lo = 0, hi = nseg_used;              // last g with seg_cu[g] <= x
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (seg_cu[mid] <= x) lo = mid; else hi = mid;
     }
     wg_start[2 * w] = lo;
-    wg_start[2 * w + 1] = (int)(x - seg_cu[lo]);
+    wg_start[2 * w + 1] = (int)(x - (nseg_used > 0 ? seg_cu[lo] : 0));
   }
 }
 
@@ -220,20 +295,25 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   constexpr int CHUNKS = HD / 8;
   constexpr int BUF = LD::K_BYTES + LD::V_BYTES;
 
-  int s, kvh, qt;
-  seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
+  const int32_t* desc = (const int32_t*)a.seg_desc + 4 * (int64_t)g;
+  const int s = uniform_load(desc, 0), kvh = uniform_load(desc, 1), qt = uniform_load(desc, 2);
   const int q0 = a.cu_q[s];
   const int L = a.cu_q[s + 1] - q0;
   const int T = a.context_lens[s];
   const int n_q = a.n_kv * G;
 
+  // Rows are query-major: row rr is query qt * QB + rr / G of head rr % G, so
+  // the valid rows of a short segment (a decode row has G of them) fill the
+  // first wave, and a wave whose queries all lie past the end of the chunk
+  // only helps stage the K/V tiles.
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, grp = lane >> 5;
   const int rr = wave * 32 + lr;             // row of the segment
-  const int hl = rr / QB;
-  const int qi = qt * QB + rr % QB;
+  const int hl = rr % G;
+  const int qi = qt * QB + rr / G;
   const bool row_ok = qi < L;
+  const bool wave_ok = qt * QB + wave * 32 / G < L;
   const int pos = T - L + qi;
   const int head = kvh * G + hl;
 
@@ -388,7 +468,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
     sstore(R0, lds + boff);
     gload(min(t + 1, t1 - 1), R0);
     __syncthreads();
-    compute(lds + boff, t);
+    if (wave_ok) compute(lds + boff, t);
     boff ^= BUF;
   }
   __syncthreads();   // the next piece reuses the LDS buffers
@@ -431,7 +511,7 @@ __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillAr
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (LD::K_BYTES + LD::V_BYTES)];
   const int W = gridDim.x;
   const int wg = xcd_local_order(blockIdx.x, W);
-  const int64_t U = a.seg_cu[a.nseg];
+  const int64_t U = uniform_load(a.hdr, 1);
   const int64_t u0 = pf_begin(wg, U, W), u1 = pf_begin(wg + 1, U, W);
   if (u0 >= u1) return;
   int g = a.wg_start[2 * wg];
@@ -466,19 +546,20 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
   static_assert(PF_ROWS % ROWS == 0, "merge tiling");
   const int g = blockIdx.x / (PF_ROWS / ROWS);
   const int part = blockIdx.x % (PF_ROWS / ROWS);
+  if (g >= a.hdr[0]) return;
   const int64_t c0 = a.seg_cu[g], c1 = a.seg_cu[g + 1];
   if (c1 <= c0) return;
-  const int64_t U = a.seg_cu[a.nseg];
+  const int64_t U = a.hdr[1];
   const int w0 = pf_owner(c0, U, num_wgs), w1 = pf_owner(c1 - 1, U, num_wgs);
   if (w0 == w1) return;
-  int s, kvh, qt;
-  seg_decode(g, a.qtiles, a.n_kv, &s, &kvh, &qt);
+  const int4 dsc = a.seg_desc[g];
+  const int s = dsc.x, kvh = dsc.y, qt = dsc.z;
   const int q0 = a.cu_q[s];
   const int L = a.cu_q[s + 1] - q0;
   const int n_q = a.n_kv * G;
   const int d0 = (threadIdx.x % LPR) * 4;
   const int rr = part * ROWS + threadIdx.x / LPR;
-  const int qi = qt * QB + rr % QB;
+  const int qi = qt * QB + rr / G;
   if (qi >= L) return;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float M = -INFINITY, lsum = 0.0f;
@@ -496,7 +577,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
     M = Mn;
   }
   const float inv = lsum > 0.0f ? a.out_scale / lsum : 0.0f;
-  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + kvh * G + rr / QB) * HD + d0;
+  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * n_q + kvh * G + rr % G) * HD + d0;
   *(uint2*)orow = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
 }
 
@@ -516,13 +597,16 @@ static int pf_cu_count() {
 constexpr int PF_MAX_WGS_PER_CU = 4;   // bounds the workspace (LDS allows at most 4)
 
 struct PfLayout {
-  size_t seg, wgs, ml, o, total;
+  size_t hdr, seq, seg, desc, wgs, ml, o, total;
 };
-static PfLayout pf_layout(int64_t nseg, int64_t wgs, int head_dim) {
+static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_dim) {
   PfLayout l;
   const size_t slots = (size_t)(wgs + nseg);
-  l.seg = 0;
-  l.wgs = pf_align((size_t)(nseg + 1) * 4);
+  l.hdr = 0;
+  l.seq = 256;
+  l.seg = l.seq + pf_align((size_t)(num_seqs + 1) * 4);
+  l.desc = l.seg + pf_align((size_t)(nseg + 1) * 4);
+  l.wgs = l.desc + pf_align((size_t)nseg * 16);
   l.ml = l.wgs + pf_align((size_t)wgs * 2 * 4);
   l.o = l.ml + pf_align(slots * PF_ROWS * 2 * 4);
   l.total = l.o + pf_align(slots * PF_ROWS * head_dim * 4);
@@ -544,33 +628,44 @@ static int pf_resident_wgs() {
 }
 
 template <int CDT, int HD, int G>
-static void pf_launch(PrefillArgs a, const PfLayout& l, char* ws, hipStream_t st) {
+static void pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len, const PfLayout& l,
+                      char* ws, hipStream_t st) {
   const int W = pf_resident_wgs<CDT, HD, G>();
+  a.hdr = (const int32_t*)(ws + l.hdr);
   a.seg_cu = (const int32_t*)(ws + l.seg);
+  a.seg_desc = (const int4*)(ws + l.desc);
   a.wg_start = (const int32_t*)(ws + l.wgs);
   a.part_ml = (float*)(ws + l.ml);
   a.part_o = (float*)(ws + l.o);
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, PF_ROWS / G, W,
-                     (int32_t*)(ws + l.seg), (int32_t*)(ws + l.wgs));
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, num_seqs, total_q,
+                     max_q_len, PF_ROWS / G, W,
+                     (int32_t*)(ws + l.hdr), (int32_t*)(ws + l.seq), (int32_t*)(ws + l.seg),
+                     (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs));
   hipLaunchKernelGGL((prefill_kernel<CDT, HD, G>), dim3(W), dim3(256), 0, st, a);
   hipLaunchKernelGGL((prefill_merge_kernel<HD, G>),
-                     dim3(a.nseg * (PF_ROWS / MergeShape<HD>::ROWS)), dim3(256), 0, st, a, W);
+                     dim3(a.nseg_max * (PF_ROWS / MergeShape<HD>::ROWS)), dim3(256), 0, st, a, W);
 }
 
 template <int CDT, int HD>
-static bool pf_dispatch_g(int G, const PrefillArgs& a, const PfLayout& l, char* ws, hipStream_t st) {
+static bool pf_dispatch_g(int G, const PrefillArgs& a, int num_seqs, int total_q, int max_q_len,
+                          const PfLayout& l, char* ws, hipStream_t st) {
   switch (G) {
-    case 1: pf_launch<CDT, HD, 1>(a, l, ws, st); return true;
-    case 2: pf_launch<CDT, HD, 2>(a, l, ws, st); return true;
-    case 4: pf_launch<CDT, HD, 4>(a, l, ws, st); return true;
-    case 8: pf_launch<CDT, HD, 8>(a, l, ws, st); return true;
+    case 1: pf_launch<CDT, HD, 1>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
+    case 2: pf_launch<CDT, HD, 2>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
+    case 4: pf_launch<CDT, HD, 4>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
+    case 8: pf_launch<CDT, HD, 8>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
     default: return false;
   }
 }
 
-static int64_t pf_nseg(int num_seqs, int max_q_len, int n_kv, int G) {
-  const int QB = PF_ROWS / G;
-  return (int64_t)num_seqs * n_kv * ((max_q_len + QB - 1) / QB);
+// Bound on the segments of a batch of num_seqs chunks holding total_q queries,
+// none longer than max_q_len: sum_s ceil(L_s / QB) <= (total_q + num_seqs (QB - 1)) / QB
+// and <= num_seqs ceil(max_q_len / QB), times the KV heads.
+static int64_t pf_nseg_bound(int num_seqs, int total_q, int max_q_len, int n_kv, int G) {
+  const int64_t QB = PF_ROWS / G;
+  const int64_t by_total = ((int64_t)total_q + (int64_t)num_seqs * (QB - 1)) / QB;
+  const int64_t by_max = (int64_t)num_seqs * (((int64_t)max_q_len + QB - 1) / QB);
+  return (int64_t)n_kv * (by_total < by_max ? by_total : by_max);
 }
 
 }  // namespace pa
@@ -580,11 +675,13 @@ using namespace pa;
 extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                              int32_t n_q_heads, int32_t n_kv_heads,
                                              int32_t head_dim, int32_t max_context_len) {
-  (void)total_q; (void)max_context_len;
-  if (num_seqs <= 0 || max_q_len <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || head_dim <= 0)
+  (void)max_context_len;
+  if (num_seqs <= 0 || total_q <= 0 || max_q_len <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 ||
+      n_q_heads % n_kv_heads || head_dim <= 0)
     return 0;
   const int G = n_q_heads / n_kv_heads;
-  return pf_layout(pf_nseg(num_seqs, max_q_len, n_kv_heads, G),
+  if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
+  return pf_layout(num_seqs, pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, G),
                    (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
 }
 
@@ -616,13 +713,14 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
   // the kernel takes row maxima of the unscaled scores
   if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
-  const int64_t nseg = pf_nseg(num_seqs, max_q_len, n_kv_heads, group_size);
+  const int64_t nseg = pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, group_size);
   // key tiles are counted in 32-bit integers
   // (the merge launches PF_ROWS / 4 workgroups per segment at head_dim 64)
   if (nseg * (PF_ROWS / 4) >= ((int64_t)1 << 31) ||
       nseg * ((int64_t)max_context_len / PF_BN + 1) >= ((int64_t)1 << 31))
     return PA_ERR_SHAPE;
-  const PfLayout l = pf_layout(nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
+  const PfLayout l =
+      pf_layout(num_seqs, nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   PrefillArgs a;
   a.q = (const uint8_t*)q;
@@ -640,24 +738,20 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   a.bs_log2 = lg;
   a.n_kv = n_kv_heads;
   a.max_blocks = max_blocks_per_seq;
-  const int QB = PF_ROWS / group_size;
-  a.qtiles = (max_q_len + QB - 1) / QB;
-  a.nseg = (int)nseg;
+  a.nseg_max = (int)nseg;
   a.causal = causal != 0;
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.out_scale = fp8 ? v_scale : 1.0f;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  bool ok;
+  bool (*dispatch)(int, const PrefillArgs&, int, int, int, const PfLayout&, char*, hipStream_t);
   if (cache_dtype == PA_BF16)
-    ok = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128>(group_size, a, l, ws, st)
-                         : pf_dispatch_g<PA_BF16, 64>(group_size, a, l, ws, st);
+    dispatch = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128> : pf_dispatch_g<PA_BF16, 64>;
   else if (cache_dtype == PA_FP8_E4M3)
-    ok = head_dim == 128 ? pf_dispatch_g<PA_FP8_E4M3, 128>(group_size, a, l, ws, st)
-                         : pf_dispatch_g<PA_FP8_E4M3, 64>(group_size, a, l, ws, st);
+    dispatch = head_dim == 128 ? pf_dispatch_g<PA_FP8_E4M3, 128> : pf_dispatch_g<PA_FP8_E4M3, 64>;
   else
-    ok = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128>(group_size, a, l, ws, st)
-                         : pf_dispatch_g<PA_INT8, 64>(group_size, a, l, ws, st);
+    dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128> : pf_dispatch_g<PA_INT8, 64>;
+  const bool ok = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -94,3 +94,28 @@ def prefill(dw: DeviceWorkload, causal=None):
                                int(w.context_lens[:P].max()), w.scale,
                                causal=w.causal if causal is None else causal,
                                k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+def varlen(dw: DeviceWorkload, order=None, out=None):
+    """The whole batch -- prefill chunks and decode rows (L = 1) -- in ONE
+    pa_prefill_chunk call, sequences taken in ``order`` (default: as drawn).
+
+    Returns the output in the workload's own row order.
+    """
+    w = dw.w
+    B = w.num_seqs
+    order = np.arange(B) if order is None else np.asarray(order)
+    cu_all = w.cu(w.q_lens)
+    rows = np.concatenate([np.arange(cu_all[s], cu_all[s + 1]) for s in order])
+    rows_t = torch.as_tensor(rows, device=dw.dev)
+    order_t = torch.as_tensor(order, device=dw.dev)
+    lens = w.q_lens[order]
+    q = dw.q.index_select(0, rows_t)
+    got = pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(w.cu(lens), dw.dev),
+                              dw.tables.index_select(0, order_t).contiguous(),
+                              dw.ctx.index_select(0, order_t), int(lens.max()),
+                              int(w.context_lens.max()), w.scale, causal=True,
+                              k_scale=w.k_scale, v_scale=w.v_scale, out=out)
+    res = torch.empty_like(got)
+    res[rows_t] = got
+    return res

@@ -154,3 +154,63 @@ def test_prefill_split_covers_every_tile_once(seed):
             continue
         for W in (1, 2, 3, 5, 17, 256):
             replay_prefill(tiles, W)
+
+
+PF_ROWS, PF_BN = 128, 32
+
+
+def prefill_plan(lens, ctx, n_kv, G, causal):
+    """The prefill planner's segment list: for each sequence, each KV head, each
+    query tile of QB = 128 / G queries; per segment the key tiles its last query needs."""
+    QB = PF_ROWS // G
+    segs = []
+    for s, (L, T) in enumerate(zip(lens, ctx)):
+        nq = -(-L // QB)
+        for kvh in range(n_kv):
+            for qt in range(nq):
+                last = min(L, (qt + 1) * QB) - 1
+                vis = min(T, T - L + last + 1) if causal else T
+                segs.append((s, kvh, qt, -(-vis // PF_BN) if vis > 0 else 0))
+    return segs
+
+
+def nseg_bound(num_seqs, total_q, max_q, n_kv, G):
+    """The workspace's segment bound, as the host computes it."""
+    QB = PF_ROWS // G
+    return n_kv * min((total_q + num_seqs * (QB - 1)) // QB, num_seqs * -(-max_q // QB))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_plan_covers_every_row_once(seed):
+    """Ragged batches of chunks and decode rows (L = 1): each (sequence, query, head)
+    row lies in exactly one segment, under the workspace bound, and its segment
+    holds every key tile the row sees; the split of those tiles is then replayed."""
+    rng = random.Random(200 + seed)
+    for _ in range(200):
+        B = rng.randint(1, 12)
+        n_kv = rng.choice([1, 2, 8])
+        G = rng.choice([1, 2, 4, 8])
+        QB = PF_ROWS // G
+        causal = rng.random() < 0.7
+        lens = [rng.choice([0, 1, 1, 1, QB - 1, QB, QB + 1, rng.randint(1, 400)]) for _ in range(B)]
+        ctx = [L + rng.choice([0, 0, 1, 31, 32, rng.randint(0, 500)]) for L in lens]
+        segs = prefill_plan(lens, ctx, n_kv, G, causal)
+        assert len(segs) <= nseg_bound(B, sum(lens), max(lens), n_kv, G)
+        seen = {}
+        for g, (s, kvh, qt, tiles) in enumerate(segs):
+            T, L = ctx[s], lens[s]
+            for rr in range(PF_ROWS):                  # query-major rows of the segment
+                qi, h = qt * QB + rr // G, rr % G
+                wave_ok = qt * QB + (rr // 32) * 32 // G < L
+                if qi < L:
+                    assert wave_ok
+                    key = (s, qi, kvh * G + h)
+                    assert key not in seen
+                    seen[key] = g
+                    last_key = (T - L + qi) if causal else T - 1
+                    assert last_key < tiles * PF_BN  # the segment loads every key it sees
+        assert len(seen) == sum(lens) * n_kv * G
+        tiles = [t for (_, _, _, t) in segs]
+        if sum(tiles):
+            for W in (1, 3, 64, 1000):
+                replay_prefill(tiles, W)
