@@ -22,6 +22,16 @@ is symmetric 8-bit integers with a per-tensor scale, like FP8 above: the
 code is the float32 product x * (1 / scale) rounded to the nearest integer
 (ties to even) and clamped to [-127, 127]; NaN encodes as 0; the value of a
 code is code * scale.
+
+INT4: the same section names 4-bit KV caches with KIVI's grouping -- keys
+quantised along the channel (head_dim) axis, values along the token axis.
+The reading taken: symmetric 4-bit integers in [-7, 7] (round half to even,
+clamp, NaN -> 0, as for INT8); a key element uses its channel's scale (one
+per KV head and channel, given by the caller); a value element uses its
+token's scale (one per token and KV head, amax of the row / 7, computed when
+the token is appended).  Storage: two codes per byte, element 2i in the low
+nibble and 2i + 1 in the high nibble, each nibble sign-magnitude
+(8 * [c < 0] + |c|); the nibble 8 (a negative zero) decodes to 0.
 """
 from __future__ import annotations
 
@@ -103,6 +113,42 @@ def int8_encode(x) -> np.ndarray:
     nan = np.isnan(x)
     c = np.clip(np.rint(np.where(nan, 0.0, x)), -127.0, 127.0)   # +-inf clamp too
     return c.astype(np.int8).view(np.uint8)
+
+
+def int4_encode(x) -> np.ndarray:
+    """float32 values -> int8 arrays of 4-bit codes: rint (ties to even), clamp to
+    [-7, 7], NaN -> 0."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    return np.clip(np.rint(np.where(nan, 0.0, x)), -7.0, 7.0).astype(np.int8)
+
+
+def int4_pack(codes) -> np.ndarray:
+    """4-bit codes [..., n] (n even) -> bytes [..., n / 2], sign-magnitude nibbles,
+    element 2i low, 2i + 1 high."""
+    c = np.asarray(codes, dtype=np.int64)
+    nib = np.where(c < 0, 8, 0) + np.abs(c)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def int4_unpack(packed) -> np.ndarray:
+    """Bytes [..., n / 2] -> int codes [..., n] (float64), inverse of int4_pack."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    nib = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    mag = (nib & 7).astype(np.float64)
+    return np.where(nib & 8, -mag, mag)
+
+
+def int4_token_scale(rows) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row (token, head) scale of an INT4 value row and its float32 inverse:
+    sigma = amax / 7 (NaN elements ignored; one float32 division), inv = 1 / sigma
+    (one float32 division; inf for an all-zero row)."""
+    x = np.abs(np.asarray(rows, dtype=np.float32))
+    a = np.max(np.where(np.isnan(x), np.float32(0), x), axis=-1).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        sigma = (a / np.float32(7.0)).astype(np.float32)
+        inv = (np.float32(1.0) / sigma).astype(np.float32)
+    return sigma, inv
 
 
 def f32_inverse(scale: float) -> np.float32:

@@ -98,6 +98,77 @@ def kv_append(pool, new_codes, slots, block_size: int, src_dtype: str, cache_dty
     return pool
 
 
+def _src_f32(new_codes, src_dtype: str) -> np.ndarray:
+    if src_dtype == "bf16":
+        return codecs.bf16_decode(new_codes).astype(np.float32)
+    if src_dtype == "f32":
+        return np.asarray(new_codes, dtype=np.uint32).view(np.float32)
+    raise ValueError(src_dtype)
+
+
+def encode_int4_tokens(k_codes, v_codes, src_dtype: str, k_channel_scales):
+    """INT4 rows of new tokens ([Engineering] 5.4, KIVI grouping).
+
+    k_codes, v_codes [n, n_kv, hd] source codes; k_channel_scales [n_kv, hd].
+    Keys: code = int4(k * (1 / s[head, channel])), one float32 product with the
+    float32 inverse of the channel's scale.  Values: per (token, head) scale
+    sigma = amax / 7, code = int4(v * (1 / sigma)).  Returns the packed K and V
+    rows [n, n_kv, hd / 2] and sigma [n, n_kv] (float32).
+    """
+    xk = _src_f32(k_codes, src_dtype)
+    xv = _src_f32(v_codes, src_dtype)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        kinv = (np.float32(1.0) / np.asarray(k_channel_scales, np.float32)).astype(np.float32)
+        yk = (xk * kinv[None]).astype(np.float32)
+        sigma, vinv = codecs.int4_token_scale(xv)
+        yv = (xv * vinv[..., None]).astype(np.float32)
+    return (codecs.int4_pack(codecs.int4_encode(yk)), codecs.int4_pack(codecs.int4_encode(yv)),
+            sigma)
+
+
+def kv_append_int4(pool_k, pool_v, v_scale_pool, k_codes, v_codes, slots, block_size: int,
+                   src_dtype: str, k_channel_scales):
+    """INT4 append: packed K/V rows into pool[slot // S_blk, slot % S_blk] and the
+    token's value scales into v_scale_pool (same address map, [num_blocks,
+    S_blk, n_kv] float32), for every slot >= 0.  All three are modified in place."""
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    pk, pv, sig = encode_int4_tokens(np.asarray(k_codes)[keep], np.asarray(v_codes)[keep],
+                                     src_dtype, k_channel_scales)
+    b, o = slots[keep] // block_size, slots[keep] % block_size
+    pool_k[b, o] = pk
+    pool_v[b, o] = pv
+    v_scale_pool[b, o] = sig
+    return pool_k, pool_v, v_scale_pool
+
+
+def int4_seq_kv(pool_k, pool_v, v_scale_pool, table_row, ctx: int, block_size: int,
+                k_channel_scales):
+    """Dequantised K, V [ctx, n_kv, hd] (float64) of one sequence of an INT4 cache."""
+    K = codecs.int4_unpack(materialise(pool_k, table_row, ctx, block_size))
+    V = codecs.int4_unpack(materialise(pool_v, table_row, ctx, block_size))
+    sig = materialise(v_scale_pool, table_row, ctx, block_size).astype(np.float64)
+    s = np.asarray(k_channel_scales, np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return K * s[None], V * sig[..., None]
+
+
+def decode_int4(q_codes, q_dtype, pool_k, pool_v, v_scale_pool, k_channel_scales, block_tables,
+                context_lens, block_size: int, group_size: int, scale: float, rows=None):
+    """Single-token decode over an INT4 cache: as ``decode`` on the dequantised K/V."""
+    rows = range(len(context_lens)) if rows is None else rows
+    q = codecs.decode(q_codes, q_dtype)
+    n_q, hd = q.shape[1], q.shape[2]
+    out = np.zeros((len(rows), n_q, hd), dtype=np.float64)
+    for i, s in enumerate(rows):
+        K, V = int4_seq_kv(pool_k, pool_v, v_scale_pool, block_tables[s], int(context_lens[s]),
+                           block_size, k_channel_scales)
+        for h in range(n_q):
+            g = h // group_size
+            out[i, h] = attention_two_pass(q[s, h][None, :], K[:, g, :], V[:, g, :], scale)[0]
+    return out
+
+
 def copy_blocks(dst_pool, src_pool, pairs):
     """Whole-block copies: dst_pool[d] = src_pool[s] for every pair (s, d).
 
