@@ -35,6 +35,7 @@ WORKLOADS = {
     "longtail": (4, "bf16"),
     "longtail-fp8": (4, "fp8"),
     "longtail-int8": (4, "int8"),
+    "longtail-int4": (4, "int4"),
     "mixed": (5, "bf16"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -55,22 +56,25 @@ def prefill_flops(w, seqs=None):
 
 def byte_model(w):
     """Algorithmic bytes of one step (what the method must move)."""
-    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.cache_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}[w.cache_dtype]
     qb = {"f32": 4, "bf16": 2}[w.q_dtype]
     sb = {"f32": 4, "bf16": 2}[w.src_dtype]
     nkv, hd, bs = w.n_kv_heads, w.head_dim, w.block_size
+    # int4: each (token, head) also carries its float32 value scale
+    tok_head = hd * 2 * eb + (4 if w.cache_dtype == "int4" else 0)
     rows = list(w.decode_rows)
     ctx = w.context_lens[rows].astype(float)
-    kv_logical = float(ctx.sum()) * nkv * hd * 2 * eb
+    kv_logical = float(ctx.sum()) * nkv * tok_head
     shared = max(len(w.shared_prefix_seqs) - 1, 0) * w.shared_prefix_blocks * bs
-    kv_unique = kv_logical - shared * nkv * hd * 2 * eb
+    kv_unique = kv_logical - shared * nkv * tok_head
     B = len(rows)
     q_bytes = B * w.n_q_heads * hd * qb
     table_bytes = float(sum(math.ceil(c / bs) for c in ctx)) * 4 + B * 4
-    split = kv_unique + q_bytes + table_bytes
+    chan_bytes = nkv * hd * 4 if w.cache_dtype == "int4" else 0   # int4 key scales
+    split = kv_unique + q_bytes + table_bytes + chan_bytes
     out_bytes = B * w.n_q_heads * hd * qb
     n_new = int(w.new_len.sum())
-    append = n_new * nkv * hd * (sb + eb) * 2 + n_new * 8
+    append = n_new * nkv * (hd * (sb + eb) * 2 + (4 if w.cache_dtype == "int4" else 0)) + n_new * 8
     slots = n_new * (8 + 4) + B * 8
     return {"kv_logical": kv_logical, "kv_unique": kv_unique, "split_kernel": split,
             "step": split + out_bytes + append + slots, "append": append}
@@ -294,9 +298,14 @@ def main():
     from tests.gpu_harness import DeviceWorkload, i32
     dw = DeviceWorkload(w, dev)
     dw.append_resident()
-    pools = [(dw.k_cache, dw.v_cache)]
+    int4 = w.cache_dtype == "int4"
+    if int4 and args.one_launch:
+        log("--one-launch takes the per-tensor-scale caches only")
+        sys.exit(2)
+    pools = [(dw.k_cache, dw.v_cache, dw.v_scales if int4 else None)]
     for _ in range(max(args.pools, 1) - 1):
-        pools.append((dw.k_cache.clone(), dw.v_cache.clone()))
+        pools.append((dw.k_cache.clone(), dw.v_cache.clone(),
+                      dw.v_scales.clone() if int4 else None))
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t0:.1f} s: {w.name}, {w.num_seqs} seqs, "
         f"{w.num_blocks} blocks, pool {2 * dw.k_cache.numel() * dw.k_cache.element_size() / 2**30:.2f} GiB x {len(pools)}")
@@ -332,9 +341,12 @@ def main():
             PB, pf_q.shape[0], pf_maxq, w.n_q_heads, w.n_kv_heads, w.head_dim, pf_maxc), dev)
 
     def step(i, ev=None, pev=None):
-        kc, vc = pools[i % len(pools)]
+        kc, vc, vsc = pools[i % len(pools)]
         pa.pa_slot_mapping(dw.tables, new_cu, new_start, w.block_size, n_new, out=slots)
-        pa.pa_kv_append(kc, vc, new_k, new_v, slots, w.k_scale, w.v_scale)
+        if int4:
+            pa.pa_kv_append_int4(kc, vc, vsc, new_k, new_v, slots, dw.k_channel_scales)
+        else:
+            pa.pa_kv_append(kc, vc, new_k, new_v, slots, w.k_scale, w.v_scale)
         if P:
             if pev is not None:
                 pev[0].record(stream)
@@ -347,8 +359,12 @@ def main():
             return
         if ev is not None:
             ev[0].record(stream)
-        pa.pa_decode_partials(q, kc, vc, tables, ctx, maxc, w.scale, ws, w.k_scale,
-                              args.split_tokens)
+        if int4:
+            pa.pa_decode_int4_partials(q, kc, vc, vsc, dw.k_channel_scales, tables, ctx, maxc,
+                                       w.scale, ws, args.split_tokens)
+        else:
+            pa.pa_decode_partials(q, kc, vc, tables, ctx, maxc, w.scale, ws, w.k_scale,
+                                  args.split_tokens)
         if ev is not None:
             ev[1].record(stream)
         pa.pa_decode_merge(out, ctx, w.n_kv_heads, maxc, ws, w.v_scale if w.cache_dtype in ("fp8", "int8") else 1.0,
@@ -415,7 +431,9 @@ def main():
                 f"= {t_min / (pf_avg * 1e-3):.1%} of the launch")
 
     cpu = None
-    if not args.no_cpu_baseline and not P:
+    if int4 and not args.no_cpu_baseline:
+        log("cpu baseline: not taken for the int4 cache")
+    if not args.no_cpu_baseline and not P and not int4:
         w_host = w
         for name in ("q", "res_k", "res_v", "new_k", "new_v"):
             setattr(w_host, name, getattr(w, name).cpu())

@@ -69,7 +69,9 @@ typedef enum pa_dtype {
   PA_F32 = 0,              /* IEEE binary32 */
   PA_BF16 = 1,             /* bfloat16 */
   PA_FP8_E4M3 = 2,         /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF) */
-  PA_INT8 = 3              /* symmetric int8 codes in [-127, 127] (cache only) */
+  PA_INT8 = 3,             /* symmetric int8 codes in [-127, 127] (cache only) */
+  PA_INT4 = 4              /* symmetric 4-bit codes in [-7, 7], two per byte (cache only;
+                              the *_int4 entry points and pa_copy_blocks) */
 } pa_dtype;
 
 /* Human-readable name of a status code.  Never NULL. */
@@ -303,6 +305,67 @@ pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks,
                          int cache_dtype, int32_t block_size, int32_t n_kv_heads,
                          int32_t head_dim, const int64_t* block_pairs, int32_t num_pairs,
                          void* stream);
+
+/*
+ * INT4 KV cache -- "From PagedAttention to Chunked Prefill", section 5.4
+ * (4-bit caches with KIVI's grouping: keys quantised along the channel axis,
+ * values along the token axis).
+ *
+ *   Codes: symmetric integers in [-7, 7], two per byte, element 2i in the low
+ *   nibble of byte i, each nibble sign-magnitude (8 * [c < 0] + |c|; the
+ *   nibble 8 reads as 0).  The pools are [num_blocks][block_size][n_kv_heads]
+ *   [head_dim / 2] bytes (cache_dtype PA_INT4 in pa_copy_blocks).
+ *   Keys: k = code * k_channel_scales[h][d] (float32 [n_kv_heads][head_dim],
+ *   device memory, from the caller's calibration).
+ *   Values: v = code * v_scales[slot][h] (float32 [num_blocks][block_size]
+ *   [n_kv_heads], device memory, written by the append beside the codes: one
+ *   scale per token and head, addressed like the pools).  Moving a block
+ *   (copy-on-write, swap) moves its codes and its rows of v_scales.
+ *
+ * pa_kv_append_int4 -- for every i with 0 <= slot_mapping[i] <
+ * num_blocks * block_size and every head h:
+ *   key codes   clamp(rint_ties_even(float(k) * (1.0f / k_channel_scales[h][d])), -7, 7)
+ *   value scale sigma = a / 7.0f, a = max_d |v[i][h][d]| (NaN elements ignored)
+ *   value codes clamp(rint_ties_even(float(v) * (1.0f / sigma)), -7, 7)
+ * with NaN products encoding 0 (an all-zero row gets sigma 0 and codes 0), each
+ * division one binary32 division.  k_new, v_new [num_tokens][n_kv_heads]
+ * [head_dim] of src_dtype F32 or BF16; head_dim 64 or 128.  Other bytes and
+ * scales are not written.
+ */
+pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_scales, int32_t num_blocks,
+                            int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                            const void* k_new, const void* v_new, int src_dtype,
+                            const int64_t* slot_mapping, int32_t num_tokens,
+                            const float* k_channel_scales, void* stream);
+
+/*
+ * pa_decode_int4 / pa_decode_int4_partials -- pa_decode and pa_decode_partials
+ * over an INT4 cache (q_dtype BF16; no per-tensor scales).  The output is the
+ * attention over the dequantised keys and values above.  In the kernel the
+ * key scales multiply the query (rounded to bf16) and each value scale
+ * multiplies its token's softmax weight (rounded to bf16); the sum l is
+ * taken over the unscaled weights in fp32.  The workspace is
+ * pa_decode_workspace_bytes(...); the partials are merged by pa_decode_merge
+ * with out_scale 1.  pa_decode and pa_decode_partials return PA_ERR_DTYPE for
+ * cache_dtype PA_INT4.
+ */
+pa_status pa_decode_int4(void* out, const void* q, int q_dtype, const void* k_cache,
+                         const void* v_cache, const float* k_channel_scales,
+                         const float* v_scales, int32_t num_blocks, int32_t block_size,
+                         int32_t n_kv_heads, int32_t head_dim, int32_t group_size,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                         float scale, int32_t split_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+pa_status pa_decode_int4_partials(const void* q, int q_dtype, const void* k_cache,
+                                  const void* v_cache, const float* k_channel_scales,
+                                  const float* v_scales, int32_t num_blocks, int32_t block_size,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t group_size,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, float scale, int32_t split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

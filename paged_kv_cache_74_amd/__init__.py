@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # PA_LIB may name another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIB") or os.path.join(_HERE, "libpa.so")
 
-PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8, PA_INT4 = 0, 1, 2, 3, 4
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
            4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
 
@@ -51,6 +51,11 @@ def lib():
         _c("pa_slot_mapping", ctypes.c_int, P, P, I, I, P, P, I, I, P)
         _c("pa_kv_append", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int, P, I,
            F, F, P)
+        _c("pa_kv_append_int4", ctypes.c_int, P, P, P, I, I, I, I, P, P, ctypes.c_int, P, I, P, P)
+        _c("pa_decode_int4", ctypes.c_int, P, P, ctypes.c_int, P, P, P, P, I, I, I, I, I, P, I, P,
+           I, I, F, I, P, S, P)
+        _c("pa_decode_int4_partials", ctypes.c_int, P, ctypes.c_int, P, P, P, P, I, I, I, I, I, P,
+           I, P, I, I, F, I, P, S, P)
         _c("pa_decode_workspace_bytes", S, I, I, I, I, I, I)
         _c("pa_decode", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I, P, I,
            P, I, I, F, F, F, I, P, S, P)
@@ -139,6 +144,77 @@ def pa_kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tens
     _check("pa_kv_append", L.pa_kv_append(
         _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv, hd, _ptr(k_new),
         _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping), k_new.shape[0], k_scale, v_scale,
+        _stream(stream)))
+
+
+def _int4_pools(k_cache, v_cache, v_scales, k_channel_scales):
+    """Shapes of an INT4 cache: packed pools uint8 [nb, bs, n_kv, hd / 2], value
+    scales float32 [nb, bs, n_kv], key scales float32 [n_kv, hd]."""
+    _dev(k_cache, v_cache, v_scales, k_channel_scales)
+    _need(k_cache.dtype == v_cache.dtype == torch.uint8 and k_cache.shape == v_cache.shape and
+          k_cache.dim() == 4, "INT4 pools: uint8 [nb, bs, n_kv, hd / 2]")
+    nb, bs, nkv, half = k_cache.shape
+    _need(v_scales.dtype == torch.float32 and tuple(v_scales.shape) == (nb, bs, nkv),
+          "v_scales: float32 [nb, bs, n_kv]")
+    _need(k_channel_scales.dtype == torch.float32 and
+          tuple(k_channel_scales.shape) == (nkv, 2 * half), "k_channel_scales: float32 [n_kv, hd]")
+    return nb, bs, nkv, 2 * half
+
+
+def pa_kv_append_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, v_scales: torch.Tensor,
+                      k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_channel_scales: torch.Tensor, stream=None) -> None:
+    """INT4 append of k_new/v_new [T, n_kv, hd] (bf16 or f32) into the packed pools."""
+    L = lib()
+    nb, bs, nkv, hd = _int4_pools(k_cache, v_cache, v_scales, k_channel_scales)
+    _dev(k_new, v_new, slot_mapping)
+    _need(k_new.dtype == v_new.dtype and k_new.shape == v_new.shape and k_new.dim() == 3 and
+          tuple(k_new.shape[1:]) == (nkv, hd), "new K/V: [T, n_kv, hd]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() >= k_new.shape[0],
+          "slot_mapping: int64 [T]")
+    _check("pa_kv_append_int4", L.pa_kv_append_int4(
+        _ptr(k_cache), _ptr(v_cache), _ptr(v_scales), nb, bs, nkv, hd, _ptr(k_new), _ptr(v_new),
+        _dtype_code(k_new), _ptr(slot_mapping), k_new.shape[0], _ptr(k_channel_scales),
+        _stream(stream)))
+
+
+def pa_decode_int4(q, k_cache, v_cache, v_scales, k_channel_scales, block_tables, context_lens,
+                   max_context_len: int, scale: float, out=None, ws=None, split_tokens: int = 0,
+                   stream=None) -> torch.Tensor:
+    """Decode attention over an INT4 cache; q [B, n_q, hd] bf16 -> out of the same shape."""
+    L = lib()
+    nb, bs, nkv, hd = _int4_pools(k_cache, v_cache, v_scales, k_channel_scales)
+    _dev(q, block_tables, context_lens)
+    B, nq, hd2 = q.shape
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(block_tables.dtype == context_lens.dtype == torch.int32, "int32 tables / lengths")
+    _need(block_tables.shape[0] >= B and context_lens.shape[0] >= B, "one table row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    if ws is None:
+        ws = workspace(pa_decode_workspace_bytes(B, nq, nkv, hd, max_context_len, split_tokens),
+                       q.device)
+    _check("pa_decode_int4", L.pa_decode_int4(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_channel_scales),
+        _ptr(v_scales), nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, max_context_len, scale, split_tokens, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def pa_decode_int4_partials(q, k_cache, v_cache, v_scales, k_channel_scales, block_tables,
+                            context_lens, max_context_len: int, scale: float, ws,
+                            split_tokens: int = 0, stream=None) -> None:
+    """Phase 1 of pa_decode_int4 (merge with pa_decode_merge, out_scale 1)."""
+    L = lib()
+    nb, bs, nkv, hd = _int4_pools(k_cache, v_cache, v_scales, k_channel_scales)
+    _dev(q, block_tables, context_lens)
+    B, nq, _ = q.shape
+    _check("pa_decode_int4_partials", L.pa_decode_int4_partials(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_channel_scales),
+        _ptr(v_scales), nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, max_context_len, scale, split_tokens, _ptr(ws), ws.numel(),
         _stream(stream)))
 
 

@@ -26,6 +26,8 @@ FLAGS = [
     # keep hand-scheduled fp32 math scalar: no packed-fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
+    # float32 divisions (quantisation scales) round correctly, as IEEE binary32
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

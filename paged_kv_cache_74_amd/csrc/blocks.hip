@@ -64,10 +64,11 @@ extern "C" pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_bl
       head_dim < 1 || num_pairs < 0)
     return PA_ERR_SHAPE;
   if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 &&
-      cache_dtype != PA_INT8)
+      cache_dtype != PA_INT8 && cache_dtype != PA_INT4)
     return PA_ERR_DTYPE;
-  const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
-  const int64_t block_bytes = (int64_t)block_size * n_kv_heads * head_dim * eb;
+  const int ebits = cache_dtype == PA_F32 ? 32 : cache_dtype == PA_BF16 ? 16
+                  : cache_dtype == PA_INT4 ? 4 : 8;
+  const int64_t block_bytes = (int64_t)block_size * n_kv_heads * head_dim * ebits / 8;
   if (block_bytes % 8) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PA_ERR_NULL;

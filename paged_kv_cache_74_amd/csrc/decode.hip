@@ -44,14 +44,14 @@ namespace pa {
 
 template <int CDT, int HD>
 struct DecodeLayout {
-  static constexpr int EB = CDT == PA_F32 ? 4 : CDT == PA_BF16 ? 2 : 1;
-  static constexpr int ROW = HD * EB;                   // bytes of one (token, head) row
+  static constexpr int EBITS = CDT == PA_F32 ? 32 : CDT == PA_BF16 ? 16 : CDT == PA_INT4 ? 4 : 8;
+  static constexpr int ROW = HD * EBITS / 8;            // bytes of one (token, head) row
   static constexpr int LANE = ROW / 8;                  // bytes per lane per token
   static constexpr int CHUNK = LANE >= 16 ? 16 : LANE;  // bytes per load instruction
   static constexpr int NCHUNK = LANE / CHUNK;
   static constexpr int DW = LANE / 4;                   // dwords per lane per token
   static constexpr int DPL = HD / 8;                    // dims per lane
-  static constexpr int EPC = CHUNK / EB;                // elements per chunk
+  static constexpr int EPC = CHUNK * 8 / EBITS;         // elements per chunk
   static constexpr bool F32 = CDT == PA_F32;
   static constexpr int QDW = F32 ? DPL : DPL / 2;       // q dwords per head per lane
 };
@@ -95,12 +95,15 @@ struct DecodeArgs {
   int hw;             // waves (KV heads) per workgroup; n_kv = hw * nhg
   int nhg;            // KV head groups
   float score_scale;  // scale * k_scale * log2(e)
+  const float* k_ch_scale;   // INT4: [n_kv][HD] key scale per channel
+  const float* v_tok_scale;  // INT4: [num_blocks][block_size][n_kv] value scale per token
 };
 
 template <class L>
 struct Frag {
   uint32_t k[2][L::DW];
   uint32_t v[2][L::DW];
+  float vs[2];   // INT4: the value scales of the two token slots
   bool ok[2];
 };
 
@@ -111,9 +114,11 @@ __device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[L::DW])
     if constexpr (L::CHUNK == 16) {
       const uint4 x = *(const uint4*)(p + k * 8 * L::CHUNK);
       d[4 * k + 0] = x.x; d[4 * k + 1] = x.y; d[4 * k + 2] = x.z; d[4 * k + 3] = x.w;
-    } else {
+    } else if constexpr (L::CHUNK == 8) {
       const uint2 x = *(const uint2*)(p + k * 8 * L::CHUNK);
       d[2 * k + 0] = x.x; d[2 * k + 1] = x.y;
+    } else {
+      d[k] = *(const uint32_t*)(p + k * 8 * L::CHUNK);
     }
   }
 }
@@ -136,9 +141,11 @@ __device__ __forceinline__ void load_row_b(__amdgpu_buffer_rsrc_t r, uint32_t vo
     if constexpr (L::CHUNK == 16) {
       const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + k * 8 * L::CHUNK, soff, DECODE_LOAD_AUX);
       d[4 * k + 0] = x.x; d[4 * k + 1] = x.y; d[4 * k + 2] = x.z; d[4 * k + 3] = x.w;
-    } else {
+    } else if constexpr (L::CHUNK == 8) {
       const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff + k * 8 * L::CHUNK, soff, DECODE_LOAD_AUX);
       d[2 * k + 0] = x.x; d[2 * k + 1] = x.y;
+    } else {
+      d[k] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + k * 8 * L::CHUNK, soff, DECODE_LOAD_AUX);
     }
   }
 }
@@ -146,9 +153,18 @@ __device__ __forceinline__ void load_row_b(__amdgpu_buffer_rsrc_t r, uint32_t vo
 template <class L>
 __device__ __forceinline__ void zero_frag(Frag<L>& f) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int i = 0; i < L::DW; ++i) { f.k[j][i] = 0u; f.v[j][i] = 0u; }
+    f.vs[j] = 0.0f;
+  }
+}
+
+// INT4: the value scale of token `tok` (its index in the pool) for KV head kvh.
+template <class L>
+__device__ __forceinline__ float token_scale(const DecodeArgs& a, int64_t tok, int kvh) {
+  if constexpr (L::EBITS == 4) return a.v_tok_scale[tok * a.n_kv + kvh];
+  else return 0.0f;
 }
 
 // Issue the loads of one 16-token step starting at token `base` (a multiple of 16).
@@ -165,14 +181,15 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
     const int j = base >> a.bs_log2;
     const int blk = j < a.max_blocks ? uniform_load(table, j) : -1;
     const bool blk_ok = (unsigned)blk < (unsigned)a.num_blocks;
-    const int64_t o0 = ((int64_t)blk * a.block_size + (base & (a.block_size - 1)) + lane_g) *
-                           a.tok_stride + head_off;
+    const int64_t t0 = (int64_t)blk * a.block_size + (base & (a.block_size - 1)) + lane_g;
+    const int64_t o0 = t0 * a.tok_stride + head_off;
     if (full && blk_ok) {           // wave-uniform fast path
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         f.ok[j] = true;
         load_row<L>(a.k_cache + o0 + 8 * j * a.tok_stride, f.k[j]);
         load_row<L>(a.v_cache + o0 + 8 * j * a.tok_stride, f.v[j]);
+        f.vs[j] = token_scale<L>(a, t0 + 8 * j, kvh);
       }
       return;
     }
@@ -184,6 +201,7 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
       if (ok) {
         load_row<L>(a.k_cache + o0 + 8 * j * a.tok_stride, f.k[j]);
         load_row<L>(a.v_cache + o0 + 8 * j * a.tok_stride, f.v[j]);
+        f.vs[j] = token_scale<L>(a, t0 + 8 * j, kvh);
       }
     }
   } else {
@@ -200,9 +218,11 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
       }
       f.ok[j] = ok;
       if (ok) {
-        const int64_t o = ((int64_t)blk * a.block_size + (pos & (a.block_size - 1))) * a.tok_stride + head_off;
+        const int64_t t = (int64_t)blk * a.block_size + (pos & (a.block_size - 1));
+        const int64_t o = t * a.tok_stride + head_off;
         load_row<L>(a.k_cache + o, f.k[j]);
         load_row<L>(a.v_cache + o, f.v[j]);
+        f.vs[j] = token_scale<L>(a, t, kvh);
       }
     }
   }
@@ -217,11 +237,16 @@ __device__ __forceinline__ void load_step(Frag<L>& f, const DecodeArgs& a, const
 template <class L>
 __device__ __forceinline__ void load_full_step(Frag<L>& f, const DecodeArgs& a,
                                                const int32_t* table, int base, uint32_t lane_off,
-                                               bool live) {
+                                               bool live, int kvh, int lane_g) {
   const int j = base >> a.bs_log2;
   int blk = j < a.max_blocks ? uniform_load(table, j) : 0;
   blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
-  const int64_t step_off = ((int64_t)blk * a.block_size + (base & (a.block_size - 1))) * a.tok_stride;
+  const int64_t tok0 = (int64_t)blk * a.block_size + (base & (a.block_size - 1));
+  const int64_t step_off = tok0 * a.tok_stride;
+  if constexpr (L::EBITS == 4) {   // value scales of the lane's two token slots (in the pool)
+    f.vs[0] = token_scale<L>(a, tok0 + lane_g, kvh);
+    f.vs[1] = token_scale<L>(a, tok0 + lane_g + 8, kvh);
+  }
   const int32_t step_bytes = live ? 16 * (int32_t)a.tok_stride : 0;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k_cache + step_off, step_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v_cache + step_off, step_bytes);
@@ -263,6 +288,22 @@ __device__ __forceinline__ void lane_scores(const DecodeState<CDT, HD, G>& st,
       for (int h = 0; h < G; ++h) {
         s[h] = dot2_bf16(st.q[h][2 * i], lo, s[h]);
         s[h] = dot2_bf16(st.q[h][2 * i + 1], hi, s[h]);
+      }
+    }
+  } else if constexpr (CDT == PA_INT4) {
+    // dword i holds elements 8i .. 8i+7; the pairs come out as (0,2) (4,6)
+    // (1,3) (5,7), the order the query pairs were packed in
+#pragma unroll
+    for (int i = 0; i < L::DW; ++i) {
+      const uint32_t lo = int4_lo_as_e4m3(kd[i]), hi = int4_hi_as_e4m3(kd[i]);
+      const uint32_t k0 = int4e4m3_to_bf16x2<false>(lo), k1 = int4e4m3_to_bf16x2<true>(lo);
+      const uint32_t k2 = int4e4m3_to_bf16x2<false>(hi), k3 = int4e4m3_to_bf16x2<true>(hi);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s[h] = dot2_bf16(st.q[h][4 * i + 0], k0, s[h]);
+        s[h] = dot2_bf16(st.q[h][4 * i + 1], k1, s[h]);
+        s[h] = dot2_bf16(st.q[h][4 * i + 2], k2, s[h]);
+        s[h] = dot2_bf16(st.q[h][4 * i + 3], k3, s[h]);
       }
     }
   } else {
@@ -311,6 +352,36 @@ __device__ __forceinline__ void process_step(DecodeState<CDT, HD, G>& st,
       for (int e = 0; e < L::DPL; ++e)
         st.o[h][e] = fmaf(p0, bits_f32(f.v[0][e]), fmaf(p1, bits_f32(f.v[1][e]), st.o[h][e]));
     }
+  } else if constexpr (CDT == PA_INT4) {
+    // A value is code * (its token's scale): the scale multiplies the weight
+    // before it is rounded to bf16; l sums the unscaled weights in fp32.
+    uint32_t P[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p0 = fast_exp2(s0[h] - st.m[h]), p1 = fast_exp2(s1[h] - st.m[h]);
+      P[h] = pack_bf16(p0 * f.vs[0], p1 * f.vs[1]);
+      st.l[h] += p0 + p1;
+    }
+#pragma unroll
+    for (int i = 0; i < L::DW; ++i) {
+      const uint32_t L0 = int4_lo_as_e4m3(f.v[0][i]), L1 = int4_lo_as_e4m3(f.v[1][i]);
+      const uint32_t H0 = int4_hi_as_e4m3(f.v[0][i]), H1 = int4_hi_as_e4m3(f.v[1][i]);
+      // bytes {t0, t1} of one element side by side: elements (0, 2), (4, 6), (1, 3), (5, 7)
+      const uint32_t x0 = perm_b32(L1, L0, 0x05010400u), x1 = perm_b32(L1, L0, 0x07030602u);
+      const uint32_t y0 = perm_b32(H1, H0, 0x05010400u), y1 = perm_b32(H1, H0, 0x07030602u);
+      const uint32_t d0 = int4e4m3_to_bf16x2<false>(x0), d2 = int4e4m3_to_bf16x2<true>(x0);
+      const uint32_t d4 = int4e4m3_to_bf16x2<false>(x1), d6 = int4e4m3_to_bf16x2<true>(x1);
+      const uint32_t d1 = int4e4m3_to_bf16x2<false>(y0), d3 = int4e4m3_to_bf16x2<true>(y0);
+      const uint32_t d5 = int4e4m3_to_bf16x2<false>(y1), d7 = int4e4m3_to_bf16x2<true>(y1);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float* o = st.o[h] + 8 * i;
+        o[0] = dot2_bf16(P[h], d0, o[0]); o[1] = dot2_bf16(P[h], d1, o[1]);
+        o[2] = dot2_bf16(P[h], d2, o[2]); o[3] = dot2_bf16(P[h], d3, o[3]);
+        o[4] = dot2_bf16(P[h], d4, o[4]); o[5] = dot2_bf16(P[h], d5, o[5]);
+        o[6] = dot2_bf16(P[h], d6, o[6]); o[7] = dot2_bf16(P[h], d7, o[7]);
+      }
+    }
   } else {
     uint32_t P[G];
 #pragma unroll
@@ -354,7 +425,7 @@ __device__ __forceinline__ void process_step(DecodeState<CDT, HD, G>& st,
 template <class L>
 __device__ __forceinline__ int lane_dim(int c, int e) {
   const int k = e / L::EPC, w = e % L::EPC;
-  return (k * 8 * L::CHUNK + c * L::CHUNK) / L::EB + w;
+  return (k * 8 * L::CHUNK + c * L::CHUNK) * 8 / L::EBITS + w;
 }
 
 // ---------------------------------------------------------------------------
@@ -443,7 +514,35 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
 
   DecodeState<CDT, HD, G> st;
   // query fragment: the same dims as this lane's K/V elements
-  {
+  if constexpr (CDT == PA_INT4) {
+    // times the key scale of each channel (folded into the query, rounded to
+    // bf16), packed as the pairs (0,2) (4,6) (1,3) (5,7) of each 8 dims
+    const int d0 = lane_dim<L>(lane_c, 0);
+    const float* ks = a.k_ch_scale + (int64_t)kvh * HD + d0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint8_t* p = a.q + (((int64_t)s * n_q + (int64_t)kvh * G + h) * HD + d0) * 2;
+#pragma unroll
+      for (int i = 0; i < L::DW; ++i) {
+        const uint4 x = *(const uint4*)(p + 16 * i);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = bf16lo_f32(w[e]) * ks[8 * i + 2 * e];
+          f[2 * e + 1] = bf16hi_f32(w[e]) * ks[8 * i + 2 * e + 1];
+        }
+        st.q[h][4 * i + 0] = pack_bf16(f[0], f[2]);
+        st.q[h][4 * i + 1] = pack_bf16(f[4], f[6]);
+        st.q[h][4 * i + 2] = pack_bf16(f[1], f[3]);
+        st.q[h][4 * i + 3] = pack_bf16(f[5], f[7]);
+      }
+      st.m[h] = -1e30f;
+      st.l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < L::DPL; ++e) st.o[h][e] = 0.0f;
+    }
+  } else {
     constexpr int QEB = L::F32 ? 4 : 2;
     const uint8_t* qrow = a.q + ((int64_t)s * n_q + (int64_t)kvh * G) * HD * QEB;
 #pragma unroll
@@ -487,14 +586,15 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
       Frag<L> buf[NBUF];
 #pragma unroll
       for (int d = 0; d < NBUF - 1; ++d)
-        load_full_step<L>(buf[d], a, table, begin + 16 * min(d, n_full - 1), lane_off, d < n_full);
+        load_full_step<L>(buf[d], a, table, begin + 16 * min(d, n_full - 1), lane_off, d < n_full,
+                          kvh, lane_g);
       int i = 0;
       for (; i + NBUF <= n_full; i += NBUF) {   // every path issues NBUF step loads
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
           const int pf = i + u + NBUF - 1;
           load_full_step<L>(buf[(u + NBUF - 1) % NBUF], a, table, begin + 16 * min(pf, n_full - 1),
-                            lane_off, pf < n_full);
+                            lane_off, pf < n_full, kvh, lane_g);
           process_step<CDT, HD, G, false>(st, buf[u], c);
         }
       }
@@ -502,7 +602,7 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
       for (int u = 0; u < NBUF - 1; ++u) {       // the last n_full % NBUF steps
         const int pf = i + u + NBUF - 1;
         load_full_step<L>(buf[(u + NBUF - 1) % NBUF], a, table, begin + 16 * min(pf, n_full - 1),
-                          lane_off, pf < n_full);
+                          lane_off, pf < n_full, kvh, lane_g);
         if (i + u < n_full) process_step<CDT, HD, G, false>(st, buf[u], c);
       }
     }
@@ -861,18 +961,22 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t num_seqs, int32_t max_context_len, float scale,
                              float k_scale, float v_scale, int32_t split_tokens, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* stream,
+                             const float* k_channel_scales = nullptr,
+                             const float* v_token_scales = nullptr) {
   pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len, split_tokens);
   if (e != PA_OK) return e;
   if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
   if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
+  const bool int4 = cache_dtype == PA_INT4;
   const bool pair_ok = (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
                        (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3 ||
-                                                 cache_dtype == PA_INT8));
+                                                 cache_dtype == PA_INT8 || cache_dtype == PA_INT4));
   if (!pair_ok) return PA_ERR_DTYPE;
   if (num_seqs == 0) return PA_OK;
   if ((merge && !out) || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
+  if (int4 && (!k_channel_scales || !v_token_scales)) return PA_ERR_NULL;
   const int G = group_size;
   const WsLayout l = ws_layout(
       entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
@@ -891,8 +995,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.header = (int32_t*)(base + l.hdr);
   a.part_ml = (float*)(base + l.ml);
   a.part_o = (float*)(base + l.o);
-  const int eb = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
-  a.tok_stride = (int64_t)n_kv_heads * head_dim * eb;
+  const int ebits = cache_dtype == PA_F32 ? 32 : cache_dtype == PA_BF16 ? 16 : int4 ? 4 : 8;
+  a.tok_stride = (int64_t)n_kv_heads * head_dim * ebits / 8;
   a.num_blocks = num_blocks;
   a.block_size = block_size;
   int lg = 0;
@@ -905,12 +1009,15 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.hw = 1;
   a.nhg = n_kv_heads;
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+  a.k_ch_scale = k_channel_scales;
+  a.v_tok_scale = v_token_scales;
 
   hipStream_t st = (hipStream_t)stream;
   bool ok = false;
   if (cache_dtype == PA_BF16) ok = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
   else if (cache_dtype == PA_FP8_E4M3) ok = dispatch_hd<PA_FP8_E4M3>(head_dim, G, a, split_tokens, max_context_len, st);
   else if (cache_dtype == PA_INT8) ok = dispatch_hd<PA_INT8>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (int4) ok = dispatch_hd<PA_INT4>(head_dim, G, a, split_tokens, max_context_len, st);
   else ok = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
@@ -927,6 +1034,7 @@ extern "C" pa_status pa_decode(void* out, const void* q, int q_dtype, const void
                                int32_t num_seqs, int32_t max_context_len, float scale,
                                float k_scale, float v_scale, int32_t split_tokens,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache_dtype == PA_INT4) return PA_ERR_DTYPE;   // its scales come through pa_decode_int4
   return decode_impl(out, true, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
                      block_size, n_kv_heads, head_dim, group_size, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
@@ -941,6 +1049,7 @@ extern "C" pa_status pa_decode_partials(const void* q, int q_dtype, const void* 
                                         int32_t num_seqs, int32_t max_context_len, float scale,
                                         float k_scale, int32_t split_tokens, void* workspace,
                                         size_t workspace_bytes, void* stream) {
+  if (cache_dtype == PA_INT4) return PA_ERR_DTYPE;   // see pa_decode_int4_partials
   return decode_impl(nullptr, false, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
                      block_size, n_kv_heads, head_dim, group_size, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
@@ -964,4 +1073,37 @@ extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* co
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   return launch_merge(out, out_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
                       out_scale, workspace, (hipStream_t)stream);
+}
+
+extern "C" pa_status pa_decode_int4(void* out, const void* q, int q_dtype, const void* k_cache,
+                                    const void* v_cache, const float* k_channel_scales,
+                                    const float* v_token_scales, int32_t num_blocks,
+                                    int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t group_size, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t max_context_len, float scale,
+                                    int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return decode_impl(out, true, q, q_dtype, k_cache, v_cache, PA_INT4, num_blocks, block_size,
+                     n_kv_heads, head_dim, group_size, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, 1.0f, 1.0f, split_tokens,
+                     workspace, workspace_bytes, stream, k_channel_scales, v_token_scales);
+}
+
+extern "C" pa_status pa_decode_int4_partials(const void* q, int q_dtype, const void* k_cache,
+                                             const void* v_cache, const float* k_channel_scales,
+                                             const float* v_token_scales, int32_t num_blocks,
+                                             int32_t block_size, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t group_size,
+                                             const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t max_context_len, float scale,
+                                             int32_t split_tokens, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return decode_impl(nullptr, false, q, q_dtype, k_cache, v_cache, PA_INT4, num_blocks,
+                     block_size, n_kv_heads, head_dim, group_size, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, 1.0f,
+                     1.0f, split_tokens, workspace, workspace_bytes, stream, k_channel_scales,
+                     v_token_scales);
 }

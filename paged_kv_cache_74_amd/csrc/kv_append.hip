@@ -160,6 +160,83 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   AppendIO<SRC, DST>::run(src, dst, is_v ? v_inv : k_inv);
 }
 
+// ---------------------------------------------------------------------------
+// INT4 append ("From PagedAttention to Chunked Prefill", section 5.4: KIVI's
+// grouping -- keys quantised per channel, values per token).  Codes are
+// symmetric in [-7, 7] (round half to even, clamp, NaN -> 0), two per byte in
+// sign-magnitude nibbles, element 2i in the low nibble.  A key element is
+// encoded with its channel's scale (k_channel_scales[head][dim], from the
+// caller); a value row (token, head) gets the scale sigma = amax / 7 of its
+// own elements (NaN ignored), stored in v_scales at the token's slot.
+//
+// One row is head_dim / 8 lanes of 8 elements each (16 lanes at head_dim 128);
+// the lanes of a value row find its amax with shuffles inside the row's lane
+// group.  grid.y picks K or V.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_int4_nibble(float x) {
+  if (!(x == x)) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -7.0f), 7.0f));
+  const int c = (int)r;
+  return c < 0 ? 8u | (uint32_t)(-c) : (uint32_t)c;
+}
+
+template <int SRC>
+__device__ __forceinline__ void load8_f32(const uint8_t* src, float (&x)[8]) {
+  if constexpr (SRC == PA_BF16) {
+    const uint4 a = ld_stream(src);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo_f32(w[i]); x[2 * i + 1] = bf16hi_f32(w[i]); }
+  } else {
+    const uint4 a = ld_stream(src), b = ld_stream(src + 16);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bits_f32(w[i]);
+  }
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void kv_append_int4_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ v_scales,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, const float* __restrict__ k_channel_scales,
+    int64_t num_slots_in_pool, int n_kv, int lanes_per_row, int total_lanes) {
+  const int lane = blockIdx.x * blockDim.x + threadIdx.x;
+  // every lane of a row takes part in the row's shuffles: no early return
+  // before them (rows never straddle a wave: lanes_per_row divides 64)
+  const bool live = lane < total_lanes;
+  const int row = (int)((unsigned)min(lane, total_lanes - 1) / (unsigned)lanes_per_row);
+  const int j = lane - row * lanes_per_row;          // 8-element piece of the row
+  const int tok = row / n_kv, head = row - tok * n_kv;
+  const int64_t slot = slots[tok];
+  const bool ok = live && slot >= 0 && slot < num_slots_in_pool;
+  const int hd = lanes_per_row * 8;
+  constexpr int SB = SRC == PA_F32 ? 4 : 2;
+  const bool is_v = blockIdx.y != 0;
+  float x[8];
+  load8_f32<SRC>((is_v ? v_new : k_new) + ((int64_t)row * hd + j * 8) * SB, x);
+  float inv[8];
+  if (!is_v) {
+    const float* sc = k_channel_scales + (int64_t)head * hd + j * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) inv[i] = 1.0f / sc[i];   // one binary32 division each
+  } else {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));   // fmaxf ignores NaN
+    for (int off = 1; off < lanes_per_row; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    const float sigma = a / 7.0f;
+    const float r = 1.0f / sigma;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) inv[i] = r;
+    if (ok && j == 0) v_scales[slot * n_kv + head] = sigma;
+  }
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed |= f32_to_int4_nibble(x[i] * inv[i]) << (4 * i);
+  if (ok) *(uint32_t*)((is_v ? v_cache : k_cache) + (slot * n_kv + head) * (hd / 2) + j * 4) = packed;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -234,5 +311,31 @@ extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
   } else {
     return PA_ERR_DTYPE;
   }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_scales,
+                                       int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                       int32_t head_dim, const void* k_new, const void* v_new,
+                                       int src_dtype, const int64_t* slot_mapping,
+                                       int32_t num_tokens, const float* k_channel_scales,
+                                       void* stream) {
+  if (num_blocks < 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || num_tokens < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (src_dtype != PA_BF16 && src_dtype != PA_F32) return PA_ERR_DTYPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !v_scales || !k_new || !v_new || !slot_mapping || !k_channel_scales)
+    return PA_ERR_NULL;
+  const int lanes_per_row = head_dim / 8;
+  const int64_t lanes = (int64_t)num_tokens * n_kv_heads * lanes_per_row;
+  if (lanes >= ((int64_t)1 << 31) - 256) return PA_ERR_SHAPE;
+  const int total = (int)lanes;
+  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  auto kernel = src_dtype == PA_BF16 ? kv_append_int4_kernel<PA_BF16> : kv_append_int4_kernel<PA_F32>;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
+                     (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new,
+                     slot_mapping, k_channel_scales, (int64_t)num_blocks * block_size, n_kv_heads,
+                     lanes_per_row, total);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -57,6 +57,24 @@ __device__ __forceinline__ uint32_t code8x2_to_bf16x2(uint32_t src) {
   else return fp8x2_to_bf16x2<HI>(src);
 }
 
+// INT4 codes as e4m3 bytes.  Eight sign-magnitude nibbles of `x` (element 2i
+// in the low nibble of byte i) become four e4m3 bytes each: an e4m3 subnormal
+// is m * 2^-9 for its mantissa m, so the magnitude goes into the mantissa bits
+// and the sign into bit 7.  lo: elements 0, 2, 4, 6; hi: elements 1, 3, 5, 7.
+__device__ __forceinline__ uint32_t int4_lo_as_e4m3(uint32_t x) {
+  return (x & 0x07070707u) | ((x << 4) & 0x80808080u);
+}
+__device__ __forceinline__ uint32_t int4_hi_as_e4m3(uint32_t x) {
+  return ((x >> 4) & 0x07070707u) | (x & 0x80808080u);
+}
+// Two such bytes -> the bf16 pair of the integer codes, exactly (the scale 2^9
+// undoes the subnormal quantum).
+template <bool HI>
+__device__ __forceinline__ uint32_t int4e4m3_to_bf16x2(uint32_t src) {
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 512.0f, HI);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

@@ -13,16 +13,18 @@ import paged_kv_cache_74_amd as pa
 from workloads import POISON, Workload
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
-               "int8": torch.int8}
-INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8}
+               "int8": torch.int8, "int4": torch.uint8}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8,
+            "int4": torch.uint8}
 
 
 def poison_pool(w: Workload, dev) -> torch.Tensor:
-    shape = (w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim)
+    hd = w.head_dim // 2 if w.cache_dtype == "int4" else w.head_dim   # int4: two codes a byte
+    shape = (w.num_blocks, w.block_size, w.n_kv_heads, hd)
     t = torch.empty(shape, dtype=TORCH_DTYPE[w.cache_dtype], device=dev)
     p = int(POISON[w.cache_dtype])
-    bits = {"f32": 32, "bf16": 16, "fp8": 8, "int8": 8}[w.cache_dtype]
-    if w.cache_dtype != "fp8" and p >= 1 << (bits - 1):
+    bits = {"f32": 32, "bf16": 16, "fp8": 8, "int8": 8, "int4": 8}[w.cache_dtype]
+    if w.cache_dtype not in ("fp8", "int4") and p >= 1 << (bits - 1):
         p -= 1 << bits            # as the signed integer of the same bits
     t.view(INT_VIEW[w.cache_dtype]).fill_(p)
     return t
@@ -43,6 +45,12 @@ class DeviceWorkload:
         self.k_cache = poison_pool(w, dev)
         self.v_cache = poison_pool(w, dev)
         self.q = w.q.to(dev) if w.q is not None else None
+        if w.cache_dtype == "int4":
+            from workloads import INT4_SCALE_POISON
+            self.v_scales = torch.full((w.num_blocks, w.block_size, w.n_kv_heads),
+                                       int(INT4_SCALE_POISON) - (1 << 32), dtype=torch.int32,
+                                       device=dev).view(torch.float32)
+            self.k_channel_scales = torch.as_tensor(w.k_channel_scales, device=dev)
 
     def _seg(self, start, lens, k, v):
         w = self.w
@@ -51,7 +59,10 @@ class DeviceWorkload:
         n = int(cu[-1])
         slots = pa.pa_slot_mapping(self.tables, i32(cu, self.dev), i32(start, self.dev),
                                    w.block_size, n)
-        if n:
+        if n and w.cache_dtype == "int4":
+            pa.pa_kv_append_int4(self.k_cache, self.v_cache, self.v_scales, k.to(self.dev),
+                                 v.to(self.dev), slots, self.k_channel_scales)
+        elif n:
             pa.pa_kv_append(self.k_cache, self.v_cache, k.to(self.dev), v.to(self.dev), slots,
                             w.k_scale, w.v_scale)
         return slots
@@ -75,6 +86,10 @@ class DeviceWorkload:
         w = self.w
         q, tables, ctx = self.decode_inputs()
         maxc = int(w.context_lens[w.num_prefill_seqs:].max()) if len(w.decode_rows) else 0
+        if w.cache_dtype == "int4":
+            return pa.pa_decode_int4(q, self.k_cache, self.v_cache, self.v_scales,
+                                     self.k_channel_scales, tables, ctx, maxc, w.scale, out=out,
+                                     ws=ws, split_tokens=split_tokens)
         return pa.pa_decode(q, self.k_cache, self.v_cache, tables, ctx, maxc, w.scale,
                             w.k_scale, w.v_scale, out=out, ws=ws, split_tokens=split_tokens)
 

@@ -67,6 +67,49 @@ def oracle_pools(w: Workload, include_new: bool = True, seqs=None):
     return pk, pv
 
 
+def oracle_pools_int4(w: Workload, include_new: bool = True, seqs=None):
+    """INT4 pools (packed K, packed V, value scales) after the appends, as
+    ``oracle_pools`` does for the other dtypes."""
+    from workloads import INT4_SCALE_POISON
+    shape = (w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim // 2)
+    pk = np.full(shape, POISON["int4"], np.uint8)
+    pv = np.full(shape, POISON["int4"], np.uint8)
+    ps = np.full(shape[:3], INT4_SCALE_POISON, np.uint32).view(np.float32)
+    src = w.src_dtype
+    if seqs is None:
+        seqs = list(range(w.num_seqs))
+    seqs = sorted(set(int(s) for s in seqs))
+    if w.shared_prefix_seqs and any(s in w.shared_prefix_seqs for s in seqs):
+        seqs = sorted(set(seqs) | {w.shared_prefix_seqs[0]})
+    steps = [(w.res_start, w.res_len, w.res_k, w.res_v)]
+    if include_new:
+        steps.append((w.new_start, w.new_len, w.new_k, w.new_v))
+    for start, lens, k, v in steps:
+        cu = w.cu(lens)
+        idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]) if seqs else np.zeros(0, int)
+        if idx.size == 0:
+            continue
+        slots = oracle.paged.slot_mapping(w.block_tables[seqs], start[seqs], lens[seqs], w.block_size)
+        ti = torch.as_tensor(idx, device=k.device)
+        oracle.paged.kv_append_int4(pk, pv, ps, codes(k.index_select(0, ti), src),
+                                    codes(v.index_select(0, ti), src), slots, w.block_size, src,
+                                    w.k_channel_scales)
+    return pk, pv, ps
+
+
+def oracle_decode_int4(w: Workload, pk, pv, ps, rows=None):
+    """Oracle decode output for the decode rows of an INT4 workload (float64)."""
+    rows = list(w.decode_rows) if rows is None else list(rows)
+    qc = codes(w.q, w.q_dtype)
+    cu = w.cu(w.q_lens)
+    qd = np.zeros((w.num_seqs,) + qc.shape[1:], dtype=qc.dtype)
+    for s in rows:
+        qd[s] = qc[cu[s]]
+    return oracle.paged.decode_int4(qd, w.q_dtype, pk, pv, ps, w.k_channel_scales,
+                                    w.block_tables, w.context_lens, w.block_size, w.group_size,
+                                    w.scale, rows=rows)
+
+
 def blocks_of(w: Workload, seqs) -> np.ndarray:
     """Physical block ids read by the listed sequences."""
     ids = []

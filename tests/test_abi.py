@@ -188,3 +188,27 @@ def test_copy_blocks_argument_checks(lib):
 def test_copy_blocks_alignment_check(lib):
     d = dict(dk=0x1000, dv=0x1000, sk=0x1000, sv=0x1008, pairs=0x1000)
     assert _copy(lib, **d) == PA_ERR_SHAPE                                 # 16-byte blocks need 16
+
+
+def test_int4_argument_checks(lib):
+    INT4 = pa.PA_INT4
+    app = lambda **kw: lib.pa_kv_append_int4(
+        kw.get("k"), kw.get("v"), kw.get("vs"), kw.get("nb", 8), 16, 2, kw.get("hd", 64),
+        kw.get("kn"), kw.get("vn"), kw.get("sdt", BF16), kw.get("slots"), kw.get("n", 4),
+        kw.get("ks"), None)
+    assert app(n=0) == PA_OK
+    assert app(nb=-1) == PA_ERR_SHAPE
+    assert app(hd=96) == PA_ERR_UNSUPPORTED
+    assert app(sdt=FP8) == PA_ERR_DTYPE
+    assert app() == PA_ERR_NULL
+    # the per-tensor-scale entry points refuse an INT4 cache
+    assert _decode(lib, cdt=INT4) == PA_ERR_DTYPE
+    dec = lambda **kw: lib.pa_decode_int4(
+        None, None, kw.get("qdt", BF16), None, None, None, None, 8, 16, 2, kw.get("hd", 128),
+        kw.get("g", 4), None, 4, None, kw.get("ns", 2), 64, 0.1, 0, None, 0, None)
+    assert dec(ns=0) == PA_OK
+    assert dec(hd=96) == PA_ERR_UNSUPPORTED
+    assert dec(qdt=F32) == PA_ERR_DTYPE
+    assert dec() == PA_ERR_NULL
+    assert _copy(lib, cdt=INT4, bs=1, nkv=1, hd=8) == PA_ERR_UNSUPPORTED   # 4-byte blocks
+    assert _copy(lib, cdt=INT4) == PA_ERR_NULL

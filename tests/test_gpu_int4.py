@@ -1,0 +1,166 @@
+"""GPU parity of the INT4 KV cache (per-channel key scales, per-token value
+scales) against the oracle.
+
+Bars: the append is bit-exact (packed codes and value-scale bits); decode
+outputs within 2e-2 absolute and 1e-2 normwise relative error per row, like
+the other bf16-output paths; a one-hot decode reproduces every code exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import codes, oracle_decode_int4, oracle_pools_int4
+from test_gpu_decode import check_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import paged_kv_cache_74_amd as pa
+    pa.lib()
+    return "cuda"
+
+
+def _src_rows(rng, n, nkv, hd, src):
+    """Source rows with the edge cases: a zero row, NaN and infinite elements,
+    exact ties, a huge row, and ordinary N(0, 1) rows of mixed magnitude."""
+    x = (rng.standard_normal((n, nkv, hd)) * rng.uniform(1e-3, 30, (n, nkv, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1, 0, 3] = np.nan
+    x[2, 0, 5] = np.inf
+    x[3, 0, :] = np.arange(hd) % 15 - 7 + 0.5            # ties after the scale
+    x[4] = 3.0e30
+    t = torch.from_numpy(x)
+    return t.to(torch.bfloat16) if src == "bf16" else t
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_int4_append_bit_exact(dev, src, hd):
+    import paged_kv_cache_74_amd as pa
+    from workloads import INT4_SCALE_POISON
+    rng = np.random.default_rng(hd)
+    nb, bs, nkv, n = 40, 16, 4, 500
+    k = _src_rows(rng, n, nkv, hd, src)
+    v = _src_rows(rng, n, nkv, hd, src)
+    ks = rng.uniform(0.01, 3.0, (nkv, hd)).astype(np.float32)
+    ks[1, 2] = 1.0                                        # a channel with scale 1: ties stay ties
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[::37] = -1                                      # skipped rows
+    pk = np.full((nb, bs, nkv, hd // 2), 0x77, np.uint8)
+    pv = pk.copy()
+    ps = np.full((nb, bs, nkv), INT4_SCALE_POISON, np.uint32).view(np.float32)
+    gk, gv = torch.as_tensor(pk, device=dev), torch.as_tensor(pv, device=dev)
+    gs = torch.as_tensor(ps.copy(), device=dev)
+    pa.pa_kv_append_int4(gk, gv, gs, k.to(dev), v.to(dev), torch.as_tensor(slots, device=dev),
+                         torch.as_tensor(ks, device=dev))
+    torch.cuda.synchronize()
+    oracle.paged.kv_append_int4(pk, pv, ps, codes(k, src), codes(v, src), slots, bs, src, ks)
+    assert np.array_equal(gk.cpu().numpy(), pk)
+    assert np.array_equal(gv.cpu().numpy(), pv)
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), ps.view(np.uint32))
+
+
+def _int4(w):
+    w.cache_dtype = "int4"
+    return workloads.draw_values(w, "cpu")
+
+
+def _decode_vs_oracle(w, dev, what, split_tokens=0):
+    from gpu_harness import DeviceWorkload, to_f64
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    got = to_f64(dw.decode(split_tokens=split_tokens))
+    pk, pv, ps = oracle_pools_int4(w)
+    ref = oracle_decode_int4(w, pk, pv, ps)
+    check_close(got, ref, "bf16", what)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_int4_decode_small_configs(dev, cfg):
+    _decode_vs_oracle(_int4(workloads.small(cfg)), dev, f"int4 decode config {cfg}")
+
+
+@pytest.mark.parametrize("split", [16, 48])
+def test_int4_decode_split_sizes(dev, split):
+    _decode_vs_oracle(_int4(workloads.small(4, seed=2)), dev, f"int4 split {split}", split)
+
+
+# (n_q, n_kv, head_dim, block_size): every group size, both head dims, small and large blocks
+SHAPES = [(8, 8, 128, 16), (8, 4, 64, 16), (16, 4, 128, 32), (16, 2, 64, 1), (32, 4, 128, 4)]
+
+
+@pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES)
+def test_int4_decode_shapes(dev, nq, nkv, hd, bs):
+    rng = np.random.default_rng(nq * 131 + hd + bs)
+    ctx = rng.integers(1, 700, 9).astype(np.int32)
+    ctx[0] = 1
+    w = workloads._decode_workload("int4-shapes", rng, ctx, nq, nkv, hd, bs, "int4", "bf16",
+                                   "bf16", seed=3)
+    _decode_vs_oracle(workloads.draw_values(w, "cpu"), dev, f"int4 {nq}/{nkv}/{hd}/bs{bs}")
+
+
+def test_int4_one_hot_reproduces_every_code(dev):
+    """One token per sequence dominates the softmax and every value row holds a
+    +-7, so its scale is exactly 1: the output is that token's codes, exactly."""
+    import paged_kv_cache_74_amd as pa
+    rng = np.random.default_rng(9)
+    B, nkv, G, hd, bs = 6, 2, 4, 128, 16
+    ctx = np.array([40, 17, 1, 200, 33, 64], np.int32)
+    nblk = -(-ctx // bs)
+    nb = int(nblk.sum())
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = -np.ones((B, nblk.max()), np.int32)
+    c = 0
+    for s in range(B):
+        tables[s, :nblk[s]] = perm[c:c + nblk[s]]
+        c += nblk[s]
+    T = int(ctx.sum())
+    target = np.array([rng.integers(0, n) for n in ctx])
+    kx = np.full((T, nkv, hd), -7.0, np.float32)      # every other score 2^-228 below: 0
+    vx = rng.integers(-7, 8, (T, nkv, hd)).astype(np.float32)
+    vx[:, :, 0] = np.where(rng.random((T, nkv)) < 0.5, 7.0, -7.0)
+    cu = np.concatenate([[0], np.cumsum(ctx)])
+    for s in range(B):
+        kx[cu[s] + target[s]] = 7.0                      # codes +7 at key scale 1
+    q = torch.ones((B, nkv * G, hd), dtype=torch.bfloat16, device=dev)
+    pools = [torch.full((nb, bs, nkv, hd // 2), 0x77, dtype=torch.uint8, device=dev) for _ in "kv"]
+    vs = torch.full((nb, bs, nkv), float("nan"), device=dev)
+    ks = torch.ones((nkv, hd), device=dev)
+    tab = torch.as_tensor(tables, device=dev)
+    slots = pa.pa_slot_mapping(tab, torch.as_tensor(cu.astype(np.int32), device=dev),
+                               torch.zeros(B, dtype=torch.int32, device=dev), bs, T)
+    pa.pa_kv_append_int4(pools[0], pools[1], vs, torch.as_tensor(kx, device=dev).to(torch.bfloat16),
+                         torch.as_tensor(vx, device=dev).to(torch.bfloat16), slots, ks)
+    out = pa.pa_decode_int4(q, pools[0], pools[1], vs, ks, tab, torch.as_tensor(ctx, device=dev),
+                            int(ctx.max()), 1.0 / np.sqrt(hd))
+    got = out.float().cpu().numpy()
+    for s in range(B):
+        for h in range(nkv * G):
+            assert np.array_equal(got[s, h], vx[cu[s] + target[s], h // G]), (s, h)
+
+
+def test_int4_full_size_sampled(dev):
+    """The long-tail decode (256 sequences up to 131072 tokens) over an INT4
+    cache, at the launch configuration the bench times; sampled sequences
+    against the oracle, one by one."""
+    from gpu_harness import DeviceWorkload, to_f64
+    print("full-size int4 decode", flush=True)
+    w = workloads.full(4, kv="int4")
+    workloads.draw_values(w, dev)
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    got = to_f64(dw.decode())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    longest = int(np.argmax(w.context_lens))
+    rows = sorted(set([longest] + rng.choice(w.num_seqs, 5, replace=False).tolist()))
+    pk, pv, ps = oracle_pools_int4(w, seqs=rows)
+    ref = oracle_decode_int4(w, pk, pv, ps, rows=rows)
+    check_close(got[rows], ref, "bf16", "full int4 sampled")

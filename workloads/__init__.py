@@ -35,14 +35,18 @@ import numpy as np
 # Bit patterns used to fill the pool before anything is appended.  They are
 # NaNs, so any read of a slot that no token owns shows up in the results.
 POISON = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F),
-          "int8": np.uint8(0x80)}       # int8: -128, outside the code range [-127, 127]
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
+          "int8": np.uint8(0x80),       # int8: -128, outside the code range [-127, 127]
+          # int4: every byte is a valid code pair, so the poison that shows is the
+          # NaN in the value-scale pool at every slot no token owns
+          "int4": np.uint8(0x77)}
+INT4_SCALE_POISON = np.uint32(0xFFC0DEAD)
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}
 
 
 @dataclasses.dataclass
 class Workload:
     name: str
-    cache_dtype: str            # "f32" | "bf16" | "fp8" | "int8"
+    cache_dtype: str            # "f32" | "bf16" | "fp8" | "int8" | "int4"
     q_dtype: str                # "f32" | "bf16"   (output dtype == q dtype)
     src_dtype: str              # dtype of K/V handed to the append call
     n_q_heads: int
@@ -61,6 +65,7 @@ class Workload:
     scale: float
     k_scale: float = 1.0
     v_scale: float = 1.0
+    k_channel_scales: object = None   # int4: float32 [n_kv, hd], one key scale per channel
     causal: bool = True
     num_prefill_seqs: int = 0   # rows [0, num_prefill_seqs) are prefill chunks
     shared_prefix_seqs: tuple = ()
@@ -184,6 +189,14 @@ def draw_values(w: Workload, device: str = "cpu") -> Workload:
         va = torch.maximum(w.res_v.float().abs().amax(), w.new_v.float().abs().amax()) if w.new_v.numel() else w.res_v.float().abs().amax()
         w.k_scale = float(np.float32(float(ka)) / top)
         w.v_scale = float(np.float32(float(va)) / top)
+    if w.cache_dtype == "int4":
+        # per-channel key scales (the caller's calibration): amax over every key
+        # of the workload per (KV head, channel) / 7, fp32
+        import torch
+        ka = w.res_k.float().abs().amax(dim=0)
+        if w.new_k.numel():
+            ka = torch.maximum(ka, w.new_k.float().abs().amax(dim=0))
+        w.k_channel_scales = (ka.cpu().numpy().astype(np.float32) / np.float32(7.0)).astype(np.float32)
     return w
 
 
