@@ -317,10 +317,11 @@ pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks,
  *   [head_dim / 2] bytes (cache_dtype PA_INT4 in pa_copy_blocks).
  *   Keys: k = code * k_channel_scales[h][d] (float32 [n_kv_heads][head_dim],
  *   device memory, from the caller's calibration).
- *   Values: v = code * v_scales[slot][h] (float32 [num_blocks][block_size]
- *   [n_kv_heads], device memory, written by the append beside the codes: one
- *   scale per token and head, addressed like the pools).  Moving a block
- *   (copy-on-write, swap) moves its codes and its rows of v_scales.
+ *   Values: v = code * v_scales[slot / block_size][h][slot % block_size]
+ *   (float32 [num_blocks][n_kv_heads][block_size], device memory, written by
+ *   the append beside the codes: one scale per token and head, the scales of
+ *   one head's tokens of a block adjacent).  Moving a block (copy-on-write,
+ *   swap) moves its codes and its v_scales block.
  *
  * pa_kv_append_int4 -- for every i with 0 <= slot_mapping[i] <
  * num_blocks * block_size and every head h:

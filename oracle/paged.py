@@ -129,8 +129,9 @@ def encode_int4_tokens(k_codes, v_codes, src_dtype: str, k_channel_scales):
 def kv_append_int4(pool_k, pool_v, v_scale_pool, k_codes, v_codes, slots, block_size: int,
                    src_dtype: str, k_channel_scales):
     """INT4 append: packed K/V rows into pool[slot // S_blk, slot % S_blk] and the
-    token's value scales into v_scale_pool (same address map, [num_blocks,
-    S_blk, n_kv] float32), for every slot >= 0.  All three are modified in place."""
+    token's value scales into v_scale_pool[slot // S_blk, h, slot % S_blk] (float32
+    [num_blocks, n_kv, S_blk]: the scales of one head's tokens of a block are
+    adjacent), for every slot >= 0.  All three are modified in place."""
     slots = np.asarray(slots, dtype=np.int64)
     keep = slots >= 0
     pk, pv, sig = encode_int4_tokens(np.asarray(k_codes)[keep], np.asarray(v_codes)[keep],
@@ -138,7 +139,7 @@ def kv_append_int4(pool_k, pool_v, v_scale_pool, k_codes, v_codes, slots, block_
     b, o = slots[keep] // block_size, slots[keep] % block_size
     pool_k[b, o] = pk
     pool_v[b, o] = pv
-    v_scale_pool[b, o] = sig
+    v_scale_pool[b, :, o] = sig
     return pool_k, pool_v, v_scale_pool
 
 
@@ -147,7 +148,7 @@ def int4_seq_kv(pool_k, pool_v, v_scale_pool, table_row, ctx: int, block_size: i
     """Dequantised K, V [ctx, n_kv, hd] (float64) of one sequence of an INT4 cache."""
     K = codecs.int4_unpack(materialise(pool_k, table_row, ctx, block_size))
     V = codecs.int4_unpack(materialise(pool_v, table_row, ctx, block_size))
-    sig = materialise(v_scale_pool, table_row, ctx, block_size).astype(np.float64)
+    sig = materialise(np.swapaxes(v_scale_pool, 1, 2), table_row, ctx, block_size).astype(np.float64)
     s = np.asarray(k_channel_scales, np.float32).astype(np.float64)
     with np.errstate(invalid="ignore"):
         return K * s[None], V * sig[..., None]

@@ -149,13 +149,13 @@ def pa_kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tens
 
 def _int4_pools(k_cache, v_cache, v_scales, k_channel_scales):
     """Shapes of an INT4 cache: packed pools uint8 [nb, bs, n_kv, hd / 2], value
-    scales float32 [nb, bs, n_kv], key scales float32 [n_kv, hd]."""
+    scales float32 [nb, n_kv, bs], key scales float32 [n_kv, hd]."""
     _dev(k_cache, v_cache, v_scales, k_channel_scales)
     _need(k_cache.dtype == v_cache.dtype == torch.uint8 and k_cache.shape == v_cache.shape and
           k_cache.dim() == 4, "INT4 pools: uint8 [nb, bs, n_kv, hd / 2]")
     nb, bs, nkv, half = k_cache.shape
-    _need(v_scales.dtype == torch.float32 and tuple(v_scales.shape) == (nb, bs, nkv),
-          "v_scales: float32 [nb, bs, n_kv]")
+    _need(v_scales.dtype == torch.float32 and tuple(v_scales.shape) == (nb, nkv, bs),
+          "v_scales: float32 [nb, n_kv, bs]")
     _need(k_channel_scales.dtype == torch.float32 and
           tuple(k_channel_scales.shape) == (nkv, 2 * half), "k_channel_scales: float32 [n_kv, hd]")
     return nb, bs, nkv, 2 * half

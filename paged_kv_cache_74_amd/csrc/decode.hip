@@ -96,7 +96,7 @@ struct DecodeArgs {
   int nhg;            // KV head groups
   float score_scale;  // scale * k_scale * log2(e)
   const float* k_ch_scale;   // INT4: [n_kv][HD] key scale per channel
-  const float* v_tok_scale;  // INT4: [num_blocks][block_size][n_kv] value scale per token
+  const float* v_tok_scale;  // INT4: [num_blocks][n_kv][block_size] value scale per token
 };
 
 template <class L>
@@ -163,7 +163,9 @@ __device__ __forceinline__ void zero_frag(Frag<L>& f) {
 // INT4: the value scale of token `tok` (its index in the pool) for KV head kvh.
 template <class L>
 __device__ __forceinline__ float token_scale(const DecodeArgs& a, int64_t tok, int kvh) {
-  if constexpr (L::EBITS == 4) return a.v_tok_scale[tok * a.n_kv + kvh];
+  if constexpr (L::EBITS == 4)
+    return a.v_tok_scale[((tok >> a.bs_log2) * a.n_kv + kvh) * a.block_size +
+                         (tok & (a.block_size - 1))];
   else return 0.0f;
 }
 
@@ -684,6 +686,356 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path (block_size >= 16).  The same work split, pieces and
+// partial format as above; inside a wave both products run on MFMA:
+//   * S^T = K Q'^T with v_mfma_f32_16x16x32_bf16: lane l = (j = l / 16,
+//     r = l % 16) holds token r of the 16-token step, dims [j HD/4, (j+1) HD/4)
+//     of K as the A operand (its natural layout: one contiguous piece of the
+//     token's row per lane) and, as the B operand, the same dims of query head
+//     r (zero for r >= G).  The result gives each lane tokens 4j .. 4j+3 of
+//     head column r.
+//   * O = P V with v_mfma_f32_16x16x16_bf16: those four weights are already the
+//     A operand (row = head r, k = tokens 4j .. 4j+3).  V is converted to bf16,
+//     written as rows to this wave's slice of LDS, and read back transposed with
+//     ds_read_b64_tr_b16, which hands lane (j, r) tokens 4j .. 4j+3 of one dim:
+//     the B operand.  The output gives each lane heads 4j .. 4j+3 of dim r of
+//     each 16-dim block.
+// The softmax runs per head column: the four lanes of a column (j = 0..3)
+// agree on its running max with two exchanges per step, and the max moves only
+// when a tile max exceeds it by more than DMF_SLACK (base-2 units), as in the
+// chunked-prefill kernel.  This takes the two products off the vector ALU,
+// which otherwise bounds the 8- and 4-bit caches (their codes must be widened
+// to bf16 either way).
+// ---------------------------------------------------------------------------
+typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short mf_s4_t __attribute__((ext_vector_type(4)));
+typedef float mf_f32x4_t __attribute__((ext_vector_type(4)));
+constexpr float DMF_SLACK = 8.0f;
+
+template <int CDT, int HD>
+struct MfLayout {
+  static constexpr int EBITS = DecodeLayout<CDT, HD>::EBITS;
+  static constexpr int ROW = HD * EBITS / 8;     // bytes of one (token, head) row
+  static constexpr int DPJ = HD / 4;             // dims per lane group j
+  static constexpr int JB = DPJ * EBITS / 8;     // bytes per lane per token
+  static constexpr int KW = JB / 4;              // dwords per lane per token
+  // A lane's bytes of a token row come in NP pieces of PS bytes: piece k of
+  // lane group j at byte (j + 4k) PS, so the four lanes of a token read PS * 4
+  // contiguous bytes per load instruction.
+  static constexpr int PS = JB < 16 ? JB : 16;
+  static constexpr int NP = JB / PS;
+  static constexpr int DPP = PS * 8 / EBITS;     // dims per piece
+  static constexpr int NT = HD / 32;             // QK MFMAs (16x16x32) per step
+  static constexpr int NB = HD / 16;             // PV MFMAs (16x16x16) per step
+  static constexpr int VROW = HD * 2 + 32;       // LDS bytes per token row of V (bf16, padded)
+  static constexpr int WAVE_LDS = 16 * VROW;
+};
+
+#ifndef DECODE_MF_AUX
+#define DECODE_MF_AUX DECODE_LOAD_AUX
+#endif
+// First dim of the 8 dims that MFMA t of a step takes from lane group j.
+template <class ML>
+__device__ __forceinline__ int mf_dim0(int t, int j) {
+  constexpr int CPP = ML::DPP / 8;   // 8-dim chunks per piece
+  return (j + 4 * (t / CPP)) * ML::DPP + 8 * (t % CPP);
+}
+
+// One lane's K or V codes of one token: NP pieces (see MfLayout).
+template <class ML>
+__device__ __forceinline__ void mf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                        uint32_t (&d)[ML::KW]) {
+  static_assert(ML::PS == 16 || ML::PS == 8, "lane pieces of 8 or 16 bytes");
+#pragma unroll
+  for (int k = 0; k < ML::NP; ++k) {
+    if constexpr (ML::PS == 8) {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 32 * k, 0, DECODE_MF_AUX);
+      d[2 * k + 0] = x.x; d[2 * k + 1] = x.y;
+    } else {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64 * k, 0, DECODE_MF_AUX);
+      d[4 * k + 0] = x.x; d[4 * k + 1] = x.y; d[4 * k + 2] = x.z; d[4 * k + 3] = x.w;
+    }
+  }
+}
+
+template <class ML>
+struct MfFrag {
+  uint32_t k[ML::KW];
+  uint32_t v[ML::KW];
+  float vs[4];   // INT4: value scales of tokens 4j .. 4j+3
+};
+
+// The loads of one step: tokens [base, base + 16) of the sequence, all in one
+// block (block_size >= 16).  Tokens at or past `end` read as zeros (the
+// descriptor covers only the valid rows), as does a step with live == false.
+template <int CDT, class ML>
+__device__ __forceinline__ void mf_load_step(MfFrag<ML>& f, const DecodeArgs& a, int blk,
+                                             int base, int end, uint32_t lane_off, bool live,
+                                             int kvh, int j) {
+  const int64_t tok0 = (int64_t)blk * a.block_size + (base & (a.block_size - 1));
+  const int n = live ? min(16, end - base) : 0;
+  const int32_t bytes = n * (int32_t)a.tok_stride;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k_cache + tok0 * a.tok_stride, bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v_cache + tok0 * a.tok_stride, bytes);
+  mf_load<ML>(kr, lane_off, f.k);
+  mf_load<ML>(vr, lane_off, f.v);
+  if constexpr (CDT == PA_INT4) {   // tokens 4j .. 4j+3: adjacent in the scale pool
+    const float4 x = *(const float4*)(a.v_tok_scale +
+                                      ((int64_t)blk * a.n_kv + kvh) * a.block_size +
+                                      (base & (a.block_size - 1)) + 4 * j);
+    f.vs[0] = 4 * j + 0 < n ? x.x : 0.0f;
+    f.vs[1] = 4 * j + 1 < n ? x.y : 0.0f;
+    f.vs[2] = 4 * j + 2 < n ? x.z : 0.0f;
+    f.vs[3] = 4 * j + 3 < n ? x.w : 0.0f;
+  }
+}
+
+// Eight dims of K as an MFMA operand (bf16), from dwords d[w0 ..] of the lane's
+// codes.  INT4 pairs come out as dims (0,2) (4,6) (1,3) (5,7); the query was
+// packed in the same order.
+template <int CDT>
+__device__ __forceinline__ mf_bf16x8_t mf_k8(const uint32_t* d) {
+  uint32_t w[4];
+  if constexpr (CDT == PA_BF16) {
+    w[0] = d[0]; w[1] = d[1]; w[2] = d[2]; w[3] = d[3];
+  } else if constexpr (CDT == PA_INT4) {
+    const uint32_t lo = int4_lo_as_e4m3(d[0]), hi = int4_hi_as_e4m3(d[0]);
+    w[0] = int4e4m3_to_bf16x2<false>(lo); w[1] = int4e4m3_to_bf16x2<true>(lo);
+    w[2] = int4e4m3_to_bf16x2<false>(hi); w[3] = int4e4m3_to_bf16x2<true>(hi);
+  } else {
+    w[0] = code8x2_to_bf16x2<CDT, false>(d[0]); w[1] = code8x2_to_bf16x2<CDT, true>(d[0]);
+    w[2] = code8x2_to_bf16x2<CDT, false>(d[1]); w[3] = code8x2_to_bf16x2<CDT, true>(d[1]);
+  }
+  return __builtin_bit_cast(mf_bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+// dwords of the lane's codes per 8 dims
+template <int CDT>
+constexpr int mf_dw8() { return CDT == PA_BF16 ? 4 : CDT == PA_INT4 ? 1 : 2; }
+
+// LDS column of dim c of a token row: INT4 rows keep each 8 dims in the
+// converter's order 0 2 4 6 1 3 5 7, the others in order.
+template <int CDT>
+__device__ __forceinline__ int mf_dim_of_col(int c) {
+  if constexpr (CDT == PA_INT4) {
+    const int p = c & 7;
+    return (c & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
+  } else {
+    return c;
+  }
+}
+
+template <int CDT, int HD, int G, int NBUF>
+__device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kvh, int st0,
+                                              int st1, int64_t slot, uint8_t* vl) {
+  using ML = MfLayout<CDT, HD>;
+  constexpr int DW8 = mf_dw8<CDT>();
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4, r = lane & 15;
+  const int ctx = uniform_load(a.context_lens, s);
+  const int begin = st0 * 16;
+  const int end = min(ctx, st1 * 16);
+  const int n_q = a.n_kv * G;
+  const float c = a.score_scale;
+
+  // B operand of QK: head r, dims j DPJ + 8t + e (INT4: times the key scale of
+  // the channel, in the converter's pair order); zero for r >= G
+  mf_bf16x8_t qb[ML::NT];
+  {
+    const int h = r < G ? r : 0;
+    const uint8_t* qp = a.q + ((int64_t)s * n_q + (int64_t)kvh * G + h) * HD * 2;
+#pragma unroll
+    for (int t = 0; t < ML::NT; ++t) {
+      const int d0 = mf_dim0<ML>(t, j);
+      const uint4 x = *(const uint4*)(qp + 2 * d0);
+      uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      if constexpr (CDT == PA_INT4) {
+        const float* ks = a.k_ch_scale + (int64_t)kvh * HD + d0;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = bf16lo_f32(w[e]) * ks[2 * e];
+          f[2 * e + 1] = bf16hi_f32(w[e]) * ks[2 * e + 1];
+        }
+        w[0] = pack_bf16(f[0], f[2]); w[1] = pack_bf16(f[4], f[6]);
+        w[2] = pack_bf16(f[1], f[3]); w[3] = pack_bf16(f[5], f[7]);
+      }
+      if (r >= G) w[0] = w[1] = w[2] = w[3] = 0u;
+      qb[t] = __builtin_bit_cast(mf_bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  }
+
+  mf_f32x4_t acc[ML::NB];
+#pragma unroll
+  for (int b = 0; b < ML::NB; ++b) acc[b] = mf_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -1e30f;     // running max of head column r (base-2 units, scaled)
+  float lp = 0.0f;      // this lane's share of l for column r
+
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+  const uint32_t lane_off = (uint32_t)(r * (int)a.tok_stride + kvh * ML::ROW + j * ML::PS);
+  // Block ids, 64 at a time in a vector register (lane i: table entry c0 + i),
+  // the next 64 loaded a chunk ahead: a step picks its id with a lane read and
+  // never waits on a table load (a scalar load would make every step wait for
+  // its latency, together with the wave's LDS traffic).
+  const int jlast = min((end - 1) >> a.bs_log2, a.max_blocks - 1);
+  auto tload = [&](int c0) -> int {
+    const int jj = c0 + lane;
+    return jj <= jlast ? table[jj] : 0;
+  };
+  int c0 = begin >> a.bs_log2;
+  int tA = tload(c0), tB = tload(c0 + 64);
+  auto block_at = [&](int base) -> int {   // base: wave-uniform, non-decreasing
+    const int jb = base >> a.bs_log2;
+    while (jb >= c0 + 64) {
+      c0 += 64;
+      tA = tB;
+      tB = tload(c0 + 64);
+    }
+    const int blk = __builtin_amdgcn_readlane(tA, jb - c0);
+    return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+  };
+
+  auto step = [&](const MfFrag<ML>& f, int base) {
+    // S^T: tokens 4j .. 4j+3 of head column r
+    mf_f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < ML::NT; ++t)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_k8<CDT>(f.k + DW8 * t), qb[t], sc, 0, 0, 0);
+    // V rows (bf16) into this wave's LDS slice: token r, this lane's dims
+    {
+      uint8_t* row = vl + r * ML::VROW;
+#pragma unroll
+      for (int t = 0; t < ML::NT; ++t) {
+        const mf_bf16x8_t v8 = mf_k8<CDT>(f.v + DW8 * t);
+        *(uint4*)(row + 2 * mf_dim0<ML>(t, j)) = __builtin_bit_cast(uint4, v8);
+      }
+    }
+    // softmax of column r over the step's 16 tokens
+    const int nvalid = end - base;   // >= 1
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * j + i < nvalid) ? sc[i] * c : -INFINITY;
+    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    if (__any(tmax > m + DMF_SLACK)) {   // wave-uniform: rescale to the new max
+      const float mn = fmaxf(m, tmax);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      lp *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {      // rows 4j+i of O belong to head column 4j+i
+        const float ai = __shfl(alpha, 4 * j + i, 64);
+#pragma unroll
+        for (int b = 0; b < ML::NB; ++b) acc[b][i] *= ai;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m);
+    uint32_t P0, P1;
+    if constexpr (CDT == PA_INT4) {     // value scale of each token into its weight
+      lp += (p[0] + p[1]) + (p[2] + p[3]);
+      P0 = pack_bf16(p[0] * f.vs[0], p[1] * f.vs[1]);
+      P1 = pack_bf16(p[2] * f.vs[2], p[3] * f.vs[3]);
+    } else {                            // l from the rounded weights
+      P0 = pack_bf16(p[0], p[1]);
+      P1 = pack_bf16(p[2], p[3]);
+      lp = dot2_bf16(P0, 0x3F803F80u, lp);
+      lp = dot2_bf16(P1, 0x3F803F80u, lp);
+    }
+    const mf_s4_t pa4 = __builtin_bit_cast(mf_s4_t, make_uint2(P0, P1));
+    // V^T blocks: lane (j, r) gets tokens 4j .. 4j+3 of LDS column 16 b + r
+    const uint8_t* rd = vl + (4 * j + (r >> 2)) * ML::VROW + (r & 3) * 8;
+#pragma unroll
+    for (int b = 0; b < ML::NB; ++b) {
+      const mf_s4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) mf_s4_t*)(rd + 32 * b));
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb, acc[b], 0, 0, 0);
+    }
+  };
+
+  // NBUF steps in flight; the same loads are issued on every path (past the
+  // last step through an empty descriptor)
+  const int nsteps = (end - begin + 15) >> 4;
+  MfFrag<ML> buf[NBUF];
+  auto prefetch = [&](MfFrag<ML>& f, int pf) {
+    const int base = begin + 16 * min(pf, nsteps - 1);
+    mf_load_step<CDT, ML>(f, a, block_at(base), base, end, lane_off, pf < nsteps, kvh, j);
+  };
+#pragma unroll
+  for (int d = 0; d < NBUF - 1; ++d) prefetch(buf[d], d);
+  int i = 0;
+  for (; i + NBUF <= nsteps; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
+      step(buf[u], begin + 16 * (i + u));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) {
+    prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
+    if (i + u < nsteps) step(buf[u], begin + 16 * (i + u));
+  }
+
+  // the piece's partial: l of column r summed over its four lanes; O rows 4j+i
+  const float lsum = lp + __shfl_xor(lp, 16, 64);
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  float* out_o = a.part_o + slot * G * HD;
+  float* out_ml = a.part_ml + slot * G * 2;
+  const int dcol = mf_dim_of_col<CDT>(r);   // dim of LDS column r within each 16-block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * j + i;
+    if (h < G) {
+#pragma unroll
+      for (int b = 0; b < ML::NB; ++b) out_o[h * HD + 16 * b + dcol] = acc[b][i];
+    }
+  }
+  if (j == 0 && r < G) *(float2*)(out_ml + 2 * r) = make_float2(m, ltot);
+}
+
+// The matrix-core split kernel: the work loop of decode_split_kernel with
+// decode_run_mf, and an LDS slice per wave for its V tile.
+#ifndef DECODE_MF_MIN_WGS
+#define DECODE_MF_MIN_WGS 1   // workgroups per CU the register budget must allow
+#endif
+template <int CDT, int HD, int G, int NBUF>
+__global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_mfma_kernel(DecodeArgs a) {
+  using ML = MfLayout<CDT, HD>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DECODE_MAX_HW * ML::WAVE_LDS];
+  const int w = blockIdx.x;
+  const int W = a.num_wgs;
+  const int wv = threadIdx.x >> 6;
+  int pre, U;
+  unit_counts(a.context_lens, a.num_seqs, a.nhg, 0, &pre, &U);
+  if (w == 0 && threadIdx.x == 0) *(int2*)a.header = make_int2(W, a.hw);   // for the merge
+  const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
+  if (u0 >= u1) return;
+  int s, before;
+  locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
+  const int steps0 = steps_of(uniform_load(a.context_lens, s));
+  const int rr = (int)u0 - before;
+  int hg = rr / steps0;
+  int step = rr % steps0;
+  int64_t u = u0;
+  uint8_t* vl = lds + wv * ML::WAVE_LDS;
+  while (true) {
+    const int steps = steps_of(uniform_load(a.context_lens, s));
+    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
+    const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
+    decode_run_mf<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv, vl);
+    u += run_end - step;
+    if (u >= u1) break;
+    step = 0;
+    if (++hg == a.nhg) {               // next sequence that has tokens
+      hg = 0;
+      do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
+    }
+  }
+}
+
 // One wave per (sequence, query head): combine the pieces' (m, l, O).
 template <int HD, int G, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
@@ -857,15 +1209,63 @@ static int64_t resident_wgs(int hw) {
   return cached[hw];
 }
 
+// Cache dtypes whose decode runs on the matrix cores (bit = dtype code) when
+// block_size >= 16: int4 and int8, whose codes cost the most vector-ALU work to
+// widen (on the long-tail step, int4 364 -> 259 us, int8 399 -> 361 us).  fp8
+// runs as fast on either path and bf16 is bound by HBM on the vector path.
+#ifndef DECODE_MFMA_MASK
+#define DECODE_MFMA_MASK ((1 << PA_INT8) | (1 << PA_INT4))
+#endif
+// steps in flight per wave on the matrix-core path (fewer bytes per step for
+// narrower codes, so more steps)
+#ifndef DECODE_MF_NBUF4
+#define DECODE_MF_NBUF4 4   // INT4
+#endif
+#ifndef DECODE_MF_NBUF8
+#define DECODE_MF_NBUF8 3   // FP8 / INT8
+#endif
+__host__ __device__ constexpr int mf_nbuf(int CDT) {
+  return CDT == PA_INT4 ? DECODE_MF_NBUF4 : CDT == PA_BF16 ? 2 : DECODE_MF_NBUF8;
+}
+
+template <int CDT, int HD, int G>
+static int64_t resident_wgs_mf(int hw) {
+  static int64_t cached[DECODE_MAX_HW + 1] = {};
+  if (!cached[hw]) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT)>, 64 * hw, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    const int target = (DECODE_WAVES_PER_CU + hw - 1) / hw;
+    if (per_cu > target) per_cu = target;
+    cached[hw] = (int64_t)device_cu_count() * per_cu;
+  }
+  return cached[hw];
+}
+
 template <int CDT, int HD, int G>
 static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
+  constexpr bool MF = (DECODE_MFMA_MASK >> CDT) & 1;
   const int hw = heads_per_wg(CDT, a.n_kv, G);
+  const bool mf = MF && a.block_size >= 16;
   const int64_t bound = wgs_bound(hw, a.num_seqs, a.n_kv, max_context_len, split_tokens);
-  int64_t W = split_tokens > 0 ? bound : resident_wgs<CDT, HD, G>(hw);
+  int64_t W = bound;
+  if (split_tokens <= 0) {
+    if constexpr (MF) W = mf ? resident_wgs_mf<CDT, HD, G>(hw) : resident_wgs<CDT, HD, G>(hw);
+    else W = resident_wgs<CDT, HD, G>(hw);
+  }
   if (W > bound) W = bound;
   a.num_wgs = (int)W;
   a.hw = hw;
   a.nhg = a.n_kv / hw;
+  if constexpr (MF) {
+    if (mf) {
+      hipLaunchKernelGGL((decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT)>), dim3((unsigned)W),
+                         dim3(64 * hw), 0, st, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W),
                      dim3(64 * hw), 0, st, a);
 }

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 // sign-magnitude nibbles, element 2i in the low nibble.  A key element is
 // encoded with its channel's scale (k_channel_scales[head][dim], from the
 // caller); a value row (token, head) gets the scale sigma = amax / 7 of its
-// own elements (NaN ignored), stored in v_scales at the token's slot.
+// own elements (NaN ignored), stored in v_scales[block][head][offset].
 //
 // One row is head_dim / 8 lanes of 8 elements each (16 lanes at head_dim 128);
 // the lanes of a value row find its amax with shuffles inside the row's lane
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void kv_append_int4_kernel(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ v_scales,
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int64_t* __restrict__ slots, const float* __restrict__ k_channel_scales,
-    int64_t num_slots_in_pool, int n_kv, int lanes_per_row, int total_lanes) {
+    int64_t num_slots_in_pool, int block_size, int n_kv, int lanes_per_row, int total_lanes) {
   const int lane = blockIdx.x * blockDim.x + threadIdx.x;
   // every lane of a row takes part in the row's shuffles: no early return
   // before them (rows never straddle a wave: lanes_per_row divides 64)
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256) void kv_append_int4_kernel(
     const float r = 1.0f / sigma;
 #pragma unroll
     for (int i = 0; i < 8; ++i) inv[i] = r;
-    if (ok && j == 0) v_scales[slot * n_kv + head] = sigma;
+    if (ok && j == 0)   // [block][head][offset]
+      v_scales[((slot / block_size) * n_kv + head) * block_size + slot % block_size] = sigma;
   }
   uint32_t packed = 0u;
 #pragma unroll
@@ -335,7 +336,7 @@ extern "C" pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_sc
   auto kernel = src_dtype == PA_BF16 ? kv_append_int4_kernel<PA_BF16> : kv_append_int4_kernel<PA_F32>;
   hipLaunchKernelGGL(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
                      (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new,
-                     slot_mapping, k_channel_scales, (int64_t)num_blocks * block_size, n_kv_heads,
-                     lanes_per_row, total);
+                     slot_mapping, k_channel_scales, (int64_t)num_blocks * block_size, block_size,
+                     n_kv_heads, lanes_per_row, total);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

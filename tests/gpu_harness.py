@@ -47,7 +47,7 @@ class DeviceWorkload:
         self.q = w.q.to(dev) if w.q is not None else None
         if w.cache_dtype == "int4":
             from workloads import INT4_SCALE_POISON
-            self.v_scales = torch.full((w.num_blocks, w.block_size, w.n_kv_heads),
+            self.v_scales = torch.full((w.num_blocks, w.n_kv_heads, w.block_size),
                                        int(INT4_SCALE_POISON) - (1 << 32), dtype=torch.int32,
                                        device=dev).view(torch.float32)
             self.k_channel_scales = torch.as_tensor(w.k_channel_scales, device=dev)

@@ -74,7 +74,8 @@ def oracle_pools_int4(w: Workload, include_new: bool = True, seqs=None):
     shape = (w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim // 2)
     pk = np.full(shape, POISON["int4"], np.uint8)
     pv = np.full(shape, POISON["int4"], np.uint8)
-    ps = np.full(shape[:3], INT4_SCALE_POISON, np.uint32).view(np.float32)
+    ps = np.full((w.num_blocks, w.n_kv_heads, w.block_size), INT4_SCALE_POISON,
+                 np.uint32).view(np.float32)
     src = w.src_dtype
     if seqs is None:
         seqs = list(range(w.num_seqs))

@@ -53,7 +53,7 @@ def test_int4_append_bit_exact(dev, src, hd):
     slots[::37] = -1                                      # skipped rows
     pk = np.full((nb, bs, nkv, hd // 2), 0x77, np.uint8)
     pv = pk.copy()
-    ps = np.full((nb, bs, nkv), INT4_SCALE_POISON, np.uint32).view(np.float32)
+    ps = np.full((nb, nkv, bs), INT4_SCALE_POISON, np.uint32).view(np.float32)
     gk, gv = torch.as_tensor(pk, device=dev), torch.as_tensor(pv, device=dev)
     gs = torch.as_tensor(ps.copy(), device=dev)
     pa.pa_kv_append_int4(gk, gv, gs, k.to(dev), v.to(dev), torch.as_tensor(slots, device=dev),
@@ -130,7 +130,7 @@ def test_int4_one_hot_reproduces_every_code(dev):
         kx[cu[s] + target[s]] = 7.0                      # codes +7 at key scale 1
     q = torch.ones((B, nkv * G, hd), dtype=torch.bfloat16, device=dev)
     pools = [torch.full((nb, bs, nkv, hd // 2), 0x77, dtype=torch.uint8, device=dev) for _ in "kv"]
-    vs = torch.full((nb, bs, nkv), float("nan"), device=dev)
+    vs = torch.full((nb, nkv, bs), float("nan"), device=dev)
     ks = torch.ones((nkv, hd), device=dev)
     tab = torch.as_tensor(tables, device=dev)
     slots = pa.pa_slot_mapping(tab, torch.as_tensor(cu.astype(np.int32), device=dev),

@@ -116,7 +116,7 @@ def _tiny_int4_cache(rng, nb=12, bs=4, nkv=2, hd=16, B=3):
         used += nblk[s]
     pk = np.full((nb, bs, nkv, hd // 2), 0x77, np.uint8)
     pv = np.full((nb, bs, nkv, hd // 2), 0x77, np.uint8)
-    ps = np.full((nb, bs, nkv), np.nan, np.float32)
+    ps = np.full((nb, nkv, bs), np.nan, np.float32)
     ks = rng.uniform(0.1, 1.0, (nkv, hd)).astype(np.float32)
     for s in range(B):
         n = int(ctx[s])
@@ -154,7 +154,7 @@ def test_int4_decode_equals_attention_over_unpacked_values():
                 blk, off = tables[s, p // bs], p % bs
                 for d in range(hd):
                     K[p, d] = nib(pk[blk, off, g, d // 2], d % 2) * float(ks[g, d])
-                    V[p, d] = nib(pv[blk, off, g, d // 2], d % 2) * float(ps[blk, off, g])
+                    V[p, d] = nib(pv[blk, off, g, d // 2], d % 2) * float(ps[blk, g, off])
             sc = 0.25 * (K @ qf[s, h])
             w = np.exp(sc - sc.max())
             ref = (w @ V) / w.sum()
