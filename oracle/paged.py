@@ -170,6 +170,30 @@ def decode_int4(q_codes, q_dtype, pool_k, pool_v, v_scale_pool, k_channel_scales
     return out
 
 
+def prefill_chunk_int4(q_codes, q_dtype, cu_seqlens_q, pool_k, pool_v, v_scale_pool,
+                       k_channel_scales, block_tables, context_lens, block_size: int,
+                       group_size: int, scale: float, causal: bool = True, rows=None):
+    """Chunk attention over an INT4 cache: as ``prefill_chunk`` on the dequantised K/V."""
+    q = codecs.decode(q_codes, q_dtype)
+    out = np.zeros(q.shape, dtype=np.float64)
+    n_q = q.shape[1]
+    seqs = range(len(cu_seqlens_q) - 1) if rows is None else rows
+    for s in seqs:
+        a, b = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        L, T = b - a, int(context_lens[s])
+        if L == 0:
+            continue
+        K, V = int4_seq_kv(pool_k, pool_v, v_scale_pool, block_tables[s], T, block_size,
+                           k_channel_scales)
+        pos = T - L + np.arange(L)
+        keys = np.arange(T)
+        allowed = (keys[None, :] <= pos[:, None]) if causal else np.ones((L, T), bool)
+        for h in range(n_q):
+            g = h // group_size
+            out[a:b, h] = attention_two_pass(q[a:b, h], K[:, g, :], V[:, g, :], scale, allowed)
+    return out
+
+
 def copy_blocks(dst_pool, src_pool, pairs):
     """Whole-block copies: dst_pool[d] = src_pool[s] for every pair (s, d).
 

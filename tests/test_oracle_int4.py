@@ -174,3 +174,33 @@ def test_int4_decode_invariant_under_block_relabelling():
     t2 = np.where(tables >= 0, perm[np.maximum(tables, 0)], -1)
     b = paged.decode_int4(qc, "bf16", pk[inv], pv[inv], ps[inv], ks, t2, ctx, bs, G, 0.3)
     assert np.array_equal(a, b)
+
+
+def test_int4_prefill_rows_match_decode_and_causality():
+    """prefill_chunk_int4: a chunk's last query equals decode_int4 of the sequence,
+    each earlier query equals decode_int4 over the cache truncated at its position,
+    and the non-causal chunk lets every query see every key."""
+    rng = np.random.default_rng(8)
+    nkv, hd, G, bs = 2, 16, 2, 4
+    pk, pv, ps, ks, tables, ctx = _tiny_int4_cache(rng, bs=bs, nkv=nkv, hd=hd)
+    B = len(ctx)
+    L = np.minimum(ctx, np.array([3, 1, 5])[:B])
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+    q = torch.from_numpy(rng.standard_normal((int(cu[-1]), nkv * G, hd)).astype(np.float32))
+    qc = q.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = paged.prefill_chunk_int4(qc, "bf16", cu, pk, pv, ps, ks, tables, ctx, bs, G, 0.3)
+    for s in range(B):
+        for i in range(int(L[s])):
+            T = int(ctx[s]) - int(L[s]) + i + 1       # keys visible to query i
+            qd = np.zeros((B, nkv * G, hd), np.uint16)
+            qd[s] = qc[cu[s] + i]
+            ref = paged.decode_int4(qd, "bf16", pk, pv, ps, ks, tables,
+                                    np.where(np.arange(B) == s, T, ctx), bs, G, 0.3, rows=[s])
+            assert np.allclose(got[cu[s] + i], ref[0], rtol=1e-12, atol=1e-12)
+    full = paged.prefill_chunk_int4(qc, "bf16", cu, pk, pv, ps, ks, tables, ctx, bs, G, 0.3,
+                                    causal=False)
+    for s in range(B):
+        qd = np.zeros((B, nkv * G, hd), np.uint16)
+        qd[s] = qc[cu[s]]
+        ref = paged.decode_int4(qd, "bf16", pk, pv, ps, ks, tables, ctx, bs, G, 0.3, rows=[s])
+        assert np.allclose(full[cu[s]], ref[0], rtol=1e-12, atol=1e-12)
