@@ -368,6 +368,24 @@ pa_status pa_decode_int4_partials(const void* q, int q_dtype, const void* k_cach
                                   int32_t max_context_len, float scale, int32_t split_tokens,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_prefill_chunk_int4 -- pa_prefill_chunk over an INT4 cache (q_dtype BF16;
+ * the key and value scales as for pa_decode_int4, no per-tensor scales).  The
+ * output is the chunk attention over the dequantised keys and values.  The
+ * workspace is pa_prefill_workspace_bytes(...); pa_prefill_chunk returns
+ * PA_ERR_DTYPE for cache_dtype PA_INT4.
+ */
+pa_status pa_prefill_chunk_int4(void* out, const void* q, int q_dtype,
+                                const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                                int32_t max_q_len, const void* k_cache, const void* v_cache,
+                                const float* k_channel_scales, const float* v_scales,
+                                int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t group_size,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                int32_t causal, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

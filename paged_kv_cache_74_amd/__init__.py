@@ -66,6 +66,8 @@ def lib():
         _c("pa_prefill_workspace_bytes", S, I, I, I, I, I, I, I)
         _c("pa_prefill_chunk", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, ctypes.c_int, I, I,
            I, I, I, P, I, P, I, I, F, F, F, P, S, P)
+        _c("pa_prefill_chunk_int4", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, P, P, I, I,
+           I, I, I, P, I, P, I, I, F, P, S, P)
     return _lib
 
 
@@ -314,6 +316,36 @@ def pa_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), max_context_len,
         1 if causal else 0, scale, k_scale, v_scale, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def pa_prefill_chunk_int4(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          v_scales: torch.Tensor, k_channel_scales: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
+                          scale: float, causal: bool = True, out: torch.Tensor | None = None,
+                          ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Ragged chunk attention over an INT4 cache: q [total_q, n_q, hd] bf16 -> out."""
+    L = lib()
+    nb, bs, nkv, hd = _int4_pools(k_cache, v_cache, v_scales, k_channel_scales)
+    _dev(q, cu_seqlens_q, block_tables, context_lens)
+    total_q, nq, hd2 = q.shape
+    B = cu_seqlens_q.numel() - 1
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(cu_seqlens_q.dtype == block_tables.dtype == context_lens.dtype == torch.int32, "int32")
+    _need(block_tables.shape[0] >= B and context_lens.shape[0] >= B, "one table row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    need = pa_prefill_workspace_bytes(B, total_q, max_q_len, nq, nkv, hd, max_context_len)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    _check("pa_prefill_chunk_int4", L.pa_prefill_chunk_int4(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(cu_seqlens_q), B, total_q, max_q_len,
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_channel_scales), _ptr(v_scales), nb, bs, nkv, hd,
+        nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        max_context_len, 1 if causal else 0, scale, _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
     return out
 
 

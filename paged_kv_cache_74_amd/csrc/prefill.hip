@@ -78,6 +78,8 @@ struct PrefillArgs {
   int causal;
   float score_scale;         // scale * k_scale * log2(e)
   float out_scale;           // v_scale for 8-bit caches, else 1
+  const float* k_ch_scale;   // INT4: [n_kv][HD] key scale per channel
+  const float* v_tok_scale;  // INT4: [num_blocks][n_kv][block_size] value scale per token
 };
 
 template <int CDT, int HD>
@@ -86,6 +88,8 @@ struct PrefillLds {
   static constexpr int VROW = PF_BN * 2 + 8;      // bytes per dim row of V^T (padded)
   static constexpr int K_BYTES = PF_BN * KROW;
   static constexpr int V_BYTES = HD * VROW;
+  static constexpr int SIG_BYTES = CDT == PA_INT4 ? PF_BN * 4 : 0;   // INT4 value scales
+  static constexpr int BUF = K_BYTES + V_BYTES + SIG_BYTES;
 };
 
 // Workgroups are dispatched to the chip's 8 XCDs round robin (workgroup b on
@@ -246,21 +250,23 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
   }
 }
 
-// K/V element rows of one tile for this thread: keys key0, key0 + 1, chunk lc.
+// K/V element rows of one tile for this thread: keys key0, key0 + 1, chunk lc
+// (and, for INT4, the two keys' value scales).
 struct TileRegs {
   uint32_t k0[4], k1[4], v0[4], v1[4];
+  float s0, s1;
 };
 
-// Address of token `key` clamped into [0, T): every load is issued and lands
+// Pool index of token `key` clamped into [0, T): every load is issued and lands
 // on a real token, so the count in flight is fixed; keys >= T are masked out
 // of the scores (their probability is 0 and the clamped V row is finite).
-__device__ __forceinline__ int64_t token_off(const PrefillArgs& a, const int32_t* table, int key,
-                                             int T) {
+__device__ __forceinline__ int64_t token_index(const PrefillArgs& a, const int32_t* table, int key,
+                                               int T) {
   const int kc = min(key, T - 1);
   const int j = min(kc >> a.bs_log2, a.max_blocks - 1);
   int blk = table[j];
   blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
-  return ((int64_t)blk * a.block_size + (kc & (a.block_size - 1))) * a.tok_stride;
+  return (int64_t)blk * a.block_size + (kc & (a.block_size - 1));
 }
 
 template <int CDT>
@@ -268,19 +274,33 @@ __device__ __forceinline__ void load8(const uint8_t* p, uint32_t (&d)[4]) {
   if constexpr (CDT == PA_BF16) {
     const uint4 x = *(const uint4*)p;
     d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+  } else if constexpr (CDT == PA_INT4) {   // 8 codes in 4 bytes, widened when stored
+    d[0] = *(const uint32_t*)p; d[1] = 0u; d[2] = 0u; d[3] = 0u;
   } else {   // 8-bit codes: keep the raw bytes, widened when stored to LDS
     const uint2 x = *(const uint2*)p;
     d[0] = x.x; d[1] = x.y; d[2] = 0u; d[3] = 0u;
   }
 }
 
+// 8 codes -> 4 bf16 pairs (exact).  INT4 pairs come out as elements (0,2)
+// (4,6) (1,3) (5,7) of the 8 (the converter's order); the others in order.
 template <int CDT>
 __device__ __forceinline__ void widen(uint32_t (&d)[4]) {
-  if constexpr (CDT == PA_FP8_E4M3 || CDT == PA_INT8) {   // 8 codes -> 4 bf16 pairs (exact)
+  if constexpr (CDT == PA_FP8_E4M3 || CDT == PA_INT8) {
     const uint32_t x = d[0], y = d[1];
     d[0] = code8x2_to_bf16x2<CDT, false>(x); d[1] = code8x2_to_bf16x2<CDT, true>(x);
     d[2] = code8x2_to_bf16x2<CDT, false>(y); d[3] = code8x2_to_bf16x2<CDT, true>(y);
+  } else if constexpr (CDT == PA_INT4) {
+    const uint32_t lo = int4_lo_as_e4m3(d[0]), hi = int4_hi_as_e4m3(d[0]);
+    d[0] = int4e4m3_to_bf16x2<false>(lo); d[1] = int4e4m3_to_bf16x2<true>(lo);
+    d[2] = int4e4m3_to_bf16x2<false>(hi); d[3] = int4e4m3_to_bf16x2<true>(hi);
   }
+}
+// element of the 8 that pair i of widen() holds in its low (HI = false) or high half
+template <int CDT>
+__device__ __forceinline__ int widened_elem(int i, bool hi) {
+  if constexpr (CDT == PA_INT4) return (i & 1) * 4 + (i >> 1) + (hi ? 2 : 0);
+  else return 2 * i + (hi ? 1 : 0);
 }
 
 template <int CDT, int HD, int G>
@@ -288,12 +308,12 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
                                               int wg, uint8_t* lds) {
   using LD = PrefillLds<CDT, HD>;
   constexpr int QB = PF_ROWS / G;            // queries per segment
-  constexpr int EB = CDT == PA_BF16 ? 2 : 1;
-  constexpr int ROWB = HD * EB;              // bytes of one (token, head) row in the cache
+  constexpr int EBITS = CDT == PA_BF16 ? 16 : CDT == PA_INT4 ? 4 : 8;
+  constexpr int ROWB = HD * EBITS / 8;       // bytes of one (token, head) row in the cache
   constexpr int NDT = HD / 32;               // 32-dim output tiles
   constexpr int NKT = HD / 16;               // 16-dim steps of the score MFMA
   constexpr int CHUNKS = HD / 8;
-  constexpr int BUF = LD::K_BYTES + LD::V_BYTES;
+  constexpr int BUF = LD::BUF;
 
   const int32_t* desc = (const int32_t*)a.seg_desc + 4 * (int64_t)g;
   const int s = uniform_load(desc, 0), kvh = uniform_load(desc, 1), qt = uniform_load(desc, 2);
@@ -325,6 +345,20 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
     for (int t = 0; t < NKT; ++t) {
       const uint4 x = *(const uint4*)(qp + t * 32);
       qreg[t][0] = x.x; qreg[t][1] = x.y; qreg[t][2] = x.z; qreg[t][3] = x.w;
+      if constexpr (CDT == PA_INT4) {
+        // times each channel's key scale, rounded to bf16, in the order the
+        // widened key codes sit in LDS
+        const float* ks = a.k_ch_scale + (int64_t)kvh * HD + 16 * t + 8 * grp;
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = bf16lo_f32(w[e]) * ks[2 * e];
+          f[2 * e + 1] = bf16hi_f32(w[e]) * ks[2 * e + 1];
+        }
+        qreg[t][0] = pack_bf16(f[0], f[2]); qreg[t][1] = pack_bf16(f[4], f[6]);
+        qreg[t][2] = pack_bf16(f[1], f[3]); qreg[t][3] = pack_bf16(f[5], f[7]);
+      }
     }
   }
   const int first_pos = T - L + qt * QB;
@@ -347,7 +381,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   const int lp = tid % (PF_BN / 2);
   const int lc = (tid / (PF_BN / 2)) % CHUNKS;
   constexpr bool loader = true;
-  const int64_t col = (int64_t)kvh * ROWB + lc * 8 * EB;
+  const int64_t col = (int64_t)kvh * ROWB + lc * EBITS;   // 8 elements of EBITS bits
 
   const int jmax = min((T - 1) >> a.bs_log2, a.max_blocks - 1);
   auto gload = [&](int t, TileRegs& R) {
@@ -365,21 +399,28 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
     }
     if (loader) {
       const int key0 = t * PF_BN + 2 * lp;
-      int64_t o0, o1;
+      int64_t tk0, tk1;   // pool token indices of the two keys
       if (a.block_size >= 16) {
         const int k0c = min(key0, T - 1), k1c = min(key0 + 1, T - 1);
         const int b0 = (k0c >> a.bs_log2) == jlo ? blo : bhi;
         const int b1 = (k1c >> a.bs_log2) == jlo ? blo : bhi;
-        o0 = ((int64_t)b0 * a.block_size + (k0c & (a.block_size - 1))) * a.tok_stride + col;
-        o1 = ((int64_t)b1 * a.block_size + (k1c & (a.block_size - 1))) * a.tok_stride + col;
+        tk0 = (int64_t)b0 * a.block_size + (k0c & (a.block_size - 1));
+        tk1 = (int64_t)b1 * a.block_size + (k1c & (a.block_size - 1));
       } else {
-        o0 = token_off(a, table, key0, T) + col;
-        o1 = token_off(a, table, key0 + 1, T) + col;
+        tk0 = token_index(a, table, key0, T);
+        tk1 = token_index(a, table, key0 + 1, T);
       }
+      const int64_t o0 = tk0 * a.tok_stride + col, o1 = tk1 * a.tok_stride + col;
       load8<CDT>(a.k_cache + o0, R.k0);
       load8<CDT>(a.k_cache + o1, R.k1);
       load8<CDT>(a.v_cache + o0, R.v0);
       load8<CDT>(a.v_cache + o1, R.v1);
+      if constexpr (CDT == PA_INT4) {   // the two keys' value scales ([block][head][offset])
+        R.s0 = a.v_tok_scale[((tk0 >> a.bs_log2) * a.n_kv + kvh) * a.block_size +
+                             (tk0 & (a.block_size - 1))];
+        R.s1 = a.v_tok_scale[((tk1 >> a.bs_log2) * a.n_kv + kvh) * a.block_size +
+                             (tk1 & (a.block_size - 1))];
+      }
     }
   };
   auto sstore = [&](TileRegs& R, uint8_t* buf) {
@@ -391,10 +432,13 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       *(uint4*)(lk + (2 * lp + 1) * LD::KROW + lc * 16) = make_uint4(R.k1[0], R.k1[1], R.k1[2], R.k1[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {   // V^T[d][key0, key0 + 1] as bf16 pairs
-        const int d = lc * 8 + 2 * i;
-        *(uint32_t*)(lv + d * LD::VROW + 4 * lp) = pair_lo(R.v0[i], R.v1[i]);
-        *(uint32_t*)(lv + (d + 1) * LD::VROW + 4 * lp) = pair_hi(R.v0[i], R.v1[i]);
+        const int dl = lc * 8 + widened_elem<CDT>(i, false);
+        const int dh = lc * 8 + widened_elem<CDT>(i, true);
+        *(uint32_t*)(lv + dl * LD::VROW + 4 * lp) = pair_lo(R.v0[i], R.v1[i]);
+        *(uint32_t*)(lv + dh * LD::VROW + 4 * lp) = pair_hi(R.v0[i], R.v1[i]);
       }
+      if constexpr (CDT == PA_INT4)
+        if (lc == 0) *(float2*)(buf + LD::K_BYTES + LD::V_BYTES + 8 * lp) = make_float2(R.s0, R.s1);
     }
   };
   auto compute = [&](const uint8_t* buf, int kt) {
@@ -436,15 +480,30 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
       m = mn;
     }
+    // INT4: the value scales of this lane's 16 keys (key 4 grp + 8 q + e of the tile)
+    float sg[16];
+    if constexpr (CDT == PA_INT4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = *(const float4*)(buf + LD::K_BYTES + LD::V_BYTES + 4 * (4 * grp + 8 * q));
+        sg[4 * q] = x.x; sg[4 * q + 1] = x.y; sg[4 * q + 2] = x.z; sg[4 * q + 3] = x.w;
+      }
+    }
     // O^T += V^T P^T; k index (grp, e) of slice t <-> key 16t + 8(e/4) + 4 grp + e%4
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t P[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        P[i] = pack_bf16(fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i], c, -m)),
-                         fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i + 1], c, -m)));
-        lsum = dot2_bf16(P[i], 0x3F803F80u, lsum);
+        const float p0 = fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i], c, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i + 1], c, -m));
+        if constexpr (CDT == PA_INT4) {   // value scale into the weight; l unscaled, fp32
+          P[i] = pack_bf16(p0 * sg[8 * t + 2 * i], p1 * sg[8 * t + 2 * i + 1]);
+          lsum += p0 + p1;
+        } else {
+          P[i] = pack_bf16(p0, p1);
+          lsum = dot2_bf16(P[i], 0x3F803F80u, lsum);
+        }
       }
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(P[0], P[1], P[2], P[3]));
 #pragma unroll
@@ -508,7 +567,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
 template <int CDT, int HD, int G>
 __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillArgs a) {
   using LD = PrefillLds<CDT, HD>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (LD::K_BYTES + LD::V_BYTES)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LD::BUF];
   const int W = gridDim.x;
   const int wg = xcd_local_order(blockIdx.x, W);
   const int64_t U = uniform_load(a.hdr, 1);
@@ -685,16 +744,16 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, 
                    (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
 }
 
-extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
-                                      const int32_t* cu_seqlens_q, int32_t num_seqs,
-                                      int32_t total_q, int32_t max_q_len, const void* k_cache,
-                                      const void* v_cache, int cache_dtype, int32_t num_blocks,
-                                      int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
-                                      int32_t group_size, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                      int32_t max_context_len, int32_t causal, float scale,
-                                      float k_scale, float v_scale, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32_t* cu_seqlens_q,
+                              int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                              const void* k_cache, const void* v_cache, int cache_dtype,
+                              int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t group_size, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t max_context_len, int32_t causal, float scale,
+                              float k_scale, float v_scale, void* workspace,
+                              size_t workspace_bytes, void* stream,
+                              const float* k_channel_scales, const float* v_scales) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || n_kv_heads < 1 ||
       max_blocks_per_seq < 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
@@ -702,12 +761,14 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1))) return PA_ERR_UNSUPPORTED;
   if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
     return PA_ERR_UNSUPPORTED;
-  if (q_dtype != PA_BF16 ||
-      (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_INT8))
+  const bool int4 = cache_dtype == PA_INT4;
+  if (q_dtype != PA_BF16 || (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 &&
+                             cache_dtype != PA_INT8 && !int4))
     return PA_ERR_DTYPE;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
+  if (int4 && (!k_channel_scales || !v_scales)) return PA_ERR_NULL;
   // 8-bit caches (fp8 or int8) carry per-tensor scales
   const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
@@ -730,7 +791,9 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
   a.v_cache = (const uint8_t*)v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.tok_stride = (int64_t)n_kv_heads * head_dim * (fp8 ? 1 : 2);
+  a.tok_stride = (int64_t)n_kv_heads * head_dim * (int4 ? 4 : fp8 ? 8 : 16) / 8;
+  a.k_ch_scale = k_channel_scales;
+  a.v_tok_scale = v_scales;
   a.num_blocks = num_blocks;
   a.block_size = block_size;
   int lg = 0;
@@ -749,9 +812,48 @@ extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128> : pf_dispatch_g<PA_BF16, 64>;
   else if (cache_dtype == PA_FP8_E4M3)
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_FP8_E4M3, 128> : pf_dispatch_g<PA_FP8_E4M3, 64>;
-  else
+  else if (cache_dtype == PA_INT8)
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128> : pf_dispatch_g<PA_INT8, 64>;
+  else
+    dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT4, 128> : pf_dispatch_g<PA_INT4, 64>;
   const bool ok = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, st);
   if (!ok) return PA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,
+                                      const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                      int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                      const void* v_cache, int cache_dtype, int32_t num_blocks,
+                                      int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t group_size, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t causal, float scale,
+                                      float k_scale, float v_scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (cache_dtype == PA_INT4) return PA_ERR_DTYPE;   // its scales come through pa_prefill_chunk_int4
+  return prefill_impl(out, q, q_dtype, cu_seqlens_q, num_seqs, total_q, max_q_len, k_cache,
+                      v_cache, cache_dtype, num_blocks, block_size, n_kv_heads, head_dim,
+                      group_size, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                      causal, scale, k_scale, v_scale, workspace, workspace_bytes, stream, nullptr,
+                      nullptr);
+}
+
+extern "C" pa_status pa_prefill_chunk_int4(void* out, const void* q, int q_dtype,
+                                           const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                           int32_t total_q, int32_t max_q_len,
+                                           const void* k_cache, const void* v_cache,
+                                           const float* k_channel_scales, const float* v_scales,
+                                           int32_t num_blocks, int32_t block_size,
+                                           int32_t n_kv_heads, int32_t head_dim,
+                                           int32_t group_size, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t max_context_len,
+                                           int32_t causal, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, q, q_dtype, cu_seqlens_q, num_seqs, total_q, max_q_len, k_cache,
+                      v_cache, PA_INT4, num_blocks, block_size, n_kv_heads, head_dim, group_size,
+                      block_tables, max_blocks_per_seq, context_lens, max_context_len, causal,
+                      scale, 1.0f, 1.0f, workspace, workspace_bytes, stream, k_channel_scales,
+                      v_scales);
 }

@@ -104,6 +104,12 @@ def prefill(dw: DeviceWorkload, causal=None):
     P = w.num_prefill_seqs
     cu = w.cu(w.q_lens[:P])
     q = dw.q[: int(cu[-1])]
+    if w.cache_dtype == "int4":
+        return pa.pa_prefill_chunk_int4(q, dw.k_cache, dw.v_cache, dw.v_scales,
+                                        dw.k_channel_scales, i32(cu, dw.dev), dw.tables[:P],
+                                        dw.ctx[:P], int(w.q_lens[:P].max()),
+                                        int(w.context_lens[:P].max()), w.scale,
+                                        causal=w.causal if causal is None else causal)
     return pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(cu, dw.dev), dw.tables[:P],
                                dw.ctx[:P], int(w.q_lens[:P].max()),
                                int(w.context_lens[:P].max()), w.scale,
@@ -126,11 +132,17 @@ def varlen(dw: DeviceWorkload, order=None, out=None):
     order_t = torch.as_tensor(order, device=dw.dev)
     lens = w.q_lens[order]
     q = dw.q.index_select(0, rows_t)
-    got = pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(w.cu(lens), dw.dev),
-                              dw.tables.index_select(0, order_t).contiguous(),
-                              dw.ctx.index_select(0, order_t), int(lens.max()),
-                              int(w.context_lens.max()), w.scale, causal=True,
-                              k_scale=w.k_scale, v_scale=w.v_scale, out=out)
+    tables = dw.tables.index_select(0, order_t).contiguous()
+    ctx = dw.ctx.index_select(0, order_t)
+    if w.cache_dtype == "int4":
+        got = pa.pa_prefill_chunk_int4(q, dw.k_cache, dw.v_cache, dw.v_scales,
+                                       dw.k_channel_scales, i32(w.cu(lens), dw.dev), tables, ctx,
+                                       int(lens.max()), int(w.context_lens.max()), w.scale,
+                                       causal=True, out=out)
+    else:
+        got = pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(w.cu(lens), dw.dev), tables,
+                                  ctx, int(lens.max()), int(w.context_lens.max()), w.scale,
+                                  causal=True, k_scale=w.k_scale, v_scale=w.v_scale, out=out)
     res = torch.empty_like(got)
     res[rows_t] = got
     return res

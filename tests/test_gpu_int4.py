@@ -164,3 +164,51 @@ def test_int4_full_size_sampled(dev):
     pk, pv, ps = oracle_pools_int4(w, seqs=rows)
     ref = oracle_decode_int4(w, pk, pv, ps, rows=rows)
     check_close(got[rows], ref, "bf16", "full int4 sampled")
+
+
+def _prefill_int4_vs_oracle(w, dev, what, one_launch=False, causal=True):
+    from gpu_harness import DeviceWorkload, prefill, to_f64, varlen
+    w.causal = causal
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    pk, pv, ps = oracle_pools_int4(w)
+    qc = codes(w.q, w.q_dtype)
+    if one_launch:       # the whole batch, decode rows as chunks of one query
+        got = to_f64(varlen(dw))
+        cu = w.cu(w.q_lens)
+        tables, ctx = w.block_tables, w.context_lens
+    else:
+        got = to_f64(prefill(dw))
+        P = w.num_prefill_seqs
+        cu = w.cu(w.q_lens[:P])
+        qc = qc[: cu[-1]]
+        tables, ctx = w.block_tables[:P], w.context_lens[:P]
+    ref = oracle.paged.prefill_chunk_int4(qc, w.q_dtype, cu, pk, pv, ps, w.k_channel_scales,
+                                          tables, ctx, w.block_size, w.group_size, w.scale,
+                                          causal)
+    check_close(got, ref, "bf16", what)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_int4_prefill(dev, causal):
+    w = workloads.mixed_prefill_decode(prior=(0, 77, 700), chunk_lens=(64, 100, 37), n_decode=3,
+                                       dlo=1, dhi=200, seed=2, kv="int4")
+    workloads.draw_values(w, "cpu")
+    _prefill_int4_vs_oracle(w, dev, f"int4 prefill causal={causal}", causal=causal)
+
+
+@pytest.mark.parametrize("nq,nkv,hd,bs", [(8, 4, 64, 16), (16, 2, 128, 32), (8, 1, 128, 1)])
+def test_int4_prefill_shapes(dev, nq, nkv, hd, bs):
+    w = workloads.mixed_prefill_decode(prior=(0, 40, 300, 1), chunk_lens=(50, 130, 33, 1),
+                                       n_decode=2, dlo=1, dhi=90, seed=7, n_q=nq, n_kv=nkv,
+                                       hd=hd, bs=bs, kv="int4")
+    workloads.draw_values(w, "cpu")
+    _prefill_int4_vs_oracle(w, dev, f"int4 prefill {nq}/{nkv}/{hd}/bs{bs}")
+
+
+def test_int4_mixed_step_one_launch(dev):
+    w = workloads.mixed_prefill_decode(prior=(0, 77, 700, 5), chunk_lens=(64, 100, 300, 37),
+                                       n_decode=24, dlo=1, dhi=400, seed=11, kv="int4")
+    workloads.draw_values(w, "cpu")
+    _prefill_int4_vs_oracle(w, dev, "int4 mixed one launch", one_launch=True)
