@@ -129,45 +129,63 @@ __device__ __forceinline__ int pf_owner(int64_t x, int64_t U, int W) {
 // per head: the segment count follows the batch, not num_seqs times its
 // longest chunk.
 
-// Inclusive scan of one int64 per thread over the 1024 threads of the block.
-__device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t x = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += x;
-    __syncthreads();
+// Inclusive scan of one int64 per thread over the 1024 threads of the block:
+// a shuffle scan inside each wave, then one over the 16 wave totals in LDS.
+// Returns the thread's inclusive prefix; *total gets the block's sum.
+__device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t* wsum, int64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t x = __shfl_up(v, off, 64);
+    if (lane >= off) v += x;
   }
-  const int64_t r = buf[t];
+  if (lane == 63) wsum[wave] = v;
   __syncthreads();
+  if (wave == 0) {
+    int64_t w = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int64_t x = __shfl_up(w, off, 64);
+      if (lane >= off) w += x;
+    }
+    if (lane < 16) wsum[16 + lane] = w;
+  }
+  __syncthreads();
+  const int64_t r = v + (wave > 0 ? wsum[16 + wave - 1] : 0);
+  *total = wsum[31];
+  __syncthreads();   // wsum is reused by the next scan
   return r;
 }
 
 // One workgroup builds the work list:
 //   1. each thread counts the segments of a contiguous range of sequences; a
-//      scan gives every sequence its first segment (seq_seg0);
+//      scan gives every sequence its first segment (seq_seg0, kept in LDS
+//      when the batch has at most PF_PREP_LDS_SEQS sequences);
 //   2. each thread takes a contiguous range of segments, writes their
 //      descriptors {sequence, KV head, query tile, key tiles} and sums the
 //      tiles; a scan gives the tile prefix sums seg_cu;
-//   3. each workgroup of the attention kernel gets its first (segment, tile)
-//      by binary search over seg_cu.
+//   3. each thread gives every workgroup whose first unit falls in one of its
+//      segments that (segment, tile): workgroup w starts at unit
+//      floor(w U / W), which lies in the segment of tiles [c, c + n) exactly
+//      when ceil(c W / U) <= w < ceil((c + n) W / U).
 // A batch whose offsets disagree with total_q and max_q_len (an offset
 // outside [0, total_q], a decreasing offset or a chunk longer than max_q_len),
 // which could need more segments than the workspace was sized for or reach
 // rows outside q and out, or one with 2^31 key tiles or more, is given no
 // work: {0, 0} in the header.
+constexpr int PF_PREP_LDS_SEQS = 4095;
 __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int num_seqs, int total_q,
                                                             int max_q_len, int QB,
                                                             int num_wgs, int32_t* __restrict__ hdr,
-                                                            int32_t* __restrict__ seq_seg0,
+                                                            int32_t* __restrict__ seq_seg0_g,
                                                             int32_t* __restrict__ seg_cu,
                                                             int4* __restrict__ seg_desc,
                                                             int32_t* __restrict__ wg_start) {
-  __shared__ int64_t buf[1024];
-  __shared__ int32_t ok;
+  __shared__ int64_t wsum[32];
+  __shared__ int32_t seq_seg0_l[PF_PREP_LDS_SEQS + 1];
   const int t = threadIdx.x;
+  const bool in_lds = num_seqs <= PF_PREP_LDS_SEQS;
+  int32_t* seq_seg0 = in_lds ? seq_seg0_l : seq_seg0_g;
   auto qtiles = [&](int s) {
     const int L = max(0, a.cu_q[s + 1] - a.cu_q[s]);
     return (int)(((int64_t)L + QB - 1) / QB);
@@ -183,8 +201,9 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
     cs += (int64_t)a.n_kv * qtiles(s);
   }
   bad = __syncthreads_or(bad);
-  const int64_t cs_end = block_scan_1024(cs, buf);
-  const int64_t nseg_all = bad ? a.nseg_max + (int64_t)1 : buf[1023];
+  int64_t nseg_all;
+  const int64_t cs_end = block_scan_1024(cs, wsum, &nseg_all);
+  if (bad) nseg_all = a.nseg_max + (int64_t)1;
   if (nseg_all <= a.nseg_max) {
     int64_t g = cs_end - cs;
     for (int s = s0; s < s1; ++s) {
@@ -218,35 +237,32 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
       ct += n;
     }
   }
-  const int64_t ct_end = block_scan_1024(ct, buf);
-  if (t == 0) ok = buf[1023] < ((int64_t)1 << 31);
-  __syncthreads();
-  const int64_t U = ok ? buf[1023] : 0;
+  int64_t U_all;
+  const int64_t ct_end = block_scan_1024(ct, wsum, &U_all);
+  const bool ok = U_all < ((int64_t)1 << 31);
+  const int64_t U = ok ? U_all : 0;
+  const int nseg_used = ok ? nseg : 0;
+  // 3. the thread's segments: their prefix sums and the workgroups starting in them
   if (ok) {
-    int run = (int)(ct_end - ct);
+    int64_t c = ct_end - ct;
     for (int g = g0; g < g1; ++g) {
-      seg_cu[g] = run;
-      run += seg_desc[g].w;
+      seg_cu[g] = (int)c;
+      const int n = seg_desc[g].w;
+      if (n > 0) {
+        const int64_t wlo = (c * num_wgs + U - 1) / U;
+        const int64_t whi = min((int64_t)num_wgs, ((c + n) * num_wgs + U - 1) / U);
+        for (int64_t w = wlo; w < whi; ++w) {
+          wg_start[2 * w] = g;
+          wg_start[2 * w + 1] = (int)(w * U / num_wgs - c);
+        }
+      }
+      c += n;
     }
   }
-  const int nseg_used = ok ? nseg : 0;
   if (t == 0) {
     seg_cu[nseg_used] = (int)U;
     hdr[0] = nseg_used;
     hdr[1] = (int)U;
-  }
-  __threadfence_block();
-  __syncthreads();
-  // 3. each workgroup's first (segment, tile)
-  for (int w = t; w < num_wgs; w += 1024) {
-    const int64_t x = pf_begin(w, U, num_wgs);
-    int lo = 0, hi = nseg_used;              // last g with seg_cu[g] <= x
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (seg_cu[mid] <= x) lo = mid; else hi = mid;
-    }
-    wg_start[2 * w] = lo;
-    wg_start[2 * w + 1] = (int)(x - (nseg_used > 0 ? seg_cu[lo] : 0));
   }
 }
 

@@ -214,3 +214,32 @@ def test_prefill_plan_covers_every_row_once(seed):
         if sum(tiles):
             for W in (1, 3, 64, 1000):
                 replay_prefill(tiles, W)
+
+
+def test_prefill_planner_workgroup_starts():
+    """The planner gives workgroup w the (segment, tile) holding unit floor(w U / W)
+    by letting each segment [c, c + n) claim w in [ceil(c W / U), ceil((c + n) W / U)):
+    every workgroup is claimed exactly once, by the segment the split expects."""
+    rng = random.Random(300)
+    for _ in range(500):
+        tiles = [rng.choice([0, 0, 1, 2, 7, rng.randint(1, 60)]) for _ in range(rng.randint(1, 30))]
+        U = sum(tiles)
+        if U == 0:
+            continue
+        for W in (1, 2, 3, 7, 64, 768, 1024):
+            claims = {}
+            c = 0
+            for g, n in enumerate(tiles):
+                if n > 0:
+                    for w in range((c * W + U - 1) // U, min(W, ((c + n) * W + U - 1) // U)):
+                        assert w not in claims
+                        claims[w] = (g, w * U // W - c)
+                c += n
+            assert sorted(claims) == list(range(W))
+            cu = [0]
+            for n in tiles:
+                cu.append(cu[-1] + n)
+            for w, (g, tile) in claims.items():
+                x = begin(w, U, W)
+                assert g == next(i for i in range(len(tiles)) if cu[i + 1] > x)
+                assert tile == x - cu[g]
