@@ -212,3 +212,46 @@ def test_int4_mixed_step_one_launch(dev):
                                        n_decode=24, dlo=1, dhi=400, seed=11, kv="int4")
     workloads.draw_values(w, "cpu")
     _prefill_int4_vs_oracle(w, dev, "int4 mixed one launch", one_launch=True)
+
+
+def test_int4_blocks_move_with_their_scales(dev):
+    """Swap one sequence's INT4 blocks out to pinned host memory and back into other
+    block ids: its codes go through pa_copy_blocks as byte pools, its value scales
+    as a float32 pool of one element per (head, offset).  The decode after the move
+    is bit-identical (the output does not depend on where the blocks live)."""
+    import paged_kv_cache_74_amd as pa
+    from gpu_harness import DeviceWorkload, to_f64
+    w = _int4(workloads.small(4, seed=3))
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    ref = to_f64(dw.decode())
+    s = int(np.argmax(w.context_lens))
+    n = -(-int(w.context_lens[s]) // w.block_size)
+    old = w.block_tables[s, :n].astype(np.int64)
+    nb = w.num_blocks
+    new = np.arange(nb, nb + n, dtype=np.int64)          # ids past the old pool
+    grow = lambda t: torch.cat([t, torch.zeros((n,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                                device=t.device)])
+    kc, vc, sc = grow(dw.k_cache), grow(dw.v_cache), grow(dw.v_scales)
+    host = [torch.empty((n,) + tuple(t.shape[1:]), dtype=t.dtype, pin_memory=True)
+            for t in (kc, sc)]
+    host_v = torch.empty_like(host[0], pin_memory=True)
+    sview = lambda t: t.view(t.shape[0], 1, t.shape[1], t.shape[2])   # scales as a pool
+    out_pairs = torch.as_tensor(np.stack([old, np.arange(n)], 1), device=dev)
+    in_pairs = torch.as_tensor(np.stack([np.arange(n), new], 1), device=dev)
+    pa.pa_copy_blocks(host[0], host_v, kc, vc, out_pairs)                 # swap out
+    pa.pa_copy_blocks(sview(host[1]), sview(host[1]), sview(sc), sview(sc), out_pairs)
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(old, device=dev)
+    kc[idx] = 0x77
+    vc[idx] = 0x77
+    sc[idx] = float("nan")                                                # the old blocks are reused
+    pa.pa_copy_blocks(kc, vc, host[0], host_v, in_pairs)                  # swap in elsewhere
+    pa.pa_copy_blocks(sview(sc), sview(sc), sview(host[1]), sview(host[1]), in_pairs)
+    tables = dw.tables.clone()
+    tables[s, :n] = torch.as_tensor(new, device=dev, dtype=torch.int32)
+    q, _, ctx = dw.decode_inputs()
+    got = pa.pa_decode_int4(q, kc, vc, sc, dw.k_channel_scales, tables, ctx,
+                            int(w.context_lens.max()), w.scale)
+    assert np.array_equal(to_f64(got)[s], ref[s])
