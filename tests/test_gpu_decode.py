@@ -267,3 +267,29 @@ def test_decode_workspace_reuse(dev):
     pk, pv = oracle_pools(w)
     check_close(to_f64(r3), oracle_decode(w, pk, pv), w.q_dtype,
                 "split 48 after split 16 on one workspace")
+
+
+# (n_q, n_kv, head_dim, block_size) for the 8-bit caches: every group size, both
+# head dims, block sizes that take the matrix-core kernel (>= 16) and one that
+# takes the vector kernel
+SHAPES_8BIT = [(8, 8, 128, 16), (8, 4, 64, 32), (16, 4, 128, 16), (32, 4, 64, 64),
+               (16, 2, 128, 8)]
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+@pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES_8BIT)
+def test_decode_8bit_shapes(dev, kv, nq, nkv, hd, bs):
+    from gpu_harness import DeviceWorkload, to_f64
+    rng = np.random.default_rng(nq * 7 + hd + bs)
+    ctx = rng.integers(1, 900, 9).astype(np.int32)
+    ctx[0] = 1
+    w = workloads._decode_workload("8bit-shapes", rng, ctx, nq, nkv, hd, bs, kv, "bf16", "bf16",
+                                   seed=4)
+    workloads.draw_values(w, "cpu")
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    for split in (0, 48):
+        got = to_f64(dw.decode(split_tokens=split))
+        pk, pv = oracle_pools(w)
+        check_close(got, oracle_decode(w, pk, pv), "bf16", f"{kv} {nq}/{nkv}/{hd}/bs{bs} split {split}")

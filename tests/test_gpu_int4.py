@@ -92,7 +92,8 @@ def test_int4_decode_split_sizes(dev, split):
 
 
 # (n_q, n_kv, head_dim, block_size): every group size, both head dims, small and large blocks
-SHAPES = [(8, 8, 128, 16), (8, 4, 64, 16), (16, 4, 128, 32), (16, 2, 64, 1), (32, 4, 128, 4)]
+SHAPES = [(8, 8, 128, 16), (8, 4, 64, 16), (16, 4, 128, 32), (16, 2, 64, 1), (32, 4, 128, 4),
+          (32, 4, 128, 16), (16, 2, 64, 64)]
 
 
 @pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES)
