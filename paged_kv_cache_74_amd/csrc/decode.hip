@@ -707,6 +707,16 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
 // chunked-prefill kernel.  This takes the two products off the vector ALU,
 // which otherwise bounds the 8- and 4-bit caches (their codes must be widened
 // to bf16 either way).
+// Loads come in one of two forms:
+//   * per head: each wave loads its own head's rows, 64 contiguous bytes per
+//     token (16 tokens per instruction, one token stride apart);
+//   * staged (STAGED): the workgroup's waves load the step's rows of all its
+//     heads together, each instruction covering 1 KiB of whole token rows in
+//     order, write them to a double-buffered LDS stage (16-byte chunks XOR-
+//     swizzled by token, so neither the writes nor the per-head reads conflict)
+//     and each wave reads its head's pieces back from there.  One barrier per
+//     step; a step is written to the stage one step before it is read.  Long
+//     runs of whole rows stream from HBM faster than per-head pieces.
 // ---------------------------------------------------------------------------
 typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short mf_s4_t __attribute__((ext_vector_type(4)));
@@ -730,7 +740,26 @@ struct MfLayout {
   static constexpr int NB = HD / 16;             // PV MFMAs (16x16x16) per step
   static constexpr int VROW = HD * 2 + 32;       // LDS bytes per token row of V (bf16, padded)
   static constexpr int WAVE_LDS = 16 * VROW;
+  // staged loads: 16-byte chunks per lane per step, and the bytes of one
+  // tensor's stage (16 tokens of up to DECODE_MAX_HW heads)
+  static constexpr int LIN = ROW / 64;
+  static constexpr int STAGE = 16 * DECODE_MAX_HW * ROW;
 };
+
+// The staged form applies to 8-bit codes when a lane's piece is 16 bytes and
+// a head group's token row is a whole number of 16-chunk (256-byte) swizzle
+// groups.  On the long-tail step it took int8 from 364 to 327 us and fp8 from
+// 356 (vector kernel) to 326 us.  int4 keeps per-head loads: its steps carry
+// the most vector work per byte (the nibble widening), and a barrier per step
+// that keeps the 8 waves in the same phase cost more than the longer runs
+// gained (285 against 251 us).
+template <int CDT, int HD>
+__host__ __device__ constexpr bool mf_stageable_layout() {
+  return MfLayout<CDT, HD>::EBITS == 8 && MfLayout<CDT, HD>::PS == 16 && MfLayout<CDT, HD>::LIN >= 1;
+}
+__host__ __device__ inline bool mf_staged_ok(int row_bytes, int hw) {
+  return row_bytes >= 64 && (hw * row_bytes) % 256 == 0;
+}
 
 #ifndef DECODE_MF_AUX
 #define DECODE_MF_AUX DECODE_LOAD_AUX
@@ -764,6 +793,7 @@ struct MfFrag {
   uint32_t k[ML::KW];
   uint32_t v[ML::KW];
   float vs[4];   // INT4: value scales of tokens 4j .. 4j+3
+  int nb;        // staged form: block id of the step NBUF steps later
 };
 
 // The loads of one step: tokens [base, base + 16) of the sequence, all in one
@@ -784,10 +814,7 @@ __device__ __forceinline__ void mf_load_step(MfFrag<ML>& f, const DecodeArgs& a,
     const float4 x = *(const float4*)(a.v_tok_scale +
                                       ((int64_t)blk * a.n_kv + kvh) * a.block_size +
                                       (base & (a.block_size - 1)) + 4 * j);
-    f.vs[0] = 4 * j + 0 < n ? x.x : 0.0f;
-    f.vs[1] = 4 * j + 1 < n ? x.y : 0.0f;
-    f.vs[2] = 4 * j + 2 < n ? x.z : 0.0f;
-    f.vs[3] = 4 * j + 3 < n ? x.w : 0.0f;
+    f.vs[0] = x.x; f.vs[1] = x.y; f.vs[2] = x.z; f.vs[3] = x.w;   // masked where used
   }
 }
 
@@ -825,9 +852,49 @@ __device__ __forceinline__ int mf_dim_of_col(int c) {
   }
 }
 
-template <int CDT, int HD, int G, int NBUF>
+// Staged loads: the lane's linear chunks of a step (global offsets from the
+// head group's row start of the step's first token), where they go in the
+// stage, and where the lane's own pieces are read back.
+template <class ML>
+struct MfStageMap {
+  uint32_t goff[ML::LIN];
+  uint32_t wpos[ML::LIN];
+  uint32_t rpos[ML::NP];
+};
+
+template <class ML>
+__device__ __forceinline__ MfStageMap<ML> mf_stage_map(const DecodeArgs& a, int wv, int lane) {
+  MfStageMap<ML> m;
+  const int rc_log2 = __builtin_ctz((unsigned)(a.hw * ML::ROW / 16));   // chunks per token row
+  const int rc = 1 << rc_log2;
+  const int j = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int k = 0; k < ML::LIN; ++k) {
+    const int q = (k * a.hw + wv) * 64 + lane;   // chunk of the step, in memory order
+    const int t = q >> rc_log2, c = q & (rc - 1);
+    m.goff[k] = (uint32_t)(t * (int)a.tok_stride + 16 * c);
+    m.wpos[k] = (uint32_t)(16 * (t * rc + (c ^ t)));
+  }
+#pragma unroll
+  for (int k = 0; k < ML::NP; ++k) {
+    const int c = wv * (ML::ROW / 16) + j + 4 * k;   // piece k of lane group j, head wv
+    m.rpos[k] = (uint32_t)(16 * (r * rc + (c ^ r)));
+  }
+  return m;
+}
+
+// LDS-only barrier: the stage's writes are visible to the workgroup after it,
+// and global loads in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int CDT, int HD, int G, int NBUF, bool STAGED>
 __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kvh, int st0,
-                                              int st1, int64_t slot, uint8_t* vl) {
+                                              int st1, int64_t slot, uint8_t* vl, int wv,
+                                              uint8_t* stage) {
   using ML = MfLayout<CDT, HD>;
   constexpr int DW8 = mf_dw8<CDT>();
   const int lane = threadIdx.x & 63;
@@ -895,18 +962,18 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
   };
 
-  auto step = [&](const MfFrag<ML>& f, int base) {
+  auto step = [&](const uint32_t* fk, const uint32_t* fv, const float* fvs, int base) {
     // S^T: tokens 4j .. 4j+3 of head column r
     mf_f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < ML::NT; ++t)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_k8<CDT>(f.k + DW8 * t), qb[t], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_k8<CDT>(fk + DW8 * t), qb[t], sc, 0, 0, 0);
     // V rows (bf16) into this wave's LDS slice: token r, this lane's dims
     {
       uint8_t* row = vl + r * ML::VROW;
 #pragma unroll
       for (int t = 0; t < ML::NT; ++t) {
-        const mf_bf16x8_t v8 = mf_k8<CDT>(f.v + DW8 * t);
+        const mf_bf16x8_t v8 = mf_k8<CDT>(fv + DW8 * t);
         *(uint4*)(row + 2 * mf_dim0<ML>(t, j)) = __builtin_bit_cast(uint4, v8);
       }
     }
@@ -936,8 +1003,11 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     uint32_t P0, P1;
     if constexpr (CDT == PA_INT4) {     // value scale of each token into its weight
       lp += (p[0] + p[1]) + (p[2] + p[3]);
-      P0 = pack_bf16(p[0] * f.vs[0], p[1] * f.vs[1]);
-      P1 = pack_bf16(p[2] * f.vs[2], p[3] * f.vs[3]);
+      float sv[4];                      // scales of tokens past the end read as 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = (4 * j + i < nvalid) ? fvs[i] : 0.0f;
+      P0 = pack_bf16(p[0] * sv[0], p[1] * sv[1]);
+      P1 = pack_bf16(p[2] * sv[2], p[3] * sv[3]);
     } else {                            // l from the rounded weights
       P0 = pack_bf16(p[0], p[1]);
       P1 = pack_bf16(p[2], p[3]);
@@ -959,24 +1029,116 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
   // last step through an empty descriptor)
   const int nsteps = (end - begin + 15) >> 4;
   MfFrag<ML> buf[NBUF];
-  auto prefetch = [&](MfFrag<ML>& f, int pf) {
-    const int base = begin + 16 * min(pf, nsteps - 1);
-    mf_load_step<CDT, ML>(f, a, block_at(base), base, end, lane_off, pf < nsteps, kvh, j);
-  };
+  if constexpr (!STAGED) {
+    auto prefetch = [&](MfFrag<ML>& f, int pf) {
+      const int base = begin + 16 * min(pf, nsteps - 1);
+      mf_load_step<CDT, ML>(f, a, block_at(base), base, end, lane_off, pf < nsteps, kvh, j);
+    };
 #pragma unroll
-  for (int d = 0; d < NBUF - 1; ++d) prefetch(buf[d], d);
-  int i = 0;
-  for (; i + NBUF <= nsteps; i += NBUF) {
+    for (int d = 0; d < NBUF - 1; ++d) prefetch(buf[d], d);
+    int i = 0;
+    for (; i + NBUF <= nsteps; i += NBUF) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
-      step(buf[u], begin + 16 * (i + u));
+      for (int u = 0; u < NBUF; ++u) {
+        prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
+        step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u));
+      }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) {
-    prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
-    if (i + u < nsteps) step(buf[u], begin + 16 * (i + u));
+    for (int u = 0; u < NBUF - 1; ++u) {
+      prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
+      if (i + u < nsteps) step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u));
+    }
+  } else {
+    // Step x is loaded into buf[x % NBUF], written to stage x & 1 while step
+    // x - 1 is computed, and read back after that step's barrier.  Its block
+    // id was loaded with step x - NBUF and travels in the same buffer; its
+    // value scales (INT4, this wave's head) go to the stage with it.  No
+    // loaded value outlives its buffer, so each wait covers exactly the step
+    // being staged.
+    const MfStageMap<ML> sm = mf_stage_map<ML>(a, wv, lane);
+    float* vsl = (float*)(stage + 4 * ML::STAGE) + wv * 16 + 4 * j;   // + parity * 16 * DECODE_MAX_HW
+    const int64_t hg_off = (int64_t)(kvh - wv) * ML::ROW;   // the head group's first row byte
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(table, (jlast + 1) * 4);
+    auto table_at = [&](int pf) -> int {   // vector load, the same entry in every lane
+      const int jb = (begin + 16 * min(pf, nsteps - 1)) >> a.bs_log2;
+      return (int)__builtin_amdgcn_raw_buffer_load_b32(tr, (uint32_t)(4 * jb), 0, 0);
+    };
+    auto prefetch = [&](MfFrag<ML>& f, int pf, int blk) {
+      const int base = begin + 16 * min(pf, nsteps - 1);
+      blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+      const int64_t tok0 = (int64_t)blk * a.block_size + (base & (a.block_size - 1));
+      const int n = pf < nsteps ? min(16, end - base) : 0;
+      const int32_t bytes = n * (int32_t)a.tok_stride;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k_cache + tok0 * a.tok_stride + hg_off, bytes);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v_cache + tok0 * a.tok_stride + hg_off, bytes);
+#pragma unroll
+      for (int k = 0; k < ML::LIN; ++k) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, sm.goff[k], 0, DECODE_MF_AUX);
+        f.k[4 * k + 0] = x.x; f.k[4 * k + 1] = x.y; f.k[4 * k + 2] = x.z; f.k[4 * k + 3] = x.w;
+        const u32x4_t y = __builtin_amdgcn_raw_buffer_load_b128(vr, sm.goff[k], 0, DECODE_MF_AUX);
+        f.v[4 * k + 0] = y.x; f.v[4 * k + 1] = y.y; f.v[4 * k + 2] = y.z; f.v[4 * k + 3] = y.w;
+      }
+      if constexpr (CDT == PA_INT4) {   // this head's tokens 4j .. 4j+3 (masked where used)
+        const float4 x = *(const float4*)(a.v_tok_scale +
+                                          ((int64_t)blk * a.n_kv + kvh) * a.block_size +
+                                          (base & (a.block_size - 1)) + 4 * j);
+        f.vs[0] = x.x; f.vs[1] = x.y; f.vs[2] = x.z; f.vs[3] = x.w;
+      }
+      f.nb = table_at(pf + NBUF);
+    };
+    auto put = [&](const MfFrag<ML>& f, int x) {
+      uint8_t* sk = stage + (x & 1) * 2 * ML::STAGE;
+#pragma unroll
+      for (int k = 0; k < ML::LIN; ++k) {
+        *(uint4*)(sk + sm.wpos[k]) = make_uint4(f.k[4 * k], f.k[4 * k + 1], f.k[4 * k + 2], f.k[4 * k + 3]);
+        *(uint4*)(sk + ML::STAGE + sm.wpos[k]) =
+            make_uint4(f.v[4 * k], f.v[4 * k + 1], f.v[4 * k + 2], f.v[4 * k + 3]);
+      }
+      if constexpr (CDT == PA_INT4) {
+        if (r == 0)
+          *(float4*)(vsl + (x & 1) * 16 * DECODE_MAX_HW) = make_float4(f.vs[0], f.vs[1], f.vs[2], f.vs[3]);
+      }
+    };
+    auto run = [&](int x) {
+      const uint8_t* sk = stage + (x & 1) * 2 * ML::STAGE;
+      uint32_t kc[ML::KW], vc[ML::KW];
+#pragma unroll
+      for (int k = 0; k < ML::NP; ++k) {
+        const uint4 p = *(const uint4*)(sk + sm.rpos[k]);
+        const uint4 q = *(const uint4*)(sk + ML::STAGE + sm.rpos[k]);
+        kc[4 * k] = p.x; kc[4 * k + 1] = p.y; kc[4 * k + 2] = p.z; kc[4 * k + 3] = p.w;
+        vc[4 * k] = q.x; vc[4 * k + 1] = q.y; vc[4 * k + 2] = q.z; vc[4 * k + 3] = q.w;
+      }
+      float vs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (CDT == PA_INT4) {
+        const float4 t = *(const float4*)(vsl + (x & 1) * 16 * DECODE_MAX_HW);
+        vs[0] = t.x; vs[1] = t.y; vs[2] = t.z; vs[3] = t.w;
+      }
+      step(kc, vc, vs, begin + 16 * x);
+    };
+#pragma unroll
+    for (int d = 0; d < NBUF; ++d) prefetch(buf[d], d, __builtin_amdgcn_readfirstlane(table_at(d)));
+    put(buf[0], 0);
+    lds_barrier();
+    int i = 0;
+    for (; i + NBUF <= nsteps; i += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        put(buf[(u + 1) % NBUF], i + u + 1);
+        prefetch(buf[u], i + u + NBUF, __builtin_amdgcn_readfirstlane(buf[u].nb));
+        run(i + u);
+        lds_barrier();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) {
+      if (i + u < nsteps) {
+        if (i + u + 1 < nsteps) put(buf[(u + 1) % NBUF], i + u + 1);
+        run(i + u);
+        lds_barrier();
+      }
+    }
   }
 
   // the piece's partial: l of column r summed over its four lanes; O rows 4j+i
@@ -1001,10 +1163,13 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 #ifndef DECODE_MF_MIN_WGS
 #define DECODE_MF_MIN_WGS 1   // workgroups per CU the register budget must allow
 #endif
-template <int CDT, int HD, int G, int NBUF>
+template <int CDT, int HD, int G, int NBUF, bool STAGED>
 __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_mfma_kernel(DecodeArgs a) {
   using ML = MfLayout<CDT, HD>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[DECODE_MAX_HW * ML::WAVE_LDS];
+  // per-wave V slices, then (staged) two stages of K and V and the INT4 value
+  // scales of each stage's 16 tokens per head
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DECODE_MAX_HW * ML::WAVE_LDS +
+                                                      (STAGED ? 4 * ML::STAGE + 2 * DECODE_MAX_HW * 64 : 0)];
   const int w = blockIdx.x;
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
@@ -1025,7 +1190,8 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
     const int steps = steps_of(uniform_load(a.context_lens, s));
     const int run_end = (int)min((int64_t)steps, step + (u1 - u));
     const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
-    decode_run_mf<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv, vl);
+    decode_run_mf<CDT, HD, G, NBUF, STAGED>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv,
+                                            vl, wv, lds + DECODE_MAX_HW * ML::WAVE_LDS);
     u += run_end - step;
     if (u >= u1) break;
     step = 0;
@@ -1210,11 +1376,12 @@ static int64_t resident_wgs(int hw) {
 }
 
 // Cache dtypes whose decode runs on the matrix cores (bit = dtype code) when
-// block_size >= 16: int4 and int8, whose codes cost the most vector-ALU work to
-// widen (on the long-tail step, int4 364 -> 259 us, int8 399 -> 361 us).  fp8
-// runs as fast on either path and bf16 is bound by HBM on the vector path.
+// block_size >= 16: int4, int8 and fp8.  Their codes cost vector-ALU work to
+// widen, which the matrix cores take the products off (on the long-tail step,
+// int4 364 -> 251 us, int8 399 -> 327 us with staged loads, fp8 356 -> 326 us
+// with staged loads).  bf16 is bound by HBM on the vector path.
 #ifndef DECODE_MFMA_MASK
-#define DECODE_MFMA_MASK ((1 << PA_INT8) | (1 << PA_INT4))
+#define DECODE_MFMA_MASK ((1 << PA_FP8_E4M3) | (1 << PA_INT8) | (1 << PA_INT4))
 #endif
 // steps in flight per wave on the matrix-core path (fewer bytes per step for
 // narrower codes, so more steps)
@@ -1224,17 +1391,22 @@ static int64_t resident_wgs(int hw) {
 #ifndef DECODE_MF_NBUF8
 #define DECODE_MF_NBUF8 3   // FP8 / INT8
 #endif
+// staged loads on the matrix-core path where the layout allows (1), or per-head
+// loads everywhere (0)
+#ifndef DECODE_MF_STAGED
+#define DECODE_MF_STAGED 1
+#endif
 __host__ __device__ constexpr int mf_nbuf(int CDT) {
   return CDT == PA_INT4 ? DECODE_MF_NBUF4 : CDT == PA_BF16 ? 2 : DECODE_MF_NBUF8;
 }
 
-template <int CDT, int HD, int G>
+template <int CDT, int HD, int G, bool STAGED>
 static int64_t resident_wgs_mf(int hw) {
   static int64_t cached[DECODE_MAX_HW + 1] = {};
   if (!cached[hw]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT)>, 64 * hw, 0) != hipSuccess ||
+            &per_cu, decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>, 64 * hw, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     const int target = (DECODE_WAVES_PER_CU + hw - 1) / hw;
@@ -1244,28 +1416,39 @@ static int64_t resident_wgs_mf(int hw) {
   return cached[hw];
 }
 
+template <int CDT, int HD, int G, bool STAGED>
+static void launch_mf(const DecodeArgs& a, int split_tokens, int64_t bound, hipStream_t st) {
+  DecodeArgs b = a;
+  int64_t W = split_tokens <= 0 ? resident_wgs_mf<CDT, HD, G, STAGED>(a.hw) : bound;
+  if (W > bound) W = bound;
+  b.num_wgs = (int)W;
+  hipLaunchKernelGGL((decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>), dim3((unsigned)W),
+                     dim3(64 * a.hw), 0, st, b);
+}
+
 template <int CDT, int HD, int G>
 static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
   constexpr bool MF = (DECODE_MFMA_MASK >> CDT) & 1;
   const int hw = heads_per_wg(CDT, a.n_kv, G);
   const bool mf = MF && a.block_size >= 16;
   const int64_t bound = wgs_bound(hw, a.num_seqs, a.n_kv, max_context_len, split_tokens);
-  int64_t W = bound;
-  if (split_tokens <= 0) {
-    if constexpr (MF) W = mf ? resident_wgs_mf<CDT, HD, G>(hw) : resident_wgs<CDT, HD, G>(hw);
-    else W = resident_wgs<CDT, HD, G>(hw);
-  }
-  if (W > bound) W = bound;
-  a.num_wgs = (int)W;
   a.hw = hw;
   a.nhg = a.n_kv / hw;
   if constexpr (MF) {
     if (mf) {
-      hipLaunchKernelGGL((decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT)>), dim3((unsigned)W),
-                         dim3(64 * hw), 0, st, a);
+      if constexpr (mf_stageable_layout<CDT, HD>() && DECODE_MF_STAGED) {
+        if (mf_staged_ok(MfLayout<CDT, HD>::ROW, hw)) {
+          launch_mf<CDT, HD, G, true>(a, split_tokens, bound, st);
+          return;
+        }
+      }
+      launch_mf<CDT, HD, G, false>(a, split_tokens, bound, st);
       return;
     }
   }
+  int64_t W = split_tokens <= 0 ? resident_wgs<CDT, HD, G>(hw) : bound;
+  if (W > bound) W = bound;
+  a.num_wgs = (int)W;
   hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W),
                      dim3(64 * hw), 0, st, a);
 }

@@ -243,3 +243,48 @@ def test_prefill_planner_workgroup_starts():
                 x = begin(w, U, W)
                 assert g == next(i for i in range(len(tiles)) if cu[i + 1] > x)
                 assert tile == x - cu[g]
+
+
+def stage_maps(hw, row):
+    """The staged decode load maps for one head group: per (wave, lane, k) the
+    (token, 16-byte chunk) a lane loads and the stage slot it writes, and per
+    (wave, lane, piece) the slot it reads back."""
+    rc = hw * row // 16                      # chunks per token row of the group
+    loads = {}
+    for wv in range(hw):
+        for lane in range(64):
+            for k in range(row // 64):
+                q = (k * hw + wv) * 64 + lane
+                t, c = q // rc, q % rc
+                loads[(wv, lane, k)] = ((t, c), t * rc + (c ^ t))
+    reads = {}
+    for wv in range(hw):
+        for lane in range(64):
+            j, r = lane >> 4, lane & 15
+            for k in range(row // 64):
+                c = wv * (row // 16) + j + 4 * k
+                reads[(wv, lane, k)] = ((r, c), r * rc + (c ^ r))
+    return rc, loads, reads
+
+
+@pytest.mark.parametrize("hw,row", [(8, 64), (4, 64), (8, 128), (4, 128), (2, 128), (8, 256),
+                                    (1, 256), (4, 256)])
+def test_decode_stage_maps(hw, row):
+    """Every chunk of a step is loaded once, lands in a distinct stage slot, and
+    each lane reads back the piece of its own head that the per-head layout
+    gives it (token r, chunk j + 4k of head wv's row); neither the writes nor
+    the reads of 16 consecutive lanes share a 16-byte bank group."""
+    rc, loads, reads = stage_maps(hw, row)
+    assert (hw * row) % 256 == 0 and row >= 64          # where the kernel stages
+    chunks = [tc for tc, _ in loads.values()]
+    assert sorted(chunks) == [(t, c) for t in range(16) for c in range(rc)]
+    slots = {pos: tc for tc, pos in loads.values()}
+    assert len(slots) == 16 * rc and max(slots) < 16 * rc
+    for key, (tc, pos) in reads.items():
+        assert slots[pos] == tc, key
+    for table in (loads, reads):
+        for wv in range(hw):
+            for k in range(row // 64):
+                for g in range(4):
+                    banks = [table[(wv, lane, k)][1] % 16 for lane in range(16 * g, 16 * g + 16)]
+                    assert len(set(banks)) == 16, (wv, k, g)

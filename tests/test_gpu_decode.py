@@ -271,9 +271,10 @@ def test_decode_workspace_reuse(dev):
 
 # (n_q, n_kv, head_dim, block_size) for the 8-bit caches: every group size, both
 # head dims, block sizes that take the matrix-core kernel (>= 16) and one that
-# takes the vector kernel
+# takes the vector kernel; int8 on 8 x 2 x 64 loads per head, the other int8
+# matrix-core shapes stage their loads through LDS
 SHAPES_8BIT = [(8, 8, 128, 16), (8, 4, 64, 32), (16, 4, 128, 16), (32, 4, 64, 64),
-               (16, 2, 128, 8)]
+               (16, 2, 128, 8), (8, 2, 64, 16)]
 
 
 @pytest.mark.parametrize("kv", ["int8", "fp8"])

@@ -92,8 +92,11 @@ def test_int4_decode_split_sizes(dev, split):
 
 
 # (n_q, n_kv, head_dim, block_size): every group size, both head dims, small and large blocks
+# (the matrix-core kernel stages loads through LDS when a head group's token row
+# is a multiple of 256 bytes: 8 x 8 x 128, 16 x 4 x 128 and 32 x 4 x 128 do,
+# 16 x 2 x 128 and the 64-dim shapes load per head)
 SHAPES = [(8, 8, 128, 16), (8, 4, 64, 16), (16, 4, 128, 32), (16, 2, 64, 1), (32, 4, 128, 4),
-          (32, 4, 128, 16), (16, 2, 64, 64)]
+          (32, 4, 128, 16), (16, 2, 64, 64), (16, 2, 128, 16)]
 
 
 @pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES)
