@@ -94,6 +94,13 @@ def source_hash(sources) -> str:
     return h.hexdigest()
 
 
+def decode_kernel(w) -> str:
+    """The split kernel pa_decode_partials launches for this workload's cache."""
+    if w.block_size >= 16 and w.cache_dtype in ("bf16", "fp8", "int8", "int4"):
+        return "decode_mfma_kernel"
+    return "decode_split_kernel"
+
+
 def measured_traffic(workload: str, kernel: str, sources):
     """HBM bytes per launch of `kernel` from the committed counter record, or
     None when there is no record for this workload or the kernel sources changed."""
@@ -471,13 +478,13 @@ def main():
         "bytes_per_step": {"algorithmic_unique": bm["step"], "kv_unique": bm["kv_unique"],
                            "kv_logical": bm["kv_logical"]},
         "roofline": prefill_rec if one else {
-            "kernel": "decode_split_kernel (pa_decode_partials)",
+            "kernel": f"{decode_kernel(w)} (pa_decode_partials)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, "decode_split_kernel", DECODE_SOURCES),
+            "traffic": measured_traffic(args.workload, decode_kernel(w), DECODE_SOURCES),
             "avg_launch_us": round(split_avg * 1e3, 2),
             "algorithmic_bytes_per_launch": bm["split_kernel"],
         },

@@ -14,7 +14,13 @@
 //   * split partials (m, l, O) combined by the same recurrence applied to whole
 //     splits (the log-sum-exp merge).
 //
-// How it maps to CDNA4 (gfx950, wave64):
+// Two split kernels share the work split, the partial format and the merge:
+//   * decode_mfma_kernel (further below): both products on the matrix cores;
+//     taken for bf16, fp8, int8 and int4 caches with blocks of >= 16 tokens;
+//   * decode_split_kernel (this part): the products on the vector ALU; taken
+//     for fp32 caches and for blocks of fewer than 16 tokens.
+//
+// How the vector kernel maps to CDNA4 (gfx950, wave64):
 //   * One wave = one (sequence, KV head, split).  It owns all group_size query
 //     heads of that KV head, so every K/V byte is fetched from HBM exactly once.
 //     The waves of a workgroup take consecutive KV heads of the same sequence
@@ -746,16 +752,17 @@ struct MfLayout {
   static constexpr int STAGE = 16 * DECODE_MAX_HW * ROW;
 };
 
-// The staged form applies to 8-bit codes when a lane's piece is 16 bytes and
-// a head group's token row is a whole number of 16-chunk (256-byte) swizzle
-// groups.  On the long-tail step it took int8 from 364 to 327 us and fp8 from
-// 356 (vector kernel) to 326 us.  int4 keeps per-head loads: its steps carry
-// the most vector work per byte (the nibble widening), and a barrier per step
-// that keeps the 8 waves in the same phase cost more than the longer runs
-// gained (285 against 251 us).
+// The staged form applies to 16- and 8-bit codes when a lane's piece is 16
+// bytes and a head group's token row is a whole number of 16-chunk (256-byte)
+// swizzle groups.  On the long-tail step it took int8 from 364 to 327 us and
+// fp8 from 356 (vector kernel) to 326 us.  int4 keeps per-head loads: its
+// steps carry the most vector work per byte (the nibble widening), and a
+// barrier per step that keeps the 8 waves in the same phase cost more than the
+// longer runs gained (285 against 251 us).
 template <int CDT, int HD>
 __host__ __device__ constexpr bool mf_stageable_layout() {
-  return MfLayout<CDT, HD>::EBITS == 8 && MfLayout<CDT, HD>::PS == 16 && MfLayout<CDT, HD>::LIN >= 1;
+  return (MfLayout<CDT, HD>::EBITS == 8 || MfLayout<CDT, HD>::EBITS == 16) &&
+         MfLayout<CDT, HD>::PS == 16 && MfLayout<CDT, HD>::LIN >= 1;
 }
 __host__ __device__ inline bool mf_staged_ok(int row_bytes, int hw) {
   return row_bytes >= 64 && (hw * row_bytes) % 256 == 0;
@@ -962,14 +969,29 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
   };
 
-  auto step = [&](const uint32_t* fk, const uint32_t* fv, const float* fvs, int base) {
+  // bf16 rows staged in LDS are already the V operand's rows: its transposed
+  // reads go to the stage directly (lane (j, r): token 4j + r / 4, the 8 bytes
+  // at 32 b + 8 (r % 4) of the head's row, through the stage's swizzle), and
+  // the wave needs no V slice of its own.
+  constexpr bool VDIRECT = STAGED && CDT == PA_BF16;
+  uint32_t vrd[VDIRECT ? ML::NB : 1];
+  if constexpr (VDIRECT) {
+    const int rc = a.hw * (ML::ROW / 16);
+    const int t = 4 * j + (r >> 2), w = t >> 1, u = ((r >> 1) & 1) ^ (t & 1);
+#pragma unroll
+    for (int b = 0; b < ML::NB; ++b)
+      vrd[b] = (uint32_t)(16 * (t * rc + wv * (ML::ROW / 16) + 2 * (b ^ w) + u) + 8 * (r & 1));
+  }
+
+  auto step = [&](const uint32_t* fk, const uint32_t* fv, const float* fvs, int base,
+                  const uint8_t* vsrc) {
     // S^T: tokens 4j .. 4j+3 of head column r
     mf_f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < ML::NT; ++t)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_k8<CDT>(fk + DW8 * t), qb[t], sc, 0, 0, 0);
     // V rows (bf16) into this wave's LDS slice: token r, this lane's dims
-    {
+    if constexpr (!VDIRECT) {
       uint8_t* row = vl + r * ML::VROW;
 #pragma unroll
       for (int t = 0; t < ML::NT; ++t) {
@@ -1019,8 +1041,11 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     const uint8_t* rd = vl + (4 * j + (r >> 2)) * ML::VROW + (r & 3) * 8;
 #pragma unroll
     for (int b = 0; b < ML::NB; ++b) {
+      const uint8_t* src;
+      if constexpr (VDIRECT) src = vsrc + vrd[b];
+      else src = rd + 32 * b;
       const mf_s4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) mf_s4_t*)(rd + 32 * b));
+          (__attribute__((address_space(3))) mf_s4_t*)src);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb, acc[b], 0, 0, 0);
     }
   };
@@ -1041,13 +1066,13 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
-        step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u));
+        step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u), nullptr);
       }
     }
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) {
       prefetch(buf[(u + NBUF - 1) % NBUF], i + u + NBUF - 1);
-      if (i + u < nsteps) step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u));
+      if (i + u < nsteps) step(buf[u].k, buf[u].v, buf[u].vs, begin + 16 * (i + u), nullptr);
     }
   } else {
     // Step x is loaded into buf[x % NBUF], written to stage x & 1 while step
@@ -1106,16 +1131,18 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 #pragma unroll
       for (int k = 0; k < ML::NP; ++k) {
         const uint4 p = *(const uint4*)(sk + sm.rpos[k]);
-        const uint4 q = *(const uint4*)(sk + ML::STAGE + sm.rpos[k]);
         kc[4 * k] = p.x; kc[4 * k + 1] = p.y; kc[4 * k + 2] = p.z; kc[4 * k + 3] = p.w;
-        vc[4 * k] = q.x; vc[4 * k + 1] = q.y; vc[4 * k + 2] = q.z; vc[4 * k + 3] = q.w;
+        if constexpr (!VDIRECT) {
+          const uint4 q = *(const uint4*)(sk + ML::STAGE + sm.rpos[k]);
+          vc[4 * k] = q.x; vc[4 * k + 1] = q.y; vc[4 * k + 2] = q.z; vc[4 * k + 3] = q.w;
+        }
       }
       float vs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (CDT == PA_INT4) {
         const float4 t = *(const float4*)(vsl + (x & 1) * 16 * DECODE_MAX_HW);
         vs[0] = t.x; vs[1] = t.y; vs[2] = t.z; vs[3] = t.w;
       }
-      step(kc, vc, vs, begin + 16 * x);
+      step(kc, vc, vs, begin + 16 * x, sk + ML::STAGE);
     };
 #pragma unroll
     for (int d = 0; d < NBUF; ++d) prefetch(buf[d], d, __builtin_amdgcn_readfirstlane(table_at(d)));
@@ -1166,10 +1193,12 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 template <int CDT, int HD, int G, int NBUF, bool STAGED>
 __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_mfma_kernel(DecodeArgs a) {
   using ML = MfLayout<CDT, HD>;
-  // per-wave V slices, then (staged) two stages of K and V and the INT4 value
-  // scales of each stage's 16 tokens per head
-  __shared__ __attribute__((aligned(16))) uint8_t lds[DECODE_MAX_HW * ML::WAVE_LDS +
-                                                      (STAGED ? 4 * ML::STAGE + 2 * DECODE_MAX_HW * 64 : 0)];
+  // per-wave V slices (none when bf16 V is read from the stage), then (staged)
+  // two stages of K and V and the INT4 value scales of each stage's 16 tokens
+  // per head
+  constexpr int SLICES = (STAGED && CDT == PA_BF16) ? 0 : DECODE_MAX_HW * ML::WAVE_LDS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SLICES +
+      (STAGED ? 4 * ML::STAGE + (CDT == PA_INT4 ? 2 * DECODE_MAX_HW * 64 : 0) : 0)];
   const int w = blockIdx.x;
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
@@ -1185,13 +1214,13 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   int hg = rr / steps0;
   int step = rr % steps0;
   int64_t u = u0;
-  uint8_t* vl = lds + wv * ML::WAVE_LDS;
+  uint8_t* vl = lds + (SLICES ? wv * ML::WAVE_LDS : 0);
   while (true) {
     const int steps = steps_of(uniform_load(a.context_lens, s));
     const int run_end = (int)min((int64_t)steps, step + (u1 - u));
     const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
     decode_run_mf<CDT, HD, G, NBUF, STAGED>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv,
-                                            vl, wv, lds + DECODE_MAX_HW * ML::WAVE_LDS);
+                                            vl, wv, lds + SLICES);
     u += run_end - step;
     if (u >= u1) break;
     step = 0;
@@ -1376,12 +1405,15 @@ static int64_t resident_wgs(int hw) {
 }
 
 // Cache dtypes whose decode runs on the matrix cores (bit = dtype code) when
-// block_size >= 16: int4, int8 and fp8.  Their codes cost vector-ALU work to
-// widen, which the matrix cores take the products off (on the long-tail step,
-// int4 364 -> 251 us, int8 399 -> 327 us with staged loads, fp8 356 -> 326 us
-// with staged loads).  bf16 is bound by HBM on the vector path.
+// block_size >= 16: bf16, fp8, int8 and int4.  The 8- and 4-bit codes cost
+// vector-ALU work to widen, which the matrix cores take the products off (on
+// the long-tail step, int4 364 -> 251 us, int8 399 -> 327 us and fp8
+// 356 -> 326 us, the 8-bit caches with staged loads).  bf16 gains from the
+// staged whole-row loads alone: Llama-3 GQA step 216 -> 209 us, long-tail
+// step 608 -> 595 us, Llama-2 MHA unchanged at 357 us.  fp32 caches and blocks
+// of fewer than 16 tokens take the vector kernel.
 #ifndef DECODE_MFMA_MASK
-#define DECODE_MFMA_MASK ((1 << PA_FP8_E4M3) | (1 << PA_INT8) | (1 << PA_INT4))
+#define DECODE_MFMA_MASK ((1 << PA_BF16) | (1 << PA_FP8_E4M3) | (1 << PA_INT8) | (1 << PA_INT4))
 #endif
 // steps in flight per wave on the matrix-core path (fewer bytes per step for
 // narrower codes, so more steps)
@@ -1391,13 +1423,16 @@ static int64_t resident_wgs(int hw) {
 #ifndef DECODE_MF_NBUF8
 #define DECODE_MF_NBUF8 3   // FP8 / INT8
 #endif
+#ifndef DECODE_MF_NBUF16
+#define DECODE_MF_NBUF16 3   // BF16
+#endif
 // staged loads on the matrix-core path where the layout allows (1), or per-head
 // loads everywhere (0)
 #ifndef DECODE_MF_STAGED
 #define DECODE_MF_STAGED 1
 #endif
 __host__ __device__ constexpr int mf_nbuf(int CDT) {
-  return CDT == PA_INT4 ? DECODE_MF_NBUF4 : CDT == PA_BF16 ? 2 : DECODE_MF_NBUF8;
+  return CDT == PA_INT4 ? DECODE_MF_NBUF4 : CDT == PA_BF16 ? DECODE_MF_NBUF16 : DECODE_MF_NBUF8;
 }
 
 template <int CDT, int HD, int G, bool STAGED>
