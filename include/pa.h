@@ -137,6 +137,35 @@ pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
                        float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_kv_append_paged -- pa_slot_mapping and pa_kv_append in one launch.
+ *   Source: the block-table address map of "3.3 Batching and memory
+ *   management", section "PagedAttention: the block table", and the append of
+ *   "KV Cache: the memory bottleneck of LLM inference", section 1.1.
+ *
+ *   Token i of segment s (cu_tokens[s] <= i < cu_tokens[s+1]) gets the slot
+ *   pa_slot_mapping gives it (from block_tables, start_pos, block_size) and is
+ *   appended exactly as pa_kv_append appends it with that slot: same encoders,
+ *   same skipping of negative and out-of-pool slots, bit-identical pools.
+ *   slot_mapping (int64 [num_tokens], may be NULL) receives the slots as
+ *   pa_slot_mapping writes them.
+ *
+ *   max_tokens_per_seq  host-side bound on the segment lengths; it sizes the
+ *                       grid only (longer segments are still appended whole)
+ *   cu_tokens           int32 [num_seqs + 1], non-decreasing, last entry
+ *                       num_tokens; token indices outside [0, num_tokens) are
+ *                       never read or written
+ *   other arguments     as in pa_slot_mapping and pa_kv_append
+ */
+pa_status pa_kv_append_paged(void* k_cache, void* v_cache, int cache_dtype,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t head_dim, const void* k_new, const void* v_new,
+                             int src_dtype, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* cu_tokens,
+                             const int32_t* start_pos, int32_t num_seqs, int32_t num_tokens,
+                             int32_t max_tokens_per_seq, int64_t* slot_mapping,
+                             float k_scale, float v_scale, void* stream);
+
+/*
  * pa_decode_workspace_bytes -- scratch needed by pa_decode for these sizes.
  *   split_tokens: 0 = the library's choice; otherwise the minimum number of
  *   context tokens one split (one workgroup) handles, rounded up to 16.
@@ -338,6 +367,21 @@ pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_scales, int32
                             const void* k_new, const void* v_new, int src_dtype,
                             const int64_t* slot_mapping, int32_t num_tokens,
                             const float* k_channel_scales, void* stream);
+
+/*
+ * pa_kv_append_int4_paged -- pa_slot_mapping and pa_kv_append_int4 in one
+ * launch, as pa_kv_append_paged is for pa_kv_append: bit-identical codes and
+ * value scales; slot_mapping (may be NULL) receives the slots.
+ */
+pa_status pa_kv_append_int4_paged(void* k_cache, void* v_cache, float* v_scales,
+                                  int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                  int32_t head_dim, const void* k_new, const void* v_new,
+                                  int src_dtype, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* cu_tokens,
+                                  const int32_t* start_pos, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t max_tokens_per_seq,
+                                  int64_t* slot_mapping, const float* k_channel_scales,
+                                  void* stream);
 
 /*
  * pa_decode_int4 / pa_decode_int4_partials -- pa_decode and pa_decode_partials

@@ -52,6 +52,10 @@ def lib():
         _c("pa_kv_append", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int, P, I,
            F, F, P)
         _c("pa_kv_append_int4", ctypes.c_int, P, P, P, I, I, I, I, P, P, ctypes.c_int, P, I, P, P)
+        _c("pa_kv_append_paged", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int,
+           P, I, P, P, I, I, I, P, F, F, P)
+        _c("pa_kv_append_int4_paged", ctypes.c_int, P, P, P, I, I, I, I, P, P, ctypes.c_int, P, I,
+           P, P, I, I, I, P, P, P)
         _c("pa_decode_int4", ctypes.c_int, P, P, ctypes.c_int, P, P, P, P, I, I, I, I, I, P, I, P,
            I, I, F, I, P, S, P)
         _c("pa_decode_int4_partials", ctypes.c_int, P, ctypes.c_int, P, P, P, P, I, I, I, I, I, P,
@@ -149,6 +153,41 @@ def pa_kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tens
         _stream(stream)))
 
 
+def _seg_args(block_tables, cu_tokens, start_pos, slot_mapping, num_tokens):
+    _dev(block_tables, cu_tokens, start_pos)
+    _need(block_tables.dtype == cu_tokens.dtype == start_pos.dtype == torch.int32, "int32 tables")
+    num_seqs = start_pos.shape[0]
+    _need(cu_tokens.numel() == num_seqs + 1, "cu_tokens: [num_seqs + 1]")
+    if slot_mapping is not None:
+        _dev(slot_mapping)
+        _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() >= num_tokens,
+              "slot_mapping: int64 [num_tokens]")
+    return (_ptr(block_tables), block_tables.shape[1] if block_tables.dim() == 2 else 0,
+            _ptr(cu_tokens), _ptr(start_pos), num_seqs)
+
+
+def pa_kv_append_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, block_tables: torch.Tensor, cu_tokens: torch.Tensor,
+                       start_pos: torch.Tensor, max_tokens_per_seq: int,
+                       slot_mapping: torch.Tensor | None = None, k_scale: float = 1.0,
+                       v_scale: float = 1.0, stream=None) -> None:
+    """pa_slot_mapping + pa_kv_append in one launch; slot_mapping (optional) gets the slots."""
+    L = lib()
+    _dev(k_cache, v_cache, k_new, v_new)
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "pools: [nb, bs, n_kv, hd]")
+    _need(k_cache.dtype == v_cache.dtype and k_new.dtype == v_new.dtype, "dtype mismatch")
+    nb, bs, nkv, hd = k_cache.shape
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3 and tuple(k_new.shape[1:]) == (nkv, hd),
+          "new K/V: [T, n_kv, hd]")
+    T = k_new.shape[0]
+    tp, mb, cp, sp, ns = _seg_args(block_tables, cu_tokens, start_pos, slot_mapping, T)
+    _check("pa_kv_append_paged", L.pa_kv_append_paged(
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv, hd, _ptr(k_new),
+        _ptr(v_new), _dtype_code(k_new), tp, mb, cp, sp, ns, T, max_tokens_per_seq,
+        _ptr(slot_mapping) if slot_mapping is not None else None, k_scale, v_scale,
+        _stream(stream)))
+
+
 def _int4_pools(k_cache, v_cache, v_scales, k_channel_scales):
     """Shapes of an INT4 cache: packed pools uint8 [nb, bs, n_kv, hd / 2], value
     scales float32 [nb, n_kv, bs], key scales float32 [n_kv, hd]."""
@@ -177,6 +216,26 @@ def pa_kv_append_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, v_scales: to
     _check("pa_kv_append_int4", L.pa_kv_append_int4(
         _ptr(k_cache), _ptr(v_cache), _ptr(v_scales), nb, bs, nkv, hd, _ptr(k_new), _ptr(v_new),
         _dtype_code(k_new), _ptr(slot_mapping), k_new.shape[0], _ptr(k_channel_scales),
+        _stream(stream)))
+
+
+def pa_kv_append_int4_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, v_scales: torch.Tensor,
+                            k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
+                            cu_tokens: torch.Tensor, start_pos: torch.Tensor,
+                            max_tokens_per_seq: int, k_channel_scales: torch.Tensor,
+                            slot_mapping: torch.Tensor | None = None, stream=None) -> None:
+    """pa_slot_mapping + pa_kv_append_int4 in one launch."""
+    L = lib()
+    nb, bs, nkv, hd = _int4_pools(k_cache, v_cache, v_scales, k_channel_scales)
+    _dev(k_new, v_new)
+    _need(k_new.dtype == v_new.dtype and k_new.shape == v_new.shape and k_new.dim() == 3 and
+          tuple(k_new.shape[1:]) == (nkv, hd), "new K/V: [T, n_kv, hd]")
+    T = k_new.shape[0]
+    tp, mb, cp, sp, ns = _seg_args(block_tables, cu_tokens, start_pos, slot_mapping, T)
+    _check("pa_kv_append_int4_paged", L.pa_kv_append_int4_paged(
+        _ptr(k_cache), _ptr(v_cache), _ptr(v_scales), nb, bs, nkv, hd, _ptr(k_new), _ptr(v_new),
+        _dtype_code(k_new), tp, mb, cp, sp, ns, T, max_tokens_per_seq,
+        _ptr(slot_mapping) if slot_mapping is not None else None, _ptr(k_channel_scales),
         _stream(stream)))
 
 

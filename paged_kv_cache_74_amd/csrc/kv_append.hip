@@ -18,6 +18,19 @@ namespace pa {
 // ---------------------------------------------------------------------------
 // slot mapping: one workgroup per segment, lanes stride over its tokens
 // ---------------------------------------------------------------------------
+// Slot of logical position p through one sequence's table row, or -1 when p is
+// negative, past the row, or its table entry is negative.
+__device__ __forceinline__ int64_t map_slot(const int32_t* row, int max_blocks, int block_size,
+                                            int64_t p) {
+  const int64_t j = p / block_size;
+  int64_t slot = -1;
+  if (p >= 0 && j < max_blocks) {
+    const int32_t blk = row[j];
+    if (blk >= 0) slot = (int64_t)blk * block_size + (p - j * block_size);
+  }
+  return slot;
+}
+
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     int64_t* __restrict__ slots, const int32_t* __restrict__ tables, int max_blocks,
     int block_size, const int32_t* __restrict__ cu_tokens,
@@ -26,16 +39,37 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   const int t0 = cu_tokens[s], t1 = cu_tokens[s + 1];
   const int64_t p0 = start_pos[s];
   const int32_t* row = tables + (int64_t)s * max_blocks;
-  for (int i = t0 + threadIdx.x; i < t1; i += blockDim.x) {
-    const int64_t p = p0 + (i - t0);
-    const int64_t j = p / block_size;
-    int64_t slot = -1;
-    if (p >= 0 && j < max_blocks) {
-      const int32_t blk = row[j];
-      if (blk >= 0) slot = (int64_t)blk * block_size + (p - j * block_size);
-    }
-    slots[i] = slot;
-  }
+  for (int i = t0 + threadIdx.x; i < t1; i += blockDim.x)
+    slots[i] = map_slot(row, max_blocks, block_size, p0 + (i - t0));
+}
+
+// The segment map of pa_slot_mapping, for the append kernels that compute each
+// token's slot themselves (one launch instead of two).  Workgroup (s, y, kv)
+// takes lane-pieces y*256 + tid, stepping by gridDim.y*256, of segment s's
+// tokens; token indices are clamped to [0, num_tokens) so a malformed
+// cu_tokens cannot reach past k_new / v_new.
+struct SegMap {
+  const int32_t* tables;
+  const int32_t* cu_tokens;
+  const int32_t* start_pos;
+  int64_t* slots_out;   // optional: the slots, as pa_slot_mapping writes them
+  int max_blocks;
+  int block_size;
+  int num_tokens;
+};
+
+struct SegRange {
+  int t0, t1;
+  int64_t p0;
+  const int32_t* row;
+};
+__device__ __forceinline__ SegRange seg_range(const SegMap& m, int s) {
+  SegRange r;
+  r.t0 = max(0, uniform_load(m.cu_tokens, s));
+  r.t1 = min(m.num_tokens, uniform_load(m.cu_tokens, s + 1));
+  r.p0 = uniform_load(m.start_pos, s);
+  r.row = m.tables + (int64_t)s * m.max_blocks;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -139,6 +173,19 @@ constexpr int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 :
 
 // One lane moves 8 elements; a row (token, head) has head_dim / 8 lanes.
 // grid.x covers num_tokens * n_kv * head_dim / 8 lanes for K, grid.y = 2 picks K or V.
+// Piece `within` (8 elements) of token `tok`'s K or V row into slot `slot`.
+template <int SRC, int DST>
+__device__ __forceinline__ void append_piece(uint8_t* k_cache, uint8_t* v_cache,
+                                             const uint8_t* k_new, const uint8_t* v_new,
+                                             int64_t tok, int within, int64_t slot,
+                                             int lanes_per_token, bool is_v, float inv) {
+  constexpr int SB = elem_bytes(SRC), DB = elem_bytes(DST);
+  const int64_t tok_elems = (int64_t)lanes_per_token * 8;  // n_kv * head_dim
+  const uint8_t* src = (is_v ? v_new : k_new) + (tok * tok_elems + within * 8) * SB;
+  uint8_t* dst = (is_v ? v_cache : k_cache) + (slot * tok_elems + within * 8) * DB;
+  AppendIO<SRC, DST>::run(src, dst, inv);
+}
+
 template <int SRC, int DST>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
@@ -153,11 +200,28 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   const int within = lane - tok * lanes_per_token;   // which 8-element piece of the token
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= num_slots_in_pool) return;
-  constexpr int SB = elem_bytes(SRC), DB = elem_bytes(DST);
-  const int64_t tok_elems = (int64_t)lanes_per_token * 8;  // n_kv * head_dim
-  const uint8_t* src = (is_v ? v_new : k_new) + (tok * tok_elems + within * 8) * SB;
-  uint8_t* dst = (is_v ? v_cache : k_cache) + (slot * tok_elems + within * 8) * DB;
-  AppendIO<SRC, DST>::run(src, dst, is_v ? v_inv : k_inv);
+  append_piece<SRC, DST>(k_cache, v_cache, k_new, v_new, tok, within, slot, lanes_per_token, is_v,
+                         is_v ? v_inv : k_inv);
+}
+
+// The same append with each token's slot computed from the block table.
+template <int SRC, int DST>
+__global__ __launch_bounds__(256) void kv_append_paged_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new, SegMap m,
+    int64_t num_slots_in_pool, int lanes_per_token, float k_inv, float v_inv) {
+  const SegRange r = seg_range(m, blockIdx.x);
+  const bool is_v = blockIdx.z != 0;
+  const int total = max(0, r.t1 - r.t0) * lanes_per_token;   // < 2^31 (host check)
+  for (int L = blockIdx.y * 256 + threadIdx.x; L < total; L += gridDim.y * 256) {
+    const int tl = (int)((unsigned)L / (unsigned)lanes_per_token);
+    const int within = L - tl * lanes_per_token;
+    const int64_t slot = map_slot(r.row, m.max_blocks, m.block_size, r.p0 + tl);
+    if (!is_v && within == 0 && m.slots_out) m.slots_out[r.t0 + tl] = slot;
+    if (slot < 0 || slot >= num_slots_in_pool) continue;
+    append_piece<SRC, DST>(k_cache, v_cache, k_new, v_new, r.t0 + tl, within, slot,
+                           lanes_per_token, is_v, is_v ? v_inv : k_inv);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,24 +259,17 @@ __device__ __forceinline__ void load8_f32(const uint8_t* src, float (&x)[8]) {
   }
 }
 
+// Piece j (8 elements) of row `row` (token * n_kv + head) into slot `slot`;
+// every lane of the row's lane group must call it (the value rows' amax is
+// found with shuffles inside the group), `ok` false only suppressing stores.
 template <int SRC>
-__global__ __launch_bounds__(256) void kv_append_int4_kernel(
+__device__ __forceinline__ void append_int4_piece(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ v_scales,
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
-    const int64_t* __restrict__ slots, const float* __restrict__ k_channel_scales,
-    int64_t num_slots_in_pool, int block_size, int n_kv, int lanes_per_row, int total_lanes) {
-  const int lane = blockIdx.x * blockDim.x + threadIdx.x;
-  // every lane of a row takes part in the row's shuffles: no early return
-  // before them (rows never straddle a wave: lanes_per_row divides 64)
-  const bool live = lane < total_lanes;
-  const int row = (int)((unsigned)min(lane, total_lanes - 1) / (unsigned)lanes_per_row);
-  const int j = lane - row * lanes_per_row;          // 8-element piece of the row
-  const int tok = row / n_kv, head = row - tok * n_kv;
-  const int64_t slot = slots[tok];
-  const bool ok = live && slot >= 0 && slot < num_slots_in_pool;
+    const float* __restrict__ k_channel_scales, int64_t row, int head, int j, int64_t slot,
+    bool ok, int block_size, int n_kv, int lanes_per_row, bool is_v) {
   const int hd = lanes_per_row * 8;
   constexpr int SB = SRC == PA_F32 ? 4 : 2;
-  const bool is_v = blockIdx.y != 0;
   float x[8];
   load8_f32<SRC>((is_v ? v_new : k_new) + ((int64_t)row * hd + j * 8) * SB, x);
   float inv[8];
@@ -236,6 +293,53 @@ __global__ __launch_bounds__(256) void kv_append_int4_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) packed |= f32_to_int4_nibble(x[i] * inv[i]) << (4 * i);
   if (ok) *(uint32_t*)((is_v ? v_cache : k_cache) + (slot * n_kv + head) * (hd / 2) + j * 4) = packed;
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void kv_append_int4_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ v_scales,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, const float* __restrict__ k_channel_scales,
+    int64_t num_slots_in_pool, int block_size, int n_kv, int lanes_per_row, int total_lanes) {
+  const int lane = blockIdx.x * blockDim.x + threadIdx.x;
+  // every lane of a row takes part in the row's shuffles: no early return
+  // before them (rows never straddle a wave: lanes_per_row divides 64)
+  const bool live = lane < total_lanes;
+  const int row = (int)((unsigned)min(lane, total_lanes - 1) / (unsigned)lanes_per_row);
+  const int j = lane - row * lanes_per_row;          // 8-element piece of the row
+  const int tok = row / n_kv, head = row - tok * n_kv;
+  const int64_t slot = slots[tok];
+  const bool ok = live && slot >= 0 && slot < num_slots_in_pool;
+  append_int4_piece<SRC>(k_cache, v_cache, v_scales, k_new, v_new, k_channel_scales, row, head, j,
+                         slot, ok, block_size, n_kv, lanes_per_row, blockIdx.y != 0);
+}
+
+// The same append with each token's slot computed from the block table.  The
+// loop bound is uniform over the workgroup, so every lane reaches the
+// shuffles; rows never straddle a wave (256-lane strides, lanes_per_row
+// divides 64).
+template <int SRC>
+__global__ __launch_bounds__(256) void kv_append_int4_paged_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ v_scales,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new, SegMap m,
+    const float* __restrict__ k_channel_scales, int64_t num_slots_in_pool, int block_size,
+    int n_kv, int lanes_per_row) {
+  const SegRange r = seg_range(m, blockIdx.x);
+  const bool is_v = blockIdx.z != 0;
+  const int total = max(0, r.t1 - r.t0) * n_kv * lanes_per_row;   // < 2^31 (host check)
+  for (int base = blockIdx.y * 256; base < total; base += gridDim.y * 256) {
+    const int L = base + threadIdx.x;
+    const bool live = L < total;
+    const int rl = (int)((unsigned)min(L, total - 1) / (unsigned)lanes_per_row);
+    const int j = min(L, total - 1) - rl * lanes_per_row;
+    const int tl = rl / n_kv, head = rl - tl * n_kv;
+    const int64_t slot = map_slot(r.row, m.max_blocks, m.block_size, r.p0 + tl);
+    if (!is_v && live && j == 0 && head == 0 && m.slots_out) m.slots_out[r.t0 + tl] = slot;
+    const bool ok = live && slot >= 0 && slot < num_slots_in_pool;
+    append_int4_piece<SRC>(k_cache, v_cache, v_scales, k_new, v_new, k_channel_scales,
+                           (int64_t)(r.t0 + tl) * n_kv + head, head, j, slot, ok, block_size, n_kv,
+                           lanes_per_row, is_v);
+  }
 }
 
 }  // namespace pa
@@ -338,5 +442,104 @@ extern "C" pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_sc
                      (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new,
                      slot_mapping, k_channel_scales, (int64_t)num_blocks * block_size, block_size,
                      n_kv_heads, lanes_per_row, total);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Grid of the paged appends: one workgroup row per segment, enough 256-lane
+// workgroups per segment for max_tokens_per_seq tokens (a hint: longer
+// segments loop), K and V in grid.z.
+static dim3 paged_grid(int num_seqs, int max_tokens_per_seq, int64_t lanes_per_token) {
+  int64_t gy = ((int64_t)max(1, max_tokens_per_seq) * lanes_per_token + 255) / 256;
+  if (gy > 65535) gy = 65535;
+  return dim3((unsigned)num_seqs, (unsigned)gy, 2);
+}
+
+extern "C" pa_status pa_kv_append_paged(void* k_cache, void* v_cache, int cache_dtype,
+                                        int32_t num_blocks, int32_t block_size,
+                                        int32_t n_kv_heads, int32_t head_dim, const void* k_new,
+                                        const void* v_new, int src_dtype,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* cu_tokens, const int32_t* start_pos,
+                                        int32_t num_seqs, int32_t num_tokens,
+                                        int32_t max_tokens_per_seq, int64_t* slot_mapping,
+                                        float k_scale, float v_scale, void* stream) {
+  if (num_blocks < 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || num_tokens < 0 ||
+      num_seqs < 0 || max_blocks_per_seq < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0 || num_seqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !cu_tokens || !start_pos)
+    return PA_ERR_NULL;
+  const int64_t lanes = (int64_t)n_kv_heads * head_dim / 8;
+  if (lanes * num_tokens >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
+  SegMap m;
+  m.tables = block_tables; m.cu_tokens = cu_tokens; m.start_pos = start_pos;
+  m.slots_out = slot_mapping; m.max_blocks = max_blocks_per_seq; m.block_size = block_size;
+  m.num_tokens = num_tokens;
+  const int64_t pool_slots = (int64_t)num_blocks * block_size;
+  const dim3 grid = paged_grid(num_seqs, max_tokens_per_seq, lanes);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* kc = (uint8_t*)k_cache;
+  uint8_t* vc = (uint8_t*)v_cache;
+  const uint8_t* kn = (const uint8_t*)k_new;
+  const uint8_t* vn = (const uint8_t*)v_new;
+  const int lpt = (int)lanes;
+  if (cache_dtype == src_dtype && cache_dtype == PA_BF16) {
+    hipLaunchKernelGGL((kv_append_paged_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc,
+                       kn, vn, m, pool_slots, lpt, 1.0f, 1.0f);
+  } else if (cache_dtype == src_dtype && cache_dtype == PA_F32) {
+    hipLaunchKernelGGL((kv_append_paged_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc,
+                       kn, vn, m, pool_slots, lpt, 1.0f, 1.0f);
+  } else if ((cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8) &&
+             (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f)) return PA_ERR_SHAPE;
+    const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;   // one binary32 division each
+    const bool i8 = cache_dtype == PA_INT8;
+    auto kernel = src_dtype == PA_BF16
+                      ? (i8 ? kv_append_paged_kernel<PA_BF16, PA_INT8>
+                            : kv_append_paged_kernel<PA_BF16, PA_FP8_E4M3>)
+                      : (i8 ? kv_append_paged_kernel<PA_F32, PA_INT8>
+                            : kv_append_paged_kernel<PA_F32, PA_FP8_E4M3>);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, m, pool_slots, lpt, k_inv,
+                       v_inv);
+  } else {
+    return PA_ERR_DTYPE;
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_kv_append_int4_paged(void* k_cache, void* v_cache, float* v_scales,
+                                             int32_t num_blocks, int32_t block_size,
+                                             int32_t n_kv_heads, int32_t head_dim,
+                                             const void* k_new, const void* v_new, int src_dtype,
+                                             const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq, const int32_t* cu_tokens,
+                                             const int32_t* start_pos, int32_t num_seqs,
+                                             int32_t num_tokens, int32_t max_tokens_per_seq,
+                                             int64_t* slot_mapping,
+                                             const float* k_channel_scales, void* stream) {
+  if (num_blocks < 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || num_tokens < 0 ||
+      num_seqs < 0 || max_blocks_per_seq < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (src_dtype != PA_BF16 && src_dtype != PA_F32) return PA_ERR_DTYPE;
+  if (num_tokens == 0 || num_seqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !v_scales || !k_new || !v_new || !block_tables || !cu_tokens ||
+      !start_pos || !k_channel_scales)
+    return PA_ERR_NULL;
+  const int lanes_per_row = head_dim / 8;
+  const int64_t lanes = (int64_t)n_kv_heads * lanes_per_row;
+  if (lanes * num_tokens >= ((int64_t)1 << 31) - 256) return PA_ERR_SHAPE;
+  SegMap m;
+  m.tables = block_tables; m.cu_tokens = cu_tokens; m.start_pos = start_pos;
+  m.slots_out = slot_mapping; m.max_blocks = max_blocks_per_seq; m.block_size = block_size;
+  m.num_tokens = num_tokens;
+  const dim3 grid = paged_grid(num_seqs, max_tokens_per_seq, lanes);
+  auto kernel = src_dtype == PA_BF16 ? kv_append_int4_paged_kernel<PA_BF16>
+                                     : kv_append_int4_paged_kernel<PA_F32>;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
+                     (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new, m,
+                     k_channel_scales, (int64_t)num_blocks * block_size, block_size, n_kv_heads,
+                     lanes_per_row);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

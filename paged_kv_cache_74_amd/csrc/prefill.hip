@@ -40,6 +40,8 @@
 //     double-buffered, one barrier per tile; three workgroups share a CU.
 #include "pa_device.h"
 
+#include <type_traits>
+
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -403,7 +405,8 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   auto gload = [&](int t, TileRegs& R) {
     // block_size >= 16: the tile spans at most two blocks; their table entries
     // are read wave-uniformly (scalar loads, which do not wait behind the K/V
-    // loads in flight)
+    // loads in flight; a vector load of both entries issued a tile ahead, with
+    // the K/V loads, measured 7% slower)
     int jlo = 0, blo = 0, bhi = 0;
     if (a.block_size >= 16) {
       jlo = min((t * PF_BN) >> a.bs_log2, jmax);
@@ -457,7 +460,11 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
         if (lc == 0) *(float2*)(buf + LD::K_BYTES + LD::V_BYTES + 8 * lp) = make_float2(R.s0, R.s1);
     }
   };
-  auto compute = [&](const uint8_t* buf, int kt) {
+  // MASKED is a compile-time flag: only the last tiles of a segment hold keys
+  // that some row must not see, and the others skip the mask's compares and
+  // selects entirely
+  auto compute = [&](const uint8_t* buf, int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const uint8_t* lk = buf;
     const uint8_t* lv = buf + LD::K_BYTES;
     const int kb = kt * PF_BN;
@@ -472,8 +479,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, sc, 0, 0, 0);
     }
     // raw scores; the positive scale c is applied inside the exponent below
-    const bool full_tile = kb + PF_BN <= T && (!a.causal || kb + PF_BN - 1 <= first_pos);
-    if (!full_tile) {
+    if constexpr (MASKED) {
       // score r holds key kb + 4 grp + 8(r/4) + r%4; keys above the row's last
       // visible key are masked
       const int lim = (a.causal ? min(pos, T - 1) : T - 1) - kb - 4 * grp;
@@ -536,16 +542,21 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   // the next tile in registers while one is computed, two LDS buffers.  One
   // loop body per tile (the buffer offset alternates at run time) keeps the
   // accumulators in the same registers from tile to tile.
+  // tiles below tfull hold only keys that every row of the segment sees
+  const int tfull = min(T, a.causal ? first_pos + 1 : T) / PF_BN;
   TileRegs R0;
   gload(t0, R0);
   int boff = 0;
-  for (int t = t0; t < t1; ++t) {
+  auto tile = [&](int t, auto masked) {
     sstore(R0, lds + boff);
     gload(min(t + 1, t1 - 1), R0);
     __syncthreads();
-    if (wave_ok) compute(lds + boff, t);
+    if (wave_ok) compute(lds + boff, t, masked);
     boff ^= BUF;
-  }
+  };
+  const int tm = max(t0, min(t1, tfull));
+  for (int t = t0; t < tm; ++t) tile(t, std::false_type{});
+  for (int t = tm; t < t1; ++t) tile(t, std::true_type{});
   __syncthreads();   // the next piece reuses the LDS buffers
 
   const float ltot = lsum + shfl_xor(lsum, 32);

@@ -37,9 +37,10 @@ def i32(a, dev) -> torch.Tensor:
 class DeviceWorkload:
     """Device copies of a workload's tables/values plus pools built by the library."""
 
-    def __init__(self, w: Workload, dev="cuda"):
+    def __init__(self, w: Workload, dev="cuda", paged_append: bool = False):
         self.w = w
         self.dev = dev
+        self.paged_append = paged_append   # slot map + append in one call
         self.tables = i32(w.block_tables, dev)
         self.ctx = i32(w.context_lens, dev)
         self.k_cache = poison_pool(w, dev)
@@ -57,6 +58,20 @@ class DeviceWorkload:
         cu = np.zeros(len(lens) + 1, np.int32)
         np.cumsum(lens, out=cu[1:])
         n = int(cu[-1])
+        if self.paged_append:
+            slots = torch.full((n,), -7, dtype=torch.int64, device=self.dev)
+            if n == 0:
+                return slots
+            args = (i32(cu, self.dev), i32(start, self.dev), int(max(lens)))
+            if w.cache_dtype == "int4":
+                pa.pa_kv_append_int4_paged(self.k_cache, self.v_cache, self.v_scales,
+                                           k.to(self.dev), v.to(self.dev), self.tables, *args,
+                                           self.k_channel_scales, slot_mapping=slots)
+            else:
+                pa.pa_kv_append_paged(self.k_cache, self.v_cache, k.to(self.dev), v.to(self.dev),
+                                      self.tables, *args, slot_mapping=slots, k_scale=w.k_scale,
+                                      v_scale=w.v_scale)
+            return slots
         slots = pa.pa_slot_mapping(self.tables, i32(cu, self.dev), i32(start, self.dev),
                                    w.block_size, n)
         if n and w.cache_dtype == "int4":
