@@ -96,6 +96,53 @@ def source_hash(sources) -> str:
     return h.hexdigest()
 
 
+def timed(fn, reps: int = 5) -> float:
+    """Median milliseconds of fn() over reps launches (one warm-up), HIP events on the
+    current stream."""
+    import numpy as np
+    import torch
+    fn()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
+    """What plain readers and a plain MFMA loop reach on this GPU (see pa.h, Measured
+    ceilings): the decode rows' whole K and V blocks read in table order (the pattern a
+    paged decode reads), the whole pools read in physical order, and the bf16 MFMA
+    issue rate."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_74_amd as pa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    W = cus * 8
+    sink = torch.empty(W, dtype=torch.int32, device=dev)
+    rec = {}
+    block_bytes = kc.numel() * kc.element_size() // kc.shape[0]
+    rows = list(w.decode_rows)
+    nblk = [-(-int(w.context_lens[s]) // w.block_size) for s in rows]
+    blocks = np.concatenate([w.block_tables[s, :n] for s, n in zip(rows, nblk)]).astype(np.int32)
+    for name, lst in (("table_order", blocks), ("physical_order", np.arange(kc.shape[0]))):
+        gb = torch.as_tensor(lst.astype(np.int32), device=dev)
+        ms = timed(lambda: pa.pa_ceiling_gather_read(kc, vc, gb, sink, W))
+        rec[f"block_read_{name}_GBps"] = round(2 * lst.size * block_bytes / (ms * 1e-3) / 1e9, 1)
+    rec["block_read_table_order_bytes"] = int(2 * blocks.size * block_bytes)
+    if want_mfma:
+        Wm, iters = cus * 2, 4000
+        fsink = torch.empty(4 * Wm, dtype=torch.float32, device=dev)
+        ms = timed(lambda: pa.pa_ceiling_mfma_bf16(fsink, Wm, iters))
+        rec["mfma_bf16_TFLOPs"] = round(Wm * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12, 1)
+    return rec
+
+
 def decode_kernel(w) -> str:
     """The split kernel pa_decode_partials launches for this workload's cache."""
     if w.block_size >= 16 and w.cache_dtype in ("bf16", "fp8", "int8", "int4"):
@@ -266,6 +313,9 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured-ceiling probes (contiguous read, block-order read, "
+                         "MFMA loop)")
     ap.add_argument("--two-call-append", action="store_true",
                     help="append through pa_slot_mapping + pa_kv_append[_int4] instead of the "
                          "one-launch pa_kv_append[_int4]_paged")
@@ -455,6 +505,25 @@ def main():
                 f"{t_min * 1e6:.1f} us (chunk flops at the MFMA peak + decode bytes at the HBM peak) "
                 f"= {t_min / (pf_avg * 1e-3):.1%} of the launch")
 
+    ceil = None
+    if not args.no_ceilings:
+        kc0, vc0, _ = pools[0]
+        ceil = measure_ceilings(w, dw, kc0, vc0, dev, want_mfma=bool(P))
+        tbl = ceil["block_read_table_order_GBps"]
+        msg = (f"measured ceilings: the decode rows' blocks read in table order {tbl:.0f} GB/s, "
+               f"the pools in physical order {ceil['block_read_physical_order_GBps']:.0f} GB/s")
+        if not one:
+            logical = bm["kv_logical"] / (split_avg * 1e-3) / 1e9
+            ceil["split_kernel_logical_GBps"] = round(logical, 1)
+            ceil["split_kernel_frac_of_table_order_read"] = round(logical / tbl, 4)
+            msg += f" (split kernel: {logical:.0f} GB/s of logical K/V = {logical / tbl:.1%} of the first)"
+        if "mfma_bf16_TFLOPs" in ceil:
+            msg += f", bf16 MFMA loop {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s"
+            if prefill_rec:
+                prefill_rec["frac_of_mfma_loop"] = round(
+                    prefill_rec["achieved"] / ceil["mfma_bf16_TFLOPs"], 4)
+        log(msg)
+
     cpu = None
     if int4 and not args.no_cpu_baseline:
         log("cpu baseline: not taken for the int4 cache")
@@ -509,6 +578,7 @@ def main():
             "algorithmic_bytes_per_launch": bm["split_kernel"],
         },
         "cpu_baseline": cpu,
+        "measured_ceilings": ceil,
     }
     if prefill_rec and not one:
         rec["prefill_roofline"] = prefill_rec

@@ -1,0 +1,111 @@
+// Measured ceilings of the device: what a kernel that only reads whole pool
+// blocks, or only issues matrix-core instructions, reaches on this GPU.  They
+// are the yardsticks the benchmark reports beside the published peaks (8 TB/s
+// HBM, 2.5 PFLOP/s dense bf16): a decode kernel is judged against what reading
+// the same blocks in the same order can reach (and in physical order, for the
+// cost of the order), the prefill kernel against what v_mfma_f32_32x32x16_bf16
+// can reach.  Not part of the attention path.
+//
+// Every reader folds what it reads into an XOR checksum that it writes out, so
+// the loads cannot be dropped and a test can check that exactly the intended
+// bytes were read.
+#include "pa_device.h"
+
+namespace pa {
+
+typedef uint32_t cu32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ cu32x4_t ld_nt16(const uint8_t* p) {
+  return __builtin_nontemporal_load((const cu32x4_t*)p);
+}
+
+__device__ __forceinline__ void reduce_xor_store(uint32_t x, uint32_t* sink) {
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  __shared__ uint32_t part[16];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r ^= part[i];
+    sink[blockIdx.x] = r;
+  }
+}
+
+// Whole blocks of two pools in list order: entry i of `blocks` names a block
+// of `block_bytes` bytes in k_pool and the same block in v_pool.  Workgroup w
+// reads an equal contiguous share of the list, each block as one run of
+// 16-byte loads (the order a paged decode reads its blocks in).
+__global__ __launch_bounds__(256) void ceiling_gather_kernel(
+    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+    const int32_t* __restrict__ blocks, int64_t n, int64_t pool_blocks, int block_bytes,
+    uint32_t* sink) {
+  const int64_t W = gridDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * n / W, i1 = (int64_t)(blockIdx.x + 1) * n / W;
+  const int per = block_bytes / 16;   // chunks per block
+  uint32_t x = 0;
+  for (int64_t i = i0; i < i1; ++i) {
+    int blk = uniform_load(blocks, (int)i);
+    blk = (uint64_t)(uint32_t)blk < (uint64_t)pool_blocks ? blk : 0;
+    const int64_t off = (int64_t)blk * block_bytes;
+#pragma unroll 4
+    for (int c = threadIdx.x; c < per; c += 256) {
+      const cu32x4_t a = ld_nt16(k_pool + off + 16 * c), b = ld_nt16(v_pool + off + 16 * c);
+      x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    }
+  }
+  reduce_xor_store(x, sink);
+}
+
+// Matrix-core issue rate: every wave runs `iters` rounds of 4 independent
+// v_mfma_f32_32x32x16_bf16 chains on register operands (A = B = 1.0), so each
+// accumulator element ends at 16 * iters.
+typedef __bf16 cbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float cf32x16_t __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256) void ceiling_mfma_kernel(int iters, float* sink) {
+  cbf16x8_t one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = (__bf16)1.0f;
+  cf32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one, one, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one, one, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one, one, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one, one, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  // every lane's sum is 64 * 16 * iters; one value per wave
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool,
+                                            int64_t pool_blocks, int32_t block_bytes,
+                                            const int32_t* blocks, int64_t n, uint32_t* sink,
+                                            int32_t num_wgs, void* stream) {
+  if (n < 0 || block_bytes < 16 || block_bytes % 16 != 0 || num_wgs < 1 || pool_blocks < 0 ||
+      n > 2147483647)
+    return PA_ERR_SHAPE;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !blocks || !sink) return PA_ERR_NULL;
+  if (pool_blocks == 0) return PA_ERR_SHAPE;
+  // entries outside [0, pool_blocks) read block 0
+  hipLaunchKernelGGL(ceiling_gather_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
+                     (hipStream_t)stream, (const uint8_t*)k_pool, (const uint8_t*)v_pool, blocks,
+                     n, pool_blocks, block_bytes, sink);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters,
+                                          void* stream) {
+  if (num_wgs < 1 || iters < 1) return PA_ERR_SHAPE;
+  if (!sink) return PA_ERR_NULL;
+  hipLaunchKernelGGL(ceiling_mfma_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
+                     (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
