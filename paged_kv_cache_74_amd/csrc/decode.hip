@@ -976,11 +976,14 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
   constexpr bool VDIRECT = STAGED && CDT == PA_BF16;
   uint32_t vrd[VDIRECT ? ML::NB : 1];
   if constexpr (VDIRECT) {
-    const int rc = a.hw * (ML::ROW / 16);
-    const int t = 4 * j + (r >> 2), w = t >> 1, u = ((r >> 1) & 1) ^ (t & 1);
+    constexpr int CPR = ML::ROW / 16;        // 16-byte chunks of one head's row
+    const int rc = a.hw * CPR;
+    const int t = 4 * j + (r >> 2);
 #pragma unroll
-    for (int b = 0; b < ML::NB; ++b)
-      vrd[b] = (uint32_t)(16 * (t * rc + wv * (ML::ROW / 16) + 2 * (b ^ w) + u) + 8 * (r & 1));
+    for (int b = 0; b < ML::NB; ++b) {
+      const int c = wv * CPR + 2 * b + ((r >> 1) & 1);   // chunk of bytes 32 b + 8 (r % 4)
+      vrd[b] = (uint32_t)(16 * (t * rc + (c ^ t)) + 8 * (r & 1));
+    }
   }
 
   auto step = [&](const uint32_t* fk, const uint32_t* fv, const float* fvs, int base,

@@ -288,3 +288,16 @@ def test_decode_stage_maps(hw, row):
                 for g in range(4):
                     banks = [table[(wv, lane, k)][1] % 16 for lane in range(16 * g, 16 * g + 16)]
                     assert len(set(banks)) == 16, (wv, k, g)
+    if row % 128 == 0:
+        # bf16 rows: the transposed V reads go to the stage directly.  Lane
+        # (j, r) of head wv, block b wants the 8 bytes at 32 b + 8 (r % 4) of
+        # token 4 j + r / 4's row: chunk 2 b + (r / 2) % 2, half r % 2.
+        cpr = row // 16
+        for wv in range(hw):
+            for lane in range(64):
+                j, r = lane >> 4, lane & 15
+                t = 4 * j + (r >> 2)
+                for b in range(row // 32):
+                    c = wv * cpr + 2 * b + ((r >> 1) & 1)
+                    pos = t * rc + (c ^ t)
+                    assert slots[pos] == (t, c), (wv, lane, b)

@@ -269,22 +269,22 @@ def test_decode_workspace_reuse(dev):
                 "split 48 after split 16 on one workspace")
 
 
-# (n_q, n_kv, head_dim, block_size) for the 8-bit caches: every group size, both
-# head dims, block sizes that take the matrix-core kernel (>= 16) and one that
-# takes the vector kernel; int8 on 8 x 2 x 64 loads per head, the other int8
-# matrix-core shapes stage their loads through LDS
+# (n_q, n_kv, head_dim, block_size) for the bf16 and 8-bit caches: every group
+# size, both head dims, block sizes that take the matrix-core kernel (>= 16) and
+# one that takes the vector kernel; int8 on 8 x 2 x 64 loads per head, the other
+# matrix-core shapes stage their loads through LDS (bf16 reading V from the stage)
 SHAPES_8BIT = [(8, 8, 128, 16), (8, 4, 64, 32), (16, 4, 128, 16), (32, 4, 64, 64),
                (16, 2, 128, 8), (8, 2, 64, 16)]
 
 
-@pytest.mark.parametrize("kv", ["int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES_8BIT)
-def test_decode_8bit_shapes(dev, kv, nq, nkv, hd, bs):
+def test_decode_shapes(dev, kv, nq, nkv, hd, bs):
     from gpu_harness import DeviceWorkload, to_f64
     rng = np.random.default_rng(nq * 7 + hd + bs)
     ctx = rng.integers(1, 900, 9).astype(np.int32)
     ctx[0] = 1
-    w = workloads._decode_workload("8bit-shapes", rng, ctx, nq, nkv, hd, bs, kv, "bf16", "bf16",
+    w = workloads._decode_workload("shapes", rng, ctx, nq, nkv, hd, bs, kv, "bf16", "bf16",
                                    seed=4)
     workloads.draw_values(w, "cpu")
     dw = DeviceWorkload(w, dev)
