@@ -272,9 +272,11 @@ def test_decode_workspace_reuse(dev):
 # (n_q, n_kv, head_dim, block_size) for the bf16 and 8-bit caches: every group
 # size, both head dims, block sizes that take the matrix-core kernel (>= 16) and
 # one that takes the vector kernel; int8 on 8 x 2 x 64 loads per head, the other
-# matrix-core shapes stage their loads through LDS (bf16 reading V from the stage)
+# matrix-core shapes stage their loads through LDS (bf16 reading V from the stage);
+# one KV head per workgroup: bf16 128 stages, bf16 64 and the 8-bit caches load per head
 SHAPES_8BIT = [(8, 8, 128, 16), (8, 4, 64, 32), (16, 4, 128, 16), (32, 4, 64, 64),
-               (16, 2, 128, 8), (8, 2, 64, 16)]
+               (16, 2, 128, 8), (8, 2, 64, 16), (32, 4, 128, 32), (8, 1, 128, 16),
+               (4, 1, 64, 16)]
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
