@@ -96,20 +96,24 @@ def source_hash(sources) -> str:
     return h.hexdigest()
 
 
-def timed(fn, reps: int = 5) -> float:
-    """Median milliseconds of fn() over reps launches (one warm-up), HIP events on the
-    current stream."""
+def timed(fn, reps: int = 3, burst: int = 8) -> float:
+    """Milliseconds per launch of fn(): the median over reps of a burst of back-to-back
+    launches between two HIP events on the current stream, divided by the burst (so the
+    host's launch overhead overlaps the GPU's work instead of being timed), after one
+    warm-up."""
     import numpy as np
     import torch
     fn()
     ts = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record()
-        fn()
+        for _ in range(burst):
+            fn()
         b.record()
         b.synchronize()
-        ts.append(a.elapsed_time(b))
+        ts.append(a.elapsed_time(b) / burst)
     return float(np.median(ts))
 
 
@@ -123,8 +127,7 @@ def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
 
     import paged_kv_cache_74_amd as pa
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    W = cus * 8
-    sink = torch.empty(W, dtype=torch.int32, device=dev)
+    sink = torch.empty(cus * 16 * 4, dtype=torch.int32, device=dev)
     rec = {}
     block_bytes = kc.numel() * kc.element_size() // kc.shape[0]
     rows = list(w.decode_rows)
@@ -132,9 +135,15 @@ def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
     blocks = np.concatenate([w.block_tables[s, :n] for s, n in zip(rows, nblk)]).astype(np.int32)
     for name, lst in (("table_order", blocks), ("physical_order", np.arange(kc.shape[0]))):
         gb = torch.as_tensor(lst.astype(np.int32), device=dev)
-        ms = timed(lambda: pa.pa_ceiling_gather_read(kc, vc, gb, sink, W))
+        # the best of 4, 8 and 16 workgroups per CU
+        ms = min(timed(lambda: pa.pa_ceiling_gather_read(kc, vc, gb, sink, W))
+                 for W in (cus * 4, cus * 8, cus * 16))
         rec[f"block_read_{name}_GBps"] = round(2 * lst.size * block_bytes / (ms * 1e-3) / 1e9, 1)
     rec["block_read_table_order_bytes"] = int(2 * blocks.size * block_bytes)
+    nbytes = kc.numel() * kc.element_size()
+    ms = min(timed(lambda: pa.pa_ceiling_stream_read(kc, sink, W))
+             for W in (cus * 4, cus * 8, cus * 16))
+    rec["contiguous_read_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     if want_mfma:
         Wm, iters = cus * 2, 4000
         fsink = torch.empty(4 * Wm, dtype=torch.float32, device=dev)
@@ -511,7 +520,8 @@ def main():
         ceil = measure_ceilings(w, dw, kc0, vc0, dev, want_mfma=bool(P))
         tbl = ceil["block_read_table_order_GBps"]
         msg = (f"measured ceilings: the decode rows' blocks read in table order {tbl:.0f} GB/s, "
-               f"the pools in physical order {ceil['block_read_physical_order_GBps']:.0f} GB/s")
+               f"the pools in physical order {ceil['block_read_physical_order_GBps']:.0f} GB/s, "
+               f"the K pool as one contiguous read {ceil['contiguous_read_GBps']:.0f} GB/s")
         if not one:
             logical = bm["kv_logical"] / (split_avg * 1e-3) / 1e9
             ceil["split_kernel_logical_GBps"] = round(logical, 1)

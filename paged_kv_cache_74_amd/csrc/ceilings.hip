@@ -19,17 +19,32 @@ __device__ __forceinline__ cu32x4_t ld_nt16(const uint8_t* p) {
   return __builtin_nontemporal_load((const cu32x4_t*)p);
 }
 
+// One XOR per wave, no workgroup barrier: sink[workgroup * 4 + wave].
 __device__ __forceinline__ void reduce_xor_store(uint32_t x, uint32_t* sink) {
   for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
-  __shared__ uint32_t part[16];
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) part[wv] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = 0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r ^= part[i];
-    sink[blockIdx.x] = r;
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
+// Contiguous read of `chunks` 16-byte chunks: workgroup w reads an equal
+// contiguous share, 8 loads in flight per lane.
+__global__ __launch_bounds__(256) void ceiling_stream_kernel(const uint8_t* __restrict__ buf,
+                                                             int64_t chunks, uint32_t* sink) {
+  const int64_t W = gridDim.x;
+  const int64_t c0 = (int64_t)blockIdx.x * chunks / W, c1 = (int64_t)(blockIdx.x + 1) * chunks / W;
+  uint32_t x = 0;
+  int64_t c = c0 + threadIdx.x;
+  for (; c + 7 * 256 < c1; c += 8 * 256) {
+    cu32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld_nt16(buf + 16 * (c + 256 * u));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
+  for (; c < c1; c += 256) {
+    const cu32x4_t a = ld_nt16(buf + 16 * c);
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  reduce_xor_store(x, sink);
 }
 
 // Whole blocks of two pools in list order: entry i of `blocks` names a block
@@ -44,11 +59,14 @@ __global__ __launch_bounds__(256) void ceiling_gather_kernel(
   const int64_t i0 = (int64_t)blockIdx.x * n / W, i1 = (int64_t)(blockIdx.x + 1) * n / W;
   const int per = block_bytes / 16;   // chunks per block
   uint32_t x = 0;
+  // the next block id is read while the current block streams in
+  int nxt = i0 < i1 ? uniform_load(blocks, (int)i0) : 0;
   for (int64_t i = i0; i < i1; ++i) {
-    int blk = uniform_load(blocks, (int)i);
+    int blk = nxt;
+    nxt = uniform_load(blocks, (int)min(i + 1, i1 - 1));
     blk = (uint64_t)(uint32_t)blk < (uint64_t)pool_blocks ? blk : 0;
     const int64_t off = (int64_t)blk * block_bytes;
-#pragma unroll 4
+#pragma unroll 8
     for (int c = threadIdx.x; c < per; c += 256) {
       const cu32x4_t a = ld_nt16(k_pool + off + 16 * c), b = ld_nt16(v_pool + off + 16 * c);
       x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
@@ -83,6 +101,16 @@ __global__ __launch_bounds__(256) void ceiling_mfma_kernel(int iters, float* sin
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
+                                            int32_t num_wgs, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || num_wgs < 1) return PA_ERR_SHAPE;
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return PA_ERR_NULL;
+  hipLaunchKernelGGL(ceiling_stream_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
+                     (hipStream_t)stream, (const uint8_t*)buf, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
 
 extern "C" pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool,
                                             int64_t pool_blocks, int32_t block_bytes,

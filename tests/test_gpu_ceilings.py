@@ -23,6 +23,18 @@ def _xor(a: np.ndarray) -> int:
     return int(np.bitwise_xor.reduce(a.view(np.uint32).ravel()))
 
 
+@pytest.mark.parametrize("nbytes,wgs", [(16, 1), (10_000_048, 37), (64 << 20, 2048)])
+def test_stream_read_reads_every_word_once(dev, nbytes, wgs):
+    import paged_kv_cache_74_amd as pa
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.as_tensor(host.view(np.int32), device=dev)
+    sink = torch.zeros(4 * wgs, dtype=torch.int32, device=dev)
+    pa.pa_ceiling_stream_read(buf, sink, wgs)
+    torch.cuda.synchronize()
+    assert _xor(sink.cpu().numpy()) == _xor(host)
+
+
 def test_gather_read_reads_the_listed_blocks(dev):
     import paged_kv_cache_74_amd as pa
     rng = np.random.default_rng(3)
@@ -37,7 +49,7 @@ def test_gather_read_reads_the_listed_blocks(dev):
         want ^= _xor(k[b]) ^ _xor(v[b])
     gk = torch.as_tensor(k.view(np.int32), device=dev)
     gv = torch.as_tensor(v.view(np.int32), device=dev)
-    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4 * 64, dtype=torch.int32, device=dev)
     pa.pa_ceiling_gather_read(gk, gv, torch.as_tensor(blocks, device=dev), sink, 64)
     torch.cuda.synchronize()
     assert _xor(sink.cpu().numpy()) == want
