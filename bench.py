@@ -500,7 +500,10 @@ def main():
                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                        "traffic": measured_traffic(args.workload + ("-one" if one else ""),
                                                    "prefill_kernel", PREFILL_SOURCES),
-                       "avg_launch_us": round(pf_avg * 1e3, 2), "flops_per_launch": fl}
+                       "avg_launch_us": round(pf_avg * 1e3, 2),
+                       "launch_us_p10_p50_p90": [round(float(np.percentile(prefill_ms, q)) * 1e3, 2)
+                                                 for q in (10, 50, 90)],
+                       "flops_per_launch": fl}
         log(f"prefill avg {pf_avg * 1e3:.1f} us -> {tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
             f"of the bf16 MFMA peak ({fl / 1e9:.1f} GFLOP)")
         if one:
@@ -585,6 +588,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.workload, decode_kernel(w), DECODE_SOURCES),
             "avg_launch_us": round(split_avg * 1e3, 2),
+            "launch_us_p10_p50_p90": [round(float(np.percentile(split_ms, q)) * 1e3, 2)
+                                      for q in (10, 50, 90)],
             "algorithmic_bytes_per_launch": bm["split_kernel"],
         },
         "cpu_baseline": cpu,
