@@ -1015,12 +1015,12 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
       const float alpha = fast_exp2(m - mn);
       m = mn;
       lp *= alpha;
+      // rows 4j+i of O belong to head column 4j+i; whole-vector products keep
+      // each accumulator one register tuple
+      const mf_f32x4_t av = {__shfl(alpha, 4 * j + 0, 64), __shfl(alpha, 4 * j + 1, 64),
+                             __shfl(alpha, 4 * j + 2, 64), __shfl(alpha, 4 * j + 3, 64)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {      // rows 4j+i of O belong to head column 4j+i
-        const float ai = __shfl(alpha, 4 * j + i, 64);
-#pragma unroll
-        for (int b = 0; b < ML::NB; ++b) acc[b][i] *= ai;
-      }
+      for (int b = 0; b < ML::NB; ++b) acc[b] *= av;
     }
     float p[4];
 #pragma unroll
