@@ -254,6 +254,8 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *                 left unwritten and nothing outside the arguments is touched.
  *   cache_dtype   BF16, FP8_E4M3 or INT8 (codes times k_scale / v_scale)
  *   head_dim      64 or 128; block_size a power of two in [1, 256];
+ *                 block_size * n_kv_heads * head_dim * 2 below 2^31 (a block's
+ *                 rows are addressed with 32-bit offsets), else PA_ERR_SHAPE
  *   group_size    1, 2, 4 or 8
  *   scale         positive and finite, else PA_ERR_SHAPE
  *   workspace     at least pa_prefill_workspace_bytes(...) bytes (may be NULL if 0)

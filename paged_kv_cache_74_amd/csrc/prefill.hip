@@ -25,13 +25,15 @@
 //   * O^T = V^T P^T: the probability registers of the score tile are already
 //     the B operand of the PV MFMA (the key order inside a 16-key slice is
 //     permuted consistently in both operands); only V is stored transposed in
-//     LDS, written as bf16 pairs of two keys.  The row paddings of the K and
+//     LDS, written as bf16 pairs of keys x and x + 16.  The row paddings of the K and
 //     V^T buffers, with loader lanes ordered key pair first, keep the LDS
 //     stores and operand reads free of bank conflicts.
-//   * The scale multiplies the scores inside the exponent (one FMA); row maxima
-//     are taken on the raw scores.  The running max moves only when a row's
-//     tile max exceeds it by more than PF_SLACK (base-2 units), so O is
-//     rescaled rarely; the result does not depend on which max is used.
+//   * The scale multiplies the scores inside the exponent (one FMA).  The
+//     weights are taken against the running max without looking for the
+//     tile's max first; only when a lane's weights of a 16-key slice add up to
+//     more than 2^PF_LOG2_TSUM does the max move (to the row's max over the
+//     slice, taken on the raw scores), O get rescaled and the slice's weights get taken
+//     again.  The result does not depend on which max is used.
 //   * Work is balanced like the decode kernel: a unit is one 32-key tile of one
 //     segment (sequence, KV head, 128-row query tile); each resident workgroup
 //     takes an equal contiguous range of units, and segments split between
@@ -54,7 +56,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int PF_WAVES = 4;
 constexpr int PF_ROWS = 32 * PF_WAVES;   // query rows per workgroup
 constexpr int PF_BN = 32;                // keys per tile
-constexpr float PF_SLACK = 8.0f;
+constexpr int PF_LOG2_TSUM = 12;
+constexpr float PF_TSUM_MAX = (float)(1 << PF_LOG2_TSUM);
 
 struct PrefillArgs {
   const uint8_t* q;          // [total_q][n_q][HD] bf16
@@ -268,8 +271,8 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
   }
 }
 
-// K/V element rows of one tile for this thread: keys key0, key0 + 1, chunk lc
-// (and, for INT4, the two keys' value scales).
+// K/V element rows of one tile for this thread: keys x and x + 16 of the tile,
+// chunk lc (and, for INT4, the two keys' value scales).
 struct TileRegs {
   uint32_t k0[4], k1[4], v0[4], v1[4];
   float s0, s1;
@@ -296,6 +299,27 @@ __device__ __forceinline__ void load8(const uint8_t* p, uint32_t (&d)[4]) {
     d[0] = *(const uint32_t*)p; d[1] = 0u; d[2] = 0u; d[3] = 0u;
   } else {   // 8-bit codes: keep the raw bytes, widened when stored to LDS
     const uint2 x = *(const uint2*)p;
+    d[0] = x.x; d[1] = x.y; d[2] = 0u; d[3] = 0u;
+  }
+}
+
+// The same through a buffer descriptor: a wave-uniform base in scalar
+// registers plus a 32-bit lane offset, so no 64-bit lane address is built.
+typedef uint32_t pf_u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t pf_u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  // 4th descriptor word for the gfx9 family: 32-bit data format, raw addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <int CDT>
+__device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&d)[4]) {
+  if constexpr (CDT == PA_BF16) {
+    const pf_u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+  } else if constexpr (CDT == PA_INT4) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); d[1] = 0u; d[2] = 0u; d[3] = 0u;
+  } else {
+    const pf_u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     d[0] = x.x; d[1] = x.y; d[2] = 0u; d[3] = 0u;
   }
 }
@@ -390,72 +414,103 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   float m = -1e30f, lsum = 0.0f;
   const float c = a.score_scale;
 
-  // thread -> (key pair, 8-element chunk), key pair fastest: the 16 lanes that
-  // share a chunk write 16 different key pairs of the same V^T rows, which
-  // with the row paddings above keeps every LDS store and operand read free of
-  // bank conflicts.  With head_dim 64 the upper half of the workgroup repeats
-  // the lower half's loads and (identical) LDS stores, so no branch separates
-  // loading threads and the wait counts stay exact
+  // thread -> (key pair, 8-element chunk), key pair fastest.  Pair x holds
+  // keys x and x + 16 of the tile: with blocks of 16 tokens the two keys lie
+  // in the two blocks the tile spans, at the same offset, so each load
+  // instruction reads one block (a scalar base plus a 32-bit lane offset that
+  // does not change from tile to tile).  V^T stores pair x as one bf16 pair at
+  // byte 4x of a dim row; the 16 lanes that share a chunk write 16 different
+  // pairs of the same rows, which with the row paddings above keeps every LDS
+  // store and operand read free of bank conflicts.  With head_dim 64 the upper
+  // half of the workgroup repeats the lower half's loads and (identical) LDS
+  // stores, so no branch separates loading threads and the wait counts stay
+  // exact
   const int lp = tid % (PF_BN / 2);
   const int lc = (tid / (PF_BN / 2)) % CHUNKS;
   constexpr bool loader = true;
   const int64_t col = (int64_t)kvh * ROWB + lc * EBITS;   // 8 elements of EBITS bits
+  // blocks of 16 tokens or more: byte offset of key x inside its block's rows
+  const uint32_t lane_off = (uint32_t)(lp * a.tok_stride + col);
+  const int64_t blk_bytes = (int64_t)a.block_size * a.tok_stride;
 
   const int jmax = min((T - 1) >> a.bs_log2, a.max_blocks - 1);
   auto gload = [&](int t, TileRegs& R) {
-    // block_size >= 16: the tile spans at most two blocks; their table entries
-    // are read wave-uniformly (scalar loads, which do not wait behind the K/V
-    // loads in flight; a vector load of both entries issued a tile ahead, with
-    // the K/V loads, measured 7% slower)
-    int jlo = 0, blo = 0, bhi = 0;
     if (a.block_size >= 16) {
-      jlo = min((t * PF_BN) >> a.bs_log2, jmax);
-      const int jhi = min(jlo + 1, jmax);
-      blo = uniform_load(table, jlo);
-      bhi = uniform_load(table, jhi);
+      // the tile spans at most two blocks; their table entries are read
+      // wave-uniformly (scalar loads, which do not wait behind the K/V loads
+      // in flight; a vector load of both entries issued a tile ahead, with the
+      // K/V loads, measured 7% slower).  Keys past the context read stale
+      // rows of the last block (never outside it): their scores are masked
+      // and their V rows zeroed when stored
+      const int jlo = min((t * PF_BN) >> a.bs_log2, jmax);
+      int blo = uniform_load(table, jlo);
       blo = (unsigned)blo < (unsigned)a.num_blocks ? blo : 0;
-      bhi = (unsigned)bhi < (unsigned)a.num_blocks ? bhi : 0;
-    }
-    if (loader) {
-      const int key0 = t * PF_BN + 2 * lp;
-      int64_t tk0, tk1;   // pool token indices of the two keys
-      if (a.block_size >= 16) {
-        const int k0c = min(key0, T - 1), k1c = min(key0 + 1, T - 1);
-        const int b0 = (k0c >> a.bs_log2) == jlo ? blo : bhi;
-        const int b1 = (k1c >> a.bs_log2) == jlo ? blo : bhi;
-        tk0 = (int64_t)b0 * a.block_size + (k0c & (a.block_size - 1));
-        tk1 = (int64_t)b1 * a.block_size + (k1c & (a.block_size - 1));
-      } else {
-        tk0 = token_index(a, table, key0, T);
-        tk1 = token_index(a, table, key0 + 1, T);
+      const int inb = (t * PF_BN) & (a.block_size - 1);   // first key's offset in its block
+      int b1 = blo, inb1 = inb + 16;                        // block and offset of key 16
+      if (a.block_size == 16) {
+        b1 = uniform_load(table, min(jlo + 1, jmax));
+        b1 = (unsigned)b1 < (unsigned)a.num_blocks ? b1 : 0;
+        inb1 = 0;
       }
+      const int64_t off0 = blo * blk_bytes + inb * a.tok_stride;
+      const int64_t off1 = b1 * blk_bytes + inb1 * a.tok_stride;
+      const int32_t nb0 = (int32_t)(blk_bytes - inb * a.tok_stride);
+      const int32_t nb1 = (int32_t)(blk_bytes - inb1 * a.tok_stride);
+      load8_buf<CDT>(make_rsrc(a.k_cache + off0, nb0), lane_off, R.k0);
+      load8_buf<CDT>(make_rsrc(a.k_cache + off1, nb1), lane_off, R.k1);
+      load8_buf<CDT>(make_rsrc(a.v_cache + off0, nb0), lane_off, R.v0);
+      load8_buf<CDT>(make_rsrc(a.v_cache + off1, nb1), lane_off, R.v1);
+      if constexpr (CDT == PA_INT4) {   // the two keys' value scales ([block][head][offset])
+        const float* vs = a.v_tok_scale + (int64_t)kvh * a.block_size + lp;
+        const int64_t hb = (int64_t)a.n_kv * a.block_size;
+        R.s0 = vs[blo * hb + inb];
+        R.s1 = vs[b1 * hb + inb1];
+      }
+    } else {
+      // smaller blocks: each key through its own table entry, clamped into
+      // the context, so every load lands on a real token
+      const int64_t tk0 = token_index(a, table, t * PF_BN + lp, T);
+      const int64_t tk1 = token_index(a, table, t * PF_BN + lp + 16, T);
       const int64_t o0 = tk0 * a.tok_stride + col, o1 = tk1 * a.tok_stride + col;
       load8<CDT>(a.k_cache + o0, R.k0);
       load8<CDT>(a.k_cache + o1, R.k1);
       load8<CDT>(a.v_cache + o0, R.v0);
       load8<CDT>(a.v_cache + o1, R.v1);
-      if constexpr (CDT == PA_INT4) {   // the two keys' value scales ([block][head][offset])
-        R.s0 = a.v_tok_scale[((tk0 >> a.bs_log2) * a.n_kv + kvh) * a.block_size +
-                             (tk0 & (a.block_size - 1))];
-        R.s1 = a.v_tok_scale[((tk1 >> a.bs_log2) * a.n_kv + kvh) * a.block_size +
-                             (tk1 & (a.block_size - 1))];
+      if constexpr (CDT == PA_INT4) {
+        R.s0 = a.v_tok_scale[((tk0 >> a.bs_log2) * a.n_kv + kvh) * a.block_size + (tk0 & (a.block_size - 1))];
+        R.s1 = a.v_tok_scale[((tk1 >> a.bs_log2) * a.n_kv + kvh) * a.block_size + (tk1 & (a.block_size - 1))];
       }
     }
   };
-  auto sstore = [&](TileRegs& R, uint8_t* buf) {
+  auto sstore = [&](TileRegs& R, uint8_t* buf, int t) {
     if (loader) {
       widen<CDT>(R.k0); widen<CDT>(R.k1); widen<CDT>(R.v0); widen<CDT>(R.v1);
+      if (t * PF_BN + PF_BN > T) {
+        // the context ends inside this tile: keys past it hold stale rows,
+        // whose weight is 0; their V (and INT4 value scale) must be finite
+        const bool z0 = t * PF_BN + lp >= T, z1 = t * PF_BN + lp + 16 >= T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          R.v0[i] = z0 ? 0u : R.v0[i];
+          R.v1[i] = z1 ? 0u : R.v1[i];
+        }
+        if constexpr (CDT == PA_INT4) {
+          R.s0 = z0 ? 0.0f : R.s0;
+          R.s1 = z1 ? 0.0f : R.s1;
+        }
+      }
       uint8_t* lk = buf;
       uint8_t* lv = buf + LD::K_BYTES;
-      *(uint4*)(lk + (2 * lp) * LD::KROW + lc * 16) = make_uint4(R.k0[0], R.k0[1], R.k0[2], R.k0[3]);
-      *(uint4*)(lk + (2 * lp + 1) * LD::KROW + lc * 16) = make_uint4(R.k1[0], R.k1[1], R.k1[2], R.k1[3]);
+      *(uint4*)(lk + lp * LD::KROW + lc * 16) = make_uint4(R.k0[0], R.k0[1], R.k0[2], R.k0[3]);
+      *(uint4*)(lk + (lp + 16) * LD::KROW + lc * 16) = make_uint4(R.k1[0], R.k1[1], R.k1[2], R.k1[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {   // V^T[d][key0, key0 + 1] as bf16 pairs
+      for (int i = 0; i < 4; ++i) {   // V^T[d][x, x + 16] as bf16 pairs
         const int dl = lc * 8 + widened_elem<CDT>(i, false);
         const int dh = lc * 8 + widened_elem<CDT>(i, true);
         *(uint32_t*)(lv + dl * LD::VROW + 4 * lp) = pair_lo(R.v0[i], R.v1[i]);
         *(uint32_t*)(lv + dh * LD::VROW + 4 * lp) = pair_hi(R.v0[i], R.v1[i]);
       }
+      // INT4 value scales in pair order: (sigma[x], sigma[x + 16]) at byte 8x
       if constexpr (CDT == PA_INT4)
         if (lc == 0) *(float2*)(buf + LD::K_BYTES + LD::V_BYTES + 8 * lp) = make_float2(R.s0, R.s1);
     }
@@ -486,53 +541,68 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) <= lim ? sc[r] : -INFINITY;
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[r]);
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    // The running max only moves when some row's tile max exceeds it by more
-    // than PF_SLACK (base-2 units): the weights 2^(s - m) then stay below
-    // 2^PF_SLACK, exact in bf16 and fp32, and the rescale of O is rare.
-    const float mt = tmax * c;
-    if (__any(mt > m + PF_SLACK)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-      m = mn;
-    }
-    // INT4: the value scales of this lane's 16 keys (key 4 grp + 8 q + e of the tile)
+    // INT4: the value scales of this lane's keys in pair order: sg[8 s + 2 i]
+    // and sg[8 s + 2 i + 1] belong to keys 8 s + 4 grp + i and that + 16
     float sg[16];
     if constexpr (CDT == PA_INT4) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 x = *(const float4*)(buf + LD::K_BYTES + LD::V_BYTES + 4 * (4 * grp + 8 * q));
+        const float4 x = *(const float4*)(buf + LD::K_BYTES + LD::V_BYTES + 32 * grp + 64 * (q >> 1) + 16 * (q & 1));
         sg[4 * q] = x.x; sg[4 * q + 1] = x.y; sg[4 * q + 2] = x.z; sg[4 * q + 3] = x.w;
       }
     }
-    // O^T += V^T P^T; k index (grp, e) of slice t <-> key 16t + 8(e/4) + 4 grp + e%4
+    // O^T += V^T P^T over two 16-key slices.  Score r of this lane is key
+    // 4 grp + 8 (r / 4) + r % 4; slice s pairs score r = 4 s + i with r + 8
+    // (keys x and x + 16, x = 8 s + 4 grp + i), the pair order of V^T in LDS.
+    //
+    // The weights are taken against the running max m without first finding
+    // the tile's max.  m moves only when the weights of a slice of some lane
+    // add up to more than 2^PF_LOG2_TSUM (always so on a segment's first tile,
+    // where m starts far below every score): then it moves to the row's max
+    // over the slice, O and l are rescaled and the slice's weights taken
+    // again.  Otherwise every weight 2^(s c - m) is at most 2^PF_LOG2_TSUM,
+    // so O and l stay far from overflow, and O / l does not depend on which
+    // m was used.
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < 2; ++s) {
       uint32_t P[4];
+      float ts;
+      auto weights = [&]() {
+        ts = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i], c, -m));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[8 * t + 2 * i + 1], c, -m));
-        if constexpr (CDT == PA_INT4) {   // value scale into the weight; l unscaled, fp32
-          P[i] = pack_bf16(p0 * sg[8 * t + 2 * i], p1 * sg[8 * t + 2 * i + 1]);
-          lsum += p0 + p1;
-        } else {
-          P[i] = pack_bf16(p0, p1);
-          lsum = dot2_bf16(P[i], 0x3F803F80u, lsum);
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(sc[4 * s + i], c, -m));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[4 * s + i + 8], c, -m));
+          if constexpr (CDT == PA_INT4) {   // value scale into the weight; l unscaled, fp32
+            P[i] = pack_bf16(p0 * sg[8 * s + 2 * i], p1 * sg[8 * s + 2 * i + 1]);
+            ts += p0 + p1;
+          } else {
+            P[i] = pack_bf16(p0, p1);
+            ts = dot2_bf16(P[i], 0x3F803F80u, ts);
+          }
         }
+      };
+      weights();
+      if (__any(!(ts <= PF_TSUM_MAX))) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, fmaxf(sc[4 * s + i], sc[4 * s + i + 8]));
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        const float mn = fmaxf(m, tmax * c);
+        const float alpha = fast_exp2(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        m = mn;
+        weights();
       }
+      lsum += ts;
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(P[0], P[1], P[2], P[3]));
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW;
-        const uint2 lo = *(const uint2*)(vrow + (16 * t + 4 * grp) * 2);
-        const uint2 hi = *(const uint2*)(vrow + (16 * t + 8 + 4 * grp) * 2);
+      for (int dt = 0; dt < NDT; ++dt) {   // V^T pairs x = 8 s + 4 grp .. + 3 of dim row 32 dt + lr
+        const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW + 32 * s + 16 * grp;
+        const uint2 lo = *(const uint2*)vrow;
+        const uint2 hi = *(const uint2*)(vrow + 8);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[dt], 0, 0, 0);
       }
@@ -548,7 +618,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   gload(t0, R0);
   int boff = 0;
   auto tile = [&](int t, auto masked) {
-    sstore(R0, lds + boff);
+    sstore(R0, lds + boff, t);
     gload(min(t + 1, t1 - 1), R0);
     __syncthreads();
     if (wave_ok) compute(lds + boff, t, masked);
@@ -810,6 +880,8 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   const PfLayout l =
       pf_layout(num_seqs, nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
+  // a block's rows are addressed with 32-bit offsets
+  if ((int64_t)block_size * n_kv_heads * head_dim * 2 >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
   PrefillArgs a;
   a.q = (const uint8_t*)q;
   a.out = out;
