@@ -202,7 +202,8 @@ def test_int4_prefill(dev, causal):
     _prefill_int4_vs_oracle(w, dev, f"int4 prefill causal={causal}", causal=causal)
 
 
-@pytest.mark.parametrize("nq,nkv,hd,bs", [(8, 4, 64, 16), (16, 2, 128, 32), (8, 1, 128, 1)])
+@pytest.mark.parametrize("nq,nkv,hd,bs", [(8, 4, 64, 16), (16, 2, 128, 32), (8, 1, 128, 1),
+                                            (8, 2, 128, 128)])
 def test_int4_prefill_shapes(dev, nq, nkv, hd, bs):
     w = workloads.mixed_prefill_decode(prior=(0, 40, 300, 1), chunk_lens=(50, 130, 33, 1),
                                        n_decode=2, dlo=1, dhi=90, seed=7, n_q=nq, n_kv=nkv,
