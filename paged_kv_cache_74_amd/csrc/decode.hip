@@ -452,12 +452,19 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int steps_of(int ctx) { return ctx > 0 ? (ctx + 15) >> 4 : 0; }
 
+// Both quotients are taken in double precision instead of 64-bit integer
+// division (a long scalar sequence, on the merge kernel's critical path).  They
+// are exact: with U < 2^31 units and W <= 2^20 workgroups the numerators are
+// below 2^53 (exact doubles), and a quotient that is not an integer lies at
+// least 1/W (1/U) from the next integer, more than the rounding error of the
+// division (half an ulp of a quotient below 2^31 (2^20), at most 2^-23
+// (2^-33)), so the floor of the rounded quotient is the integer quotient.
 __device__ __forceinline__ int64_t wave_begin(int w, int64_t U, int W) {
-  return (int64_t)w * U / W;
+  return (int64_t)__builtin_floor((double)w * (double)U / (double)W);
 }
 // the wave whose unit range holds unit x (0 <= x < U)
 __device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
-  return (int)(((x + 1) * W - 1) / U);
+  return (int)__builtin_floor(((double)(x + 1) * (double)W - 1.0) / (double)U);
 }
 
 // Units of the sequences before `s` (pre) and in total (all), one pass of the
@@ -1274,11 +1281,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     auto entry = [&](int w) -> int64_t { return (((int64_t)w + g) * hw + wv) * G + hl; };
     auto piece_ml = [&](int b, bool* has) -> float2 {
       const int w = w0 + b + t;
-      *has = w <= w1 && wave_begin(w, U, num_wgs) < wave_begin(w + 1, U, num_wgs);
+      // with at least as many units as workgroups every workgroup holds a piece
+      *has = w <= w1 && (U >= num_wgs || wave_begin(w, U, num_wgs) < wave_begin(w + 1, U, num_wgs));
       return *has ? *(const float2*)(part_ml + entry(w) * 2) : make_float2(-INFINITY, 0.0f);
     };
     bool has0;
     const float2 ml0 = piece_ml(0, &has0);
+    // the first four pieces' O go out with the (m, l) loads: they do not
+    // depend on M, and most rows have no more pieces than that
+    const uint64_t present0 = __ballot(has0);
+    float o0[4][DPT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t sl = entry((present0 >> u) & 1 ? w0 + u : w0);
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) o0[u][i] = part_o[sl * HD + t * DPT + i];
+    }
     float M = ml0.x;
     for (int b = 64; b < npc; b += 64) {
       bool has;
@@ -1300,7 +1318,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
         for (int u = 0; u < 4; ++u) {
           const int64_t sl = entry((present >> (j + u)) & 1 ? w0 + b + j + u : w0);
 #pragma unroll
-          for (int i = 0; i < DPT; ++i) o[u][i] = part_o[sl * HD + t * DPT + i];
+          for (int i = 0; i < DPT; ++i)
+            o[u][i] = b + j == 0 ? o0[u][i] : part_o[sl * HD + t * DPT + i];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {

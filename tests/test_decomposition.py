@@ -301,3 +301,27 @@ def test_decode_stage_maps(hw, row):
                     c = wv * cpr + 2 * b + ((r >> 1) & 1)
                     pos = t * rc + (c ^ t)
                     assert slots[pos] == (t, c), (wv, lane, b)
+
+
+def test_decode_split_quotients_in_double_are_exact():
+    """The decode kernels take floor(w U / W) and floor(((x + 1) W - 1) / U) in
+    IEEE double precision (a correctly rounded division, then floor).  Check
+    that this equals the integer quotient over the whole supported range: up to
+    2^31 - 1 units and 2^20 workgroups, at the extremes and at random."""
+    import numpy as np
+
+    rng = np.random.default_rng(0)
+    W_MAX, U_MAX = 1 << 20, (1 << 31) - 1
+    Us = np.concatenate([[1, 2, 3, W_MAX - 1, W_MAX, W_MAX + 1, U_MAX - 1, U_MAX],
+                         rng.integers(1, U_MAX, 4000, endpoint=True)]).astype(np.int64)
+    Ws = np.concatenate([[1, 2, 255, 256, 768, W_MAX - 1, W_MAX, 7, W_MAX, 3],
+                         rng.integers(1, W_MAX, 3998, endpoint=True)]).astype(np.int64)
+    for U, W in zip(Us, Ws):
+        ws = np.unique(np.concatenate([[0, 1, W - 1, W], rng.integers(0, W, 64, endpoint=True)]))
+        got = np.floor(ws.astype(np.float64) * float(U) / float(W)).astype(np.int64)
+        want = np.array([int(w) * int(U) // int(W) for w in ws], dtype=np.int64)
+        assert np.array_equal(got, want), (U, W)
+        xs = np.unique(np.concatenate([[0, U - 1], rng.integers(0, U - 1, 64, endpoint=True)]))
+        got = np.floor(((xs + 1).astype(np.float64) * float(W) - 1.0) / float(U)).astype(np.int64)
+        want = np.array([((int(x) + 1) * int(W) - 1) // int(U) for x in xs], dtype=np.int64)
+        assert np.array_equal(got, want), (U, W)
