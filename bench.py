@@ -125,7 +125,7 @@ def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
     import numpy as np
     import torch
 
-    import paged_kv_cache_74_amd as pa
+    from paged_kv_cache_74_amd import probes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(cus * 16 * 4, dtype=torch.int32, device=dev)
     rec = {}
@@ -136,18 +136,18 @@ def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
     for name, lst in (("table_order", blocks), ("physical_order", np.arange(kc.shape[0]))):
         gb = torch.as_tensor(lst.astype(np.int32), device=dev)
         # the best of 4, 8 and 16 workgroups per CU
-        ms = min(timed(lambda: pa.pa_ceiling_gather_read(kc, vc, gb, sink, W))
+        ms = min(timed(lambda: probes.pa_ceiling_gather_read(kc, vc, gb, sink, W))
                  for W in (cus * 4, cus * 8, cus * 16))
         rec[f"block_read_{name}_GBps"] = round(2 * lst.size * block_bytes / (ms * 1e-3) / 1e9, 1)
     rec["block_read_table_order_bytes"] = int(2 * blocks.size * block_bytes)
     nbytes = kc.numel() * kc.element_size()
-    ms = min(timed(lambda: pa.pa_ceiling_stream_read(kc, sink, W))
+    ms = min(timed(lambda: probes.pa_ceiling_stream_read(kc, sink, W))
              for W in (cus * 4, cus * 8, cus * 16))
     rec["contiguous_read_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     if want_mfma:
         Wm, iters = cus * 2, 4000
         fsink = torch.empty(4 * Wm, dtype=torch.float32, device=dev)
-        ms = timed(lambda: pa.pa_ceiling_mfma_bf16(fsink, Wm, iters))
+        ms = timed(lambda: probes.pa_ceiling_mfma_bf16(fsink, Wm, iters))
         rec["mfma_bf16_TFLOPs"] = round(Wm * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12, 1)
     return rec
 
@@ -173,66 +173,178 @@ def measured_traffic(workload: str, kernel: str, sources):
     return r["fetch_kib"] * r["fetch_scale"] * 1024 + r["write_kib"] * r["write_scale"] * 1024
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle, as it is, on a bounded sample of the same step (host cores)."""
+def _oracle_worker(job):
+    """One host core's share of the oracle baseline (runs in a spawned process with one
+    BLAS thread): for each task, build the oracle pools it reads (setup, not timed),
+    then time the oracle on it, until the timed total reaches the budget.
+
+    Tasks: ("decode", s) -- slot map + append of sequence s's new token + decode of s;
+    ("prefill", s, i) -- chunk s's query row i as a chunk of its own (its causal
+    context).  Returns {kind: [seconds, bytes, flops, count]}."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle
-    from tests.helpers import codes
+    w, files, tasks, budget_s = job
+    a = {k: np.load(f, mmap_mode="r") for k, f in files.items()}
+    paged = oracle.paged
+    src, cdt, bs = w.src_dtype, w.cache_dtype, w.block_size
+    int4 = cdt == "int4"
+    hd_store = w.head_dim // 2 if int4 else w.head_dim
+    dt = {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8, "int8": np.uint8,
+          "int4": np.uint8}[cdt]
+    shape = (w.num_blocks, bs, w.n_kv_heads, hd_store)
+    pk, pv = np.zeros(shape, dt), np.zeros(shape, dt)          # pages touched on demand
+    ps = np.zeros((w.num_blocks, w.n_kv_heads, bs), np.float32) if int4 else None
+    res_cu, new_cu, q_cu = w.cu(w.res_len), w.cu(w.new_len), w.cu(w.q_lens)
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}[cdt]
+    tok_head = w.head_dim * 2 * eb + (4 if int4 else 0)
 
-    rows = list(w.decode_rows)
-    src = w.src_dtype
-    eb = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.cache_dtype]
-    res_cu, new_cu = w.cu(w.res_len), w.cu(w.new_len)
-    qc = codes(w.q, w.q_dtype)
-    done, t_total, nbytes = 0, 0.0, 0.0
-    poison = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F),
-              "int8": np.uint8(0x80)}
-    pk = np.full((w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim), poison[w.cache_dtype])
-    pv = pk.copy()
-    with threadpool_limits(limits=1):
-        ready = set()
-        passes = 0
-        while t_total < budget_s:          # whole passes over the step's sequences
-            for s in rows:
-                if passes and t_total >= budget_s:
-                    break
-                seqs = [s]
-                if w.shared_prefix_seqs and s in w.shared_prefix_seqs[1:]:
-                    seqs = [w.shared_prefix_seqs[0], s]
-                for r in seqs:                   # resident tokens: setup, not timed
-                    if r in ready:
-                        continue
+    def append(r, which):
+        start, lens, kk, vv, cu = ((w.res_start, w.res_len, a["res_k"], a["res_v"], res_cu)
+                                   if which == "res" else
+                                   (w.new_start, w.new_len, a["new_k"], a["new_v"], new_cu))
+        sl = paged.slot_mapping(w.block_tables[[r]], start[[r]], lens[[r]], bs)
+        k, v = np.asarray(kk[cu[r]:cu[r + 1]]), np.asarray(vv[cu[r]:cu[r + 1]])
+        if int4:
+            paged.kv_append_int4(pk, pv, ps, k, v, sl, bs, src, w.k_channel_scales)
+        else:
+            paged.kv_append(pk, k, sl, bs, src, cdt, w.k_scale)
+            paged.kv_append(pv, v, sl, bs, src, cdt, w.v_scale)
+
+    ready = set()
+    out = {}
+    t_total, done = 0.0, 0
+    while True:
+        for task in tasks:
+            if done and t_total >= budget_s:
+                return out
+            kind, s = task[0], task[1]
+            seqs = [s]
+            if w.shared_prefix_seqs and s in w.shared_prefix_seqs[1:]:
+                seqs = [w.shared_prefix_seqs[0], s]
+            for r in seqs:                              # resident tokens: setup, not timed
+                if r not in ready:
                     ready.add(r)
-                    a, b = res_cu[r], res_cu[r + 1]
-                    sl = oracle.paged.slot_mapping(w.block_tables[[r]], w.res_start[[r]],
-                                                   w.res_len[[r]], w.block_size)
-                    oracle.paged.kv_append(pk, codes(w.res_k[a:b], src), sl, w.block_size, src,
-                                           w.cache_dtype, w.k_scale)
-                    oracle.paged.kv_append(pv, codes(w.res_v[a:b], src), sl, w.block_size, src,
-                                           w.cache_dtype, w.v_scale)
-                nk = codes(w.new_k[new_cu[s]:new_cu[s + 1]], src)
-                nv = codes(w.new_v[new_cu[s]:new_cu[s + 1]], src)
-                qd = np.zeros((w.num_seqs,) + qc.shape[1:], qc.dtype)
-                qd[s] = qc[s]
-                t0 = time.perf_counter()           # timed: slot map + append + decode
-                sl = oracle.paged.slot_mapping(w.block_tables[[s]], w.new_start[[s]],
-                                               w.new_len[[s]], w.block_size)
-                oracle.paged.kv_append(pk, nk, sl, w.block_size, src, w.cache_dtype, w.k_scale)
-                oracle.paged.kv_append(pv, nv, sl, w.block_size, src, w.cache_dtype, w.v_scale)
-                oracle.paged.decode(qd, w.q_dtype, pk, pv, w.cache_dtype, w.block_tables,
-                                    w.context_lens, w.block_size, w.group_size, w.scale,
-                                    w.k_scale, w.v_scale, rows=[s])
-                t_total += time.perf_counter() - t0
-                nbytes += float(w.context_lens[s]) * w.n_kv_heads * w.head_dim * 2 * eb
-                done += 1
-            passes += 1
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} sequence decodes ({passes} pass(es) over the {len(rows)} sequences "
-                      f"of the same step: slot map + append + decode), {t_total:.1f} s, single "
-                      f"thread, float64 NumPy; logical K/V bytes"}
+                    append(r, "res")
+                    if kind == "prefill":
+                        append(r, "new")                # the chunk's own K/V
+            if kind == "decode":
+                qd = np.zeros((w.num_seqs,) + a["q"].shape[1:], a["q"].dtype)
+                qd[s] = a["q"][q_cu[s]]
+                t0 = time.perf_counter()                # timed: slot map + append + decode
+                append(s, "new")
+                if int4:
+                    paged.decode_int4(qd, w.q_dtype, pk, pv, ps, w.k_channel_scales,
+                                      w.block_tables, w.context_lens, bs, w.group_size,
+                                      w.scale, rows=[s])
+                else:
+                    paged.decode(qd, w.q_dtype, pk, pv, cdt, w.block_tables, w.context_lens, bs,
+                                 w.group_size, w.scale, w.k_scale, w.v_scale, rows=[s])
+                dt_s = time.perf_counter() - t0
+                nbytes, nflops = float(w.context_lens[s]) * w.n_kv_heads * tok_head, 0.0
+            else:
+                i = task[2]
+                row = int(q_cu[s]) + i
+                T = int(w.context_lens[s]) - int(w.q_lens[s]) + i + 1
+                t0 = time.perf_counter()                # timed: one query row of the chunk
+                paged.prefill_chunk(np.asarray(a["q"][row:row + 1]), w.q_dtype, np.array([0, 1]),
+                                    pk, pv, cdt, w.block_tables[s:s + 1], np.array([T]), bs,
+                                    w.group_size, w.scale, True, w.k_scale, w.v_scale)
+                dt_s = time.perf_counter() - t0
+                nbytes, nflops = 0.0, 4.0 * w.head_dim * w.n_q_heads * T
+            acc = out.setdefault(kind, [0.0, 0.0, 0.0, 0])
+            acc[0] += dt_s
+            acc[1] += nbytes
+            acc[2] += nflops
+            acc[3] += 1
+            t_total += dt_s
+            done += 1
+
+
+def cpu_baseline(w, budget_s: float, step_bytes: float, step_flops: float):
+    """The oracle, as it is, on a bounded sample of the same step, on the host cores:
+    one spawned worker process per core (up to 16), each with one BLAS thread (a
+    per-(sequence, head) product does not spread over BLAS threads), each timing its
+    share for about budget_s seconds.  Scaled to the step: the oracle's time for the
+    whole step on these cores is step_bytes at the decode rate plus step_flops at the
+    prefill rate; value = step_bytes / that time (the unit of the step's value)."""
+    import concurrent.futures as cf
+    import dataclasses
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    from workloads import codes
+
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    tmp = tempfile.mkdtemp(prefix="pa_oracle_")
+    try:
+        files = {}
+        for name, dtype in (("q", w.q_dtype), ("res_k", w.src_dtype), ("res_v", w.src_dtype),
+                            ("new_k", w.src_dtype), ("new_v", w.src_dtype)):
+            files[name] = os.path.join(tmp, name + ".npy")
+            np.save(files[name], codes(getattr(w, name), dtype))
+        meta = dataclasses.replace(w, q=None, res_k=None, res_v=None, new_k=None, new_v=None)
+        tasks = [("decode", s) for s in w.decode_rows]
+        rng = np.random.default_rng(0)
+        for s in range(w.num_prefill_seqs):             # sampled query rows of each chunk
+            L = int(w.q_lens[s])
+            for i in sorted(set([0, L - 1] + rng.integers(0, L, 6).tolist())):
+                tasks.append(("prefill", s, i))
+        order = rng.permutation(len(tasks))
+        shares = [[tasks[k] for k in order[j::n]] for j in range(n)]
+        shares = [sh for sh in shares if sh]
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                              "MKL_NUM_THREADS")}
+        os.environ.update({k: "1" for k in env})        # inherited by the spawned workers
+        try:
+            t0 = time.perf_counter()
+            with cf.ProcessPoolExecutor(len(shares), mp_context=mp.get_context("spawn")) as ex:
+                res = list(ex.map(_oracle_worker, [(meta, files, sh, budget_s) for sh in shares]))
+            wall = time.perf_counter() - t0
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    cores = len(shares)
+    tot = {}
+    for r in res:
+        for kind, acc in r.items():
+            t = tot.setdefault(kind, [0.0, 0.0, 0.0, 0])
+            for k in range(4):
+                t[k] += acc[k]
+    # per core-second rates, times the cores that ran them side by side
+    t_step = 0.0
+    sample = []
+    if "decode" in tot:
+        sec, by, _, cnt = tot["decode"]
+        gbs = cores * by / sec / 1e9
+        t_step += step_bytes / (gbs * 1e9)
+        sample.append(f"{cnt} sequence decodes (slot map + append + decode of one sequence, "
+                      f"{sec:.1f} core-s, {gbs:.3f} GB/s of logical K/V on {cores} cores)")
+    if "prefill" in tot:
+        sec, _, fl, cnt = tot["prefill"]
+        gfs = cores * fl / sec / 1e9
+        t_step += step_flops / (gfs * 1e9)
+        sample.append(f"{cnt} chunk query rows ({sec:.1f} core-s, {gfs:.3f} GFLOP/s of visible "
+                      f"pairs on {cores} cores)")
+    rec = {"value": round(step_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": "; ".join(sample) + f"; {wall:.1f} s wall, one process per core, float64 "
+                     f"NumPy; scaled to the step ({step_bytes / 1e9:.3f} GB"
+                     + (f" + {step_flops / 1e9:.1f} GFLOP" if step_flops else "") + ")",
+           "oracle_step_ms": round(t_step * 1e3, 3)}
+    if "decode" in tot:
+        rec["decode_GBps"] = round(gbs, 4)
+    if "prefill" in tot:
+        rec["prefill_GFLOPs"] = round(gfs, 4)
+    return rec
 
 
 # Block copies on the Llama-3-8B-shaped pool (block 16, 8 KV heads, 128 dims, bf16:
@@ -320,7 +432,8 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--pools", type=int, default=2, help="pool copies rotated across steps")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="timed oracle seconds per host core for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured-ceiling probes (contiguous read, block-order read, "
@@ -366,7 +479,7 @@ def main():
     t0 = time.perf_counter()
     w = workloads.full(cfg, kv=kv)
     workloads.draw_values(w, dev)
-    from tests.gpu_harness import DeviceWorkload, i32
+    from workloads.device import DeviceWorkload, i32
     dw = DeviceWorkload(w, dev)
     dw.append_resident()
     int4 = w.cache_dtype == "int4"
@@ -538,13 +651,11 @@ def main():
         log(msg)
 
     cpu = None
-    if int4 and not args.no_cpu_baseline:
-        log("cpu baseline: not taken for the int4 cache")
-    if not args.no_cpu_baseline and not P and not int4:
-        w_host = w
+    if not args.no_cpu_baseline:
         for name in ("q", "res_k", "res_v", "new_k", "new_v"):
-            setattr(w_host, name, getattr(w, name).cpu())
-        cpu = cpu_baseline(w_host, args.cpu_seconds)
+            setattr(w, name, getattr(w, name).cpu())
+        cpu = cpu_baseline(w, args.cpu_seconds, bm["step"],
+                           prefill_flops(w, range(P)) if P else 0.0)
         log(f"cpu baseline (oracle): {cpu['value']} GB/s, {cpu['sample']}")
 
     rec = {

@@ -216,9 +216,9 @@ pa_status pa_decode(void* out, const void* q, int q_dtype,
 
 /*
  * pa_prefill_workspace_bytes -- scratch needed by pa_prefill_chunk (0 for an
- * empty batch or unsupported head counts).  It grows with num_seqs and
- * total_q, not with num_seqs times max_q_len: a batch of many decode rows
- * beside a few long chunks needs little.  The call must pass the same
+ * empty batch or unsupported head counts), for either dtype pair.  It grows
+ * with num_seqs and total_q, not with num_seqs times max_q_len: a batch of
+ * many decode rows beside a few long chunks needs little.  The call must pass the same
  * num_seqs, total_q and max_q_len.
  */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
@@ -246,13 +246,19 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *   Work is spread over the device in equal shares of 32-key tiles; a short
  *   chunk occupies only the matrix-core rows it needs.
  *
- *   out, q        [total_q][n_q_heads][head_dim] bf16 (q_dtype must be BF16)
+ *   (q, cache) dtype pairs: (BF16, BF16), (BF16, FP8_E4M3), (BF16, INT8) on
+ *   the matrix cores, and (F32, F32), where each query row runs as a decode
+ *   row of its chunk's sequence (context T_s - L_s + i + 1 when causal, T_s
+ *   otherwise) on the fp32 vector decode kernel.
+ *
+ *   out, q        [total_q][n_q_heads][head_dim] of q_dtype (BF16 or F32)
  *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[num_seqs] == total_q
  *   max_q_len     host-side upper bound of the L_s.  A cu_seqlens_q that
  *                 needs more query tiles than total_q and max_q_len allow
  *                 (the device-side planner checks) is not computed: out is
  *                 left unwritten and nothing outside the arguments is touched.
- *   cache_dtype   BF16, FP8_E4M3 or INT8 (codes times k_scale / v_scale)
+ *   cache_dtype   BF16, FP8_E4M3 or INT8 (codes times k_scale / v_scale) with
+ *                 BF16 queries; F32 with F32 queries
  *   head_dim      64 or 128; block_size a power of two in [1, 256];
  *                 block_size * n_kv_heads * head_dim * 2 below 2^31 (a block's
  *                 rows are addressed with 32-bit offsets), else PA_ERR_SHAPE
@@ -431,34 +437,6 @@ pa_status pa_prefill_chunk_int4(void* out, const void* q, int q_dtype,
                                 const int32_t* context_lens, int32_t max_context_len,
                                 int32_t causal, float scale, void* workspace,
                                 size_t workspace_bytes, void* stream);
-
-/*
- * Measured ceilings -- yardsticks for the benchmark, not part of the attention
- * path.  Each launches num_wgs workgroups of 256 threads on `stream`.
- *
- * pa_ceiling_stream_read: reads bytes (a multiple of 16) of buf once,
- *   contiguously, 16-byte non-temporal loads with 8 in flight per lane; sink
- *   as below, over the buffer's words.
- * pa_ceiling_gather_read: reads whole blocks of block_bytes (a multiple of
- *   16) from k_pool and v_pool with 16-byte non-temporal loads, block
- *   blocks[i] for i < n in list order (a block table's order is the order a
- *   paged decode reads them in; 0, 1, 2, ... is a contiguous read); entries
- *   outside [0, pool_blocks) read block 0.  Workgroup w takes an equal
- *   contiguous share of the list, and sink[4 w + v] (uint32 [num_wgs * 4])
- *   receives the XOR of the 32-bit words wave v of workgroup w read, so the
- *   XOR of all sink entries is the XOR of every word of the listed blocks of
- *   both pools.
- * pa_ceiling_mfma_bf16: each of the num_wgs * 4 waves issues iters rounds of 4
- *   independent v_mfma_f32_32x32x16_bf16 (A = B = 1); sink (float
- *   [num_wgs * 4]) receives 64 * 16 * iters per wave.  FLOPs per launch:
- *   num_wgs * 4 * iters * 4 * 32768.
- */
-pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
-                                 int32_t num_wgs, void* stream);
-pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool, int64_t pool_blocks,
-                                 int32_t block_bytes, const int32_t* blocks, int64_t n,
-                                 uint32_t* sink, int32_t num_wgs, void* stream);
-pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters, void* stream);
 
 #ifdef __cplusplus
 }

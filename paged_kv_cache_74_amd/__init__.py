@@ -52,10 +52,6 @@ def lib():
         _c("pa_kv_append", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int, P, I,
            F, F, P)
         _c("pa_kv_append_int4", ctypes.c_int, P, P, P, I, I, I, I, P, P, ctypes.c_int, P, I, P, P)
-        L64 = ctypes.c_int64
-        _c("pa_ceiling_stream_read", ctypes.c_int, P, L64, P, I, P)
-        _c("pa_ceiling_gather_read", ctypes.c_int, P, P, L64, I, P, L64, P, I, P)
-        _c("pa_ceiling_mfma_bf16", ctypes.c_int, P, I, I, P)
         _c("pa_kv_append_paged", ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, P, P, ctypes.c_int,
            P, I, P, P, I, I, I, P, F, F, P)
         _c("pa_kv_append_int4_paged", ctypes.c_int, P, P, P, I, I, I, I, P, P, ctypes.c_int, P, I,
@@ -190,38 +186,6 @@ def pa_kv_append_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torc
         _ptr(v_new), _dtype_code(k_new), tp, mb, cp, sp, ns, T, max_tokens_per_seq,
         _ptr(slot_mapping) if slot_mapping is not None else None, k_scale, v_scale,
         _stream(stream)))
-
-
-def pa_ceiling_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_wgs: int,
-                           stream=None) -> None:
-    """Read all of buf once, contiguously (measurement); sink: 4-byte [4 * num_wgs]."""
-    _dev(buf, sink)
-    _need(buf.is_contiguous() and sink.numel() >= 4 * num_wgs and sink.element_size() == 4,
-          "sink: 4-byte [4 * num_wgs]")
-    _check("pa_ceiling_stream_read", lib().pa_ceiling_stream_read(
-        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), num_wgs, _stream(stream)))
-
-
-def pa_ceiling_gather_read(k_pool: torch.Tensor, v_pool: torch.Tensor, blocks: torch.Tensor,
-                           sink: torch.Tensor, num_wgs: int, stream=None) -> None:
-    """Read whole pool blocks in list order (measurement)."""
-    _dev(k_pool, v_pool, blocks, sink)
-    _need(k_pool.shape == v_pool.shape and k_pool.is_contiguous() and v_pool.is_contiguous(),
-          "pools")
-    _need(blocks.dtype == torch.int32 and sink.numel() >= 4 * num_wgs and
-          sink.element_size() == 4, "blocks int32, sink 4-byte [4 * num_wgs]")
-    nb = k_pool.shape[0]
-    _check("pa_ceiling_gather_read", lib().pa_ceiling_gather_read(
-        _ptr(k_pool), _ptr(v_pool), nb, k_pool.numel() * k_pool.element_size() // nb,
-        _ptr(blocks), blocks.numel(), _ptr(sink), num_wgs, _stream(stream)))
-
-
-def pa_ceiling_mfma_bf16(sink: torch.Tensor, num_wgs: int, iters: int, stream=None) -> None:
-    """Matrix-core issue rate (measurement); sink: float32 [num_wgs * 4]."""
-    _dev(sink)
-    _need(sink.dtype == torch.float32 and sink.numel() >= 4 * num_wgs, "sink: float32 [4 W]")
-    _check("pa_ceiling_mfma_bf16", lib().pa_ceiling_mfma_bf16(_ptr(sink), num_wgs, iters,
-                                                              _stream(stream)))
 
 
 def _int4_pools(k_cache, v_cache, v_scales, k_channel_scales):

@@ -11,8 +11,9 @@
 //
 // The copy is bandwidth bound: each workgroup moves one 16 KiB chunk of one
 // block of K or V with 16-byte (8-byte when the block size needs it)
-// non-temporal loads and stores, so a batch of pairs spreads over the whole
-// chip.
+// non-temporal loads and stores, all of a lane's loads issued before its
+// stores, so a batch of pairs spreads over the whole chip with many reads in
+// flight.
 #include "pa_device.h"
 
 namespace pa {
@@ -37,17 +38,27 @@ __global__ __launch_bounds__(CB_THREADS) void copy_blocks_kernel(
     const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v, int64_t src_blocks,
     const int64_t* __restrict__ pairs, int64_t block_bytes, int chunks_per_block) {
   typedef typename CopyVec<VEC>::T V;
+  // every load of the chunk is issued before the first store, so a lane keeps
+  // CB_CHUNK / (CB_THREADS * VEC) loads in flight instead of one
+  constexpr int N = (int)(CB_CHUNK / (CB_THREADS * VEC));
   const int pair = blockIdx.x / chunks_per_block;
   const int chunk = blockIdx.x % chunks_per_block;
   const int64_t s = pairs[2 * (int64_t)pair], d = pairs[2 * (int64_t)pair + 1];
   if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
   const uint8_t* src = (blockIdx.y ? src_v : src_k) + s * block_bytes;
   uint8_t* dst = (blockIdx.y ? dst_v : dst_k) + d * block_bytes;
+  const int64_t base = (int64_t)chunk * CB_CHUNK + threadIdx.x * VEC;
   const int64_t end = min(block_bytes, (int64_t)(chunk + 1) * CB_CHUNK);
-  for (int64_t off = (int64_t)chunk * CB_CHUNK + threadIdx.x * VEC; off < end;
-       off += (int64_t)CB_THREADS * VEC) {
-    const V x = __builtin_nontemporal_load((const V*)(src + off));
-    __builtin_nontemporal_store(x, (V*)(dst + off));
+  V x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int64_t off = base + (int64_t)i * CB_THREADS * VEC;
+    if (off < end) x[i] = __builtin_nontemporal_load((const V*)(src + off));
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int64_t off = base + (int64_t)i * CB_THREADS * VEC;
+    if (off < end) __builtin_nontemporal_store(x[i], (V*)(dst + off));
   }
 }
 
@@ -80,14 +91,12 @@ extern "C" pa_status pa_copy_blocks(void* dst_k, void* dst_v, int32_t dst_num_bl
   const dim3 grid((unsigned)(num_pairs * chunks), 2);
   hipStream_t st = (hipStream_t)stream;
   if (vec == 16)
-    hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(CB_THREADS), 0, st, (uint8_t*)dst_k,
-                       (uint8_t*)dst_v, (int64_t)dst_num_blocks, (const uint8_t*)src_k,
-                       (const uint8_t*)src_v, (int64_t)src_num_blocks, block_pairs, block_bytes,
-                       (int)chunks);
-  else
-    hipLaunchKernelGGL(copy_blocks_kernel<8>, grid, dim3(CB_THREADS), 0, st, (uint8_t*)dst_k,
-                       (uint8_t*)dst_v, (int64_t)dst_num_blocks, (const uint8_t*)src_k,
-                       (const uint8_t*)src_v, (int64_t)src_num_blocks, block_pairs, block_bytes,
-                       (int)chunks);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+    return launch(copy_blocks_kernel<16>, grid, dim3(CB_THREADS), 0, st, (uint8_t*)dst_k,
+                  (uint8_t*)dst_v, (int64_t)dst_num_blocks, (const uint8_t*)src_k,
+                  (const uint8_t*)src_v, (int64_t)src_num_blocks, block_pairs, block_bytes,
+                  (int)chunks);
+  return launch(copy_blocks_kernel<8>, grid, dim3(CB_THREADS), 0, st, (uint8_t*)dst_k,
+                (uint8_t*)dst_v, (int64_t)dst_num_blocks, (const uint8_t*)src_k,
+                (const uint8_t*)src_v, (int64_t)src_num_blocks, block_pairs, block_bytes,
+                (int)chunks);
 }

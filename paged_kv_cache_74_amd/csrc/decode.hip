@@ -103,6 +103,10 @@ struct DecodeArgs {
   float score_scale;  // scale * k_scale * log2(e)
   const float* k_ch_scale;   // INT4: [n_kv][HD] key scale per channel
   const float* v_tok_scale;  // INT4: [num_blocks][n_kv][block_size] value scale per token
+  // vector kernel only: block-table row of each query row (NULL: row s reads
+  // table row s).  The fp32 chunked prefill runs each query row as a decode
+  // row of its own sequence.
+  const int32_t* table_row;
 };
 
 template <class L>
@@ -581,7 +585,8 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, int s, int kvh, 
     }
   }
 
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+  const int trow = a.table_row ? uniform_load(a.table_row, s) : s;
+  const int32_t* table = a.block_tables + (int64_t)trow * a.max_blocks;
   const int lane_byte = lane_c * L::CHUNK;
   const float c = a.score_scale;
 
@@ -1412,7 +1417,9 @@ static WsLayout ws_layout(int64_t entries, int G, int head_dim) {
 
 template <int CDT, int HD, int G>
 static int64_t resident_wgs(int hw) {
-  static int64_t cached[DECODE_MAX_HW + 1] = {};   // per instantiation and group size
+  // per device, instantiation and group size
+  static int64_t cache[MAX_DEVICES][DECODE_MAX_HW + 1] = {};
+  int64_t* cached = cache[current_device()];
   if (!cached[hw]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -1459,7 +1466,8 @@ __host__ __device__ constexpr int mf_nbuf(int CDT) {
 
 template <int CDT, int HD, int G, bool STAGED>
 static int64_t resident_wgs_mf(int hw) {
-  static int64_t cached[DECODE_MAX_HW + 1] = {};
+  static int64_t cache[MAX_DEVICES][DECODE_MAX_HW + 1] = {};   // per device
+  int64_t* cached = cache[current_device()];
   if (!cached[hw]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -1474,17 +1482,17 @@ static int64_t resident_wgs_mf(int hw) {
 }
 
 template <int CDT, int HD, int G, bool STAGED>
-static void launch_mf(const DecodeArgs& a, int split_tokens, int64_t bound, hipStream_t st) {
+static pa_status launch_mf(const DecodeArgs& a, int split_tokens, int64_t bound, hipStream_t st) {
   DecodeArgs b = a;
   int64_t W = split_tokens <= 0 ? resident_wgs_mf<CDT, HD, G, STAGED>(a.hw) : bound;
   if (W > bound) W = bound;
   b.num_wgs = (int)W;
-  hipLaunchKernelGGL((decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>), dim3((unsigned)W),
-                     dim3(64 * a.hw), 0, st, b);
+  return launch(decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>, dim3((unsigned)W),
+                dim3(64 * a.hw), 0, st, b);
 }
 
 template <int CDT, int HD, int G>
-static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
+static pa_status launch_split(DecodeArgs a, int split_tokens, int max_context_len, hipStream_t st) {
   constexpr bool MF = (DECODE_MFMA_MASK >> CDT) & 1;
   const int hw = heads_per_wg(CDT, a.n_kv, G);
   const bool mf = MF && a.block_size >= 16;
@@ -1494,60 +1502,58 @@ static void launch_split(DecodeArgs a, int split_tokens, int max_context_len, hi
   if constexpr (MF) {
     if (mf) {
       if constexpr (mf_stageable_layout<CDT, HD>() && DECODE_MF_STAGED) {
-        if (mf_staged_ok(MfLayout<CDT, HD>::ROW, hw)) {
-          launch_mf<CDT, HD, G, true>(a, split_tokens, bound, st);
-          return;
-        }
+        if (mf_staged_ok(MfLayout<CDT, HD>::ROW, hw))
+          return launch_mf<CDT, HD, G, true>(a, split_tokens, bound, st);
       }
-      launch_mf<CDT, HD, G, false>(a, split_tokens, bound, st);
-      return;
+      return launch_mf<CDT, HD, G, false>(a, split_tokens, bound, st);
     }
   }
   int64_t W = split_tokens <= 0 ? resident_wgs<CDT, HD, G>(hw) : bound;
   if (W > bound) W = bound;
   a.num_wgs = (int)W;
-  hipLaunchKernelGGL((decode_split_kernel<CDT, HD, G, DECODE_NBUF>), dim3((unsigned)W),
-                     dim3(64 * hw), 0, st, a);
+  return launch(decode_split_kernel<CDT, HD, G, DECODE_NBUF>, dim3((unsigned)W), dim3(64 * hw), 0,
+                st, a);
 }
 
 template <int CDT, int HD>
-static bool dispatch_group(int G, const DecodeArgs& a, int split_tokens, int max_ctx, hipStream_t st) {
+static pa_status dispatch_group(int G, const DecodeArgs& a, int split_tokens, int max_ctx,
+                                hipStream_t st) {
   switch (G) {
-    case 1: launch_split<CDT, HD, 1>(a, split_tokens, max_ctx, st); return true;
-    case 2: launch_split<CDT, HD, 2>(a, split_tokens, max_ctx, st); return true;
-    case 4: launch_split<CDT, HD, 4>(a, split_tokens, max_ctx, st); return true;
-    case 8: launch_split<CDT, HD, 8>(a, split_tokens, max_ctx, st); return true;
-    default: return false;
+    case 1: return launch_split<CDT, HD, 1>(a, split_tokens, max_ctx, st);
+    case 2: return launch_split<CDT, HD, 2>(a, split_tokens, max_ctx, st);
+    case 4: return launch_split<CDT, HD, 4>(a, split_tokens, max_ctx, st);
+    case 8: return launch_split<CDT, HD, 8>(a, split_tokens, max_ctx, st);
+    default: return PA_ERR_UNSUPPORTED;
   }
 }
 
 template <int CDT>
-static bool dispatch_hd(int hd, int G, const DecodeArgs& a, int split_tokens, int max_ctx,
-                        hipStream_t st) {
+static pa_status dispatch_hd(int hd, int G, const DecodeArgs& a, int split_tokens, int max_ctx,
+                             hipStream_t st) {
   if (hd == 128) return dispatch_group<CDT, 128>(G, a, split_tokens, max_ctx, st);
   if (hd == 64) return dispatch_group<CDT, 64>(G, a, split_tokens, max_ctx, st);
-  return false;
+  return PA_ERR_UNSUPPORTED;
 }
 
 // The merge reads the wave count the split kernel used from the workspace.
 template <int HD, int G, bool BF16>
-static void launch_merge_t(void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
-                           int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+static pa_status launch_merge_t(void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
+                                int num_seqs, int n_kv, float out_scale, hipStream_t st) {
   const char* base = (const char*)ws;
-  hipLaunchKernelGGL((decode_merge_kernel<HD, G, BF16>), dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
-                     dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
-                     ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale);
+  return launch(decode_merge_kernel<HD, G, BF16>, dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
+                dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
+                ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale);
 }
 
 template <int HD, bool BF16>
-static bool merge_g(int G, void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
-                    int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+static pa_status merge_g(int G, void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
+                         int num_seqs, int n_kv, float out_scale, hipStream_t st) {
   switch (G) {
-    case 1: launch_merge_t<HD, 1, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
-    case 2: launch_merge_t<HD, 2, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
-    case 4: launch_merge_t<HD, 4, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
-    case 8: launch_merge_t<HD, 8, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st); return true;
-    default: return false;
+    case 1: return launch_merge_t<HD, 1, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
+    case 2: return launch_merge_t<HD, 2, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
+    case 4: return launch_merge_t<HD, 4, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
+    case 8: return launch_merge_t<HD, 8, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
+    default: return PA_ERR_UNSUPPORTED;
   }
 }
 
@@ -1582,15 +1588,11 @@ static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int 
 static pa_status launch_merge(void* out, int out_dtype, const int32_t* context_lens, int num_seqs,
                               int n_kv, int G, int head_dim, const WsLayout& l, float out_scale,
                               const void* workspace, hipStream_t st) {
-  bool ok;
   if (out_dtype == PA_BF16)
-    ok = head_dim == 128 ? merge_g<128, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
-                         : merge_g<64, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
-  else
-    ok = head_dim == 128 ? merge_g<128, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
+    return head_dim == 128 ? merge_g<128, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
+                           : merge_g<64, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
+  return head_dim == 128 ? merge_g<128, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
                          : merge_g<64, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
-  if (!ok) return PA_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 // Both phases of decode; merge == false runs the partials phase only.
@@ -1603,7 +1605,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
                              float k_scale, float v_scale, int32_t split_tokens, void* workspace,
                              size_t workspace_bytes, void* stream,
                              const float* k_channel_scales = nullptr,
-                             const float* v_token_scales = nullptr) {
+                             const float* v_token_scales = nullptr,
+                             const int32_t* table_row = nullptr) {
   pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len, split_tokens);
   if (e != PA_OK) return e;
   if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
@@ -1651,17 +1654,15 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.k_ch_scale = k_channel_scales;
   a.v_tok_scale = v_token_scales;
+  a.table_row = table_row;
 
   hipStream_t st = (hipStream_t)stream;
-  bool ok = false;
-  if (cache_dtype == PA_BF16) ok = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
-  else if (cache_dtype == PA_FP8_E4M3) ok = dispatch_hd<PA_FP8_E4M3>(head_dim, G, a, split_tokens, max_context_len, st);
-  else if (cache_dtype == PA_INT8) ok = dispatch_hd<PA_INT8>(head_dim, G, a, split_tokens, max_context_len, st);
-  else if (int4) ok = dispatch_hd<PA_INT4>(head_dim, G, a, split_tokens, max_context_len, st);
-  else ok = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
-  if (!ok) return PA_ERR_UNSUPPORTED;
-  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  if (!merge) return PA_OK;
+  if (cache_dtype == PA_BF16) e = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (cache_dtype == PA_FP8_E4M3) e = dispatch_hd<PA_FP8_E4M3>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (cache_dtype == PA_INT8) e = dispatch_hd<PA_INT8>(head_dim, G, a, split_tokens, max_context_len, st);
+  else if (int4) e = dispatch_hd<PA_INT4>(head_dim, G, a, split_tokens, max_context_len, st);
+  else e = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
+  if (e != PA_OK || !merge) return e;
   return launch_merge(out, q_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
                       fp8 ? v_scale : 1.0f, workspace, st);
 }
@@ -1747,3 +1748,70 @@ extern "C" pa_status pa_decode_int4_partials(const void* q, int q_dtype, const v
                      1.0f, split_tokens, workspace, workspace_bytes, stream, k_channel_scales,
                      v_token_scales);
 }
+
+// ---------------------------------------------------------------------------
+// Chunked prefill over an fp32 cache (pa_prefill_chunk with F32 q and cache).
+// Query row i of chunk s (L_s rows, T_s cached tokens including the chunk)
+// sees the keys j <= T_s - L_s + i when causal, all T_s keys otherwise
+// ("3.3 Batching and memory management", section "Chunked prefill"): that is
+// a decode row of sequence s whose context is T_s - L_s + i + 1 (or T_s)
+// tokens.  A planning kernel writes each row's context length and table row;
+// the vector decode kernel and its merge then run over the total_q rows.
+// fp32 has no matrix-core path here: every row reads its keys itself.
+// ---------------------------------------------------------------------------
+namespace pa {
+
+__global__ __launch_bounds__(256) void prefill_rows_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx, int num_seqs, int total_q,
+    int causal, int32_t* __restrict__ row_ctx, int32_t* __restrict__ row_seq) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= total_q) return;
+  // the chunk holding row r: the last s with cu[s] <= r (cu non-decreasing)
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int c0 = cu[lo], c1 = cu[lo + 1];
+  int n = 0;
+  if (c0 <= r && r < c1) {
+    const int T = ctx[lo];
+    n = causal ? T - (c1 - c0) + (r - c0) + 1 : T;
+    n = n < 0 ? 0 : n > T ? T : n;
+  }
+  row_ctx[r] = n;     // rows outside every chunk: no keys, zero output
+  row_seq[r] = lo;
+}
+
+size_t prefill_f32_workspace_bytes(int total_q, int n_kv, int G, int head_dim,
+                                   int max_context_len) {
+  if (total_q <= 0) return 0;
+  return 2 * align256((size_t)total_q * 4) +
+         ws_layout(entries_bound(total_q, n_kv, G, max_context_len, 0), G, head_dim).total;
+}
+
+pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens_q, int num_seqs,
+                           int total_q, const void* k_cache, const void* v_cache, int num_blocks,
+                           int block_size, int n_kv, int head_dim, int G,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int max_context_len, int causal,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           hipStream_t st) {
+  if ((int64_t)total_q * n_kv * steps_of(max_context_len) >= (int64_t)1 << 31) return PA_ERR_SHAPE;
+  const size_t rows = align256((size_t)total_q * 4);
+  if (workspace_bytes < prefill_f32_workspace_bytes(total_q, n_kv, G, head_dim, max_context_len))
+    return PA_ERR_WORKSPACE;
+  char* base = (char*)workspace;
+  int32_t* row_ctx = (int32_t*)base;
+  int32_t* row_seq = (int32_t*)(base + rows);
+  pa_status e = launch(prefill_rows_kernel, dim3((unsigned)((total_q + 255) / 256)), dim3(256), 0,
+                       st, cu_seqlens_q, context_lens, num_seqs, total_q, causal, row_ctx,
+                       row_seq);
+  if (e != PA_OK) return e;
+  return decode_impl(out, true, q, PA_F32, k_cache, v_cache, PA_F32, num_blocks, block_size, n_kv,
+                     head_dim, G, block_tables, max_blocks_per_seq, row_ctx, total_q,
+                     max_context_len, scale, 1.0f, 1.0f, 0, base + 2 * rows,
+                     workspace_bytes - 2 * rows, st, nullptr, nullptr, row_seq);
+}
+
+}  // namespace pa

@@ -1,0 +1,20 @@
+// Host-side functions one source file of the library calls in another (not
+// exported: the C ABI is include/pa.h).
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+// decode.hip: chunked prefill over an fp32 cache, each query row run as a
+// decode row of its chunk's sequence on the vector decode kernel.
+size_t prefill_f32_workspace_bytes(int total_q, int n_kv, int G, int head_dim,
+                                   int max_context_len);
+pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens_q, int num_seqs,
+                           int total_q, const void* k_cache, const void* v_cache, int num_blocks,
+                           int block_size, int n_kv, int head_dim, int G,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int max_context_len, int causal,
+                           float scale, void* workspace, size_t workspace_bytes, hipStream_t st);
+
+}  // namespace pa

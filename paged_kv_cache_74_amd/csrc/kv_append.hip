@@ -304,9 +304,12 @@ __global__ __launch_bounds__(256) void kv_append_int4_kernel(
   const int lane = blockIdx.x * blockDim.x + threadIdx.x;
   // every lane of a row takes part in the row's shuffles: no early return
   // before them (rows never straddle a wave: lanes_per_row divides 64)
+  // idle lanes past the last row redo the last lane's reads (stores off), so
+  // every load address stays inside k_new / v_new / k_channel_scales
   const bool live = lane < total_lanes;
-  const int row = (int)((unsigned)min(lane, total_lanes - 1) / (unsigned)lanes_per_row);
-  const int j = lane - row * lanes_per_row;          // 8-element piece of the row
+  const int lc = min(lane, total_lanes - 1);
+  const int row = (int)((unsigned)lc / (unsigned)lanes_per_row);
+  const int j = lc - row * lanes_per_row;            // 8-element piece of the row
   const int tok = row / n_kv, head = row - tok * n_kv;
   const int64_t slot = slots[tok];
   const bool ok = live && slot >= 0 && slot < num_slots_in_pool;
@@ -369,10 +372,9 @@ extern "C" pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!slot_mapping || !block_tables || !cu_tokens || !start_pos) return PA_ERR_NULL;
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, (hipStream_t)stream,
+  return launch(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, (hipStream_t)stream,
                      slot_mapping, block_tables, max_blocks_per_seq, block_size, cu_tokens,
                      start_pos);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
@@ -397,10 +399,10 @@ extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
   const uint8_t* kn = (const uint8_t*)k_new;
   const uint8_t* vn = (const uint8_t*)v_new;
   if (cache_dtype == src_dtype && cache_dtype == PA_BF16) {
-    hipLaunchKernelGGL((kv_append_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc, kn,
+    return launch((kv_append_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc, kn,
                        vn, slot_mapping, pool_slots, lanes_per_token, total, 1.0f, 1.0f);
   } else if (cache_dtype == src_dtype && cache_dtype == PA_F32) {
-    hipLaunchKernelGGL((kv_append_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc, kn,
+    return launch((kv_append_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc, kn,
                        vn, slot_mapping, pool_slots, lanes_per_token, total, 1.0f, 1.0f);
   } else if ((cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8) &&
              (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
@@ -411,12 +413,10 @@ extern "C" pa_status pa_kv_append(void* k_cache, void* v_cache, int cache_dtype,
                                              : kv_append_kernel<PA_BF16, PA_FP8_E4M3>)
                                        : (i8 ? kv_append_kernel<PA_F32, PA_INT8>
                                              : kv_append_kernel<PA_F32, PA_FP8_E4M3>);
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, slot_mapping, pool_slots,
+    return launch(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, slot_mapping, pool_slots,
                        lanes_per_token, total, k_inv, v_inv);
-  } else {
-    return PA_ERR_DTYPE;
   }
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_ERR_DTYPE;
 }
 
 extern "C" pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_scales,
@@ -438,11 +438,10 @@ extern "C" pa_status pa_kv_append_int4(void* k_cache, void* v_cache, float* v_sc
   const int total = (int)lanes;
   const dim3 grid((unsigned)((total + 255) / 256), 2);
   auto kernel = src_dtype == PA_BF16 ? kv_append_int4_kernel<PA_BF16> : kv_append_int4_kernel<PA_F32>;
-  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
+  return launch(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
                      (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new,
                      slot_mapping, k_channel_scales, (int64_t)num_blocks * block_size, block_size,
                      n_kv_heads, lanes_per_row, total);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 // Grid of the paged appends: one workgroup row per segment, enough 256-lane
@@ -485,10 +484,10 @@ extern "C" pa_status pa_kv_append_paged(void* k_cache, void* v_cache, int cache_
   const uint8_t* vn = (const uint8_t*)v_new;
   const int lpt = (int)lanes;
   if (cache_dtype == src_dtype && cache_dtype == PA_BF16) {
-    hipLaunchKernelGGL((kv_append_paged_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc,
+    return launch((kv_append_paged_kernel<PA_BF16, PA_BF16>), grid, dim3(256), 0, st, kc, vc,
                        kn, vn, m, pool_slots, lpt, 1.0f, 1.0f);
   } else if (cache_dtype == src_dtype && cache_dtype == PA_F32) {
-    hipLaunchKernelGGL((kv_append_paged_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc,
+    return launch((kv_append_paged_kernel<PA_F32, PA_F32>), grid, dim3(256), 0, st, kc, vc,
                        kn, vn, m, pool_slots, lpt, 1.0f, 1.0f);
   } else if ((cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8) &&
              (src_dtype == PA_BF16 || src_dtype == PA_F32)) {
@@ -500,12 +499,10 @@ extern "C" pa_status pa_kv_append_paged(void* k_cache, void* v_cache, int cache_
                             : kv_append_paged_kernel<PA_BF16, PA_FP8_E4M3>)
                       : (i8 ? kv_append_paged_kernel<PA_F32, PA_INT8>
                             : kv_append_paged_kernel<PA_F32, PA_FP8_E4M3>);
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, m, pool_slots, lpt, k_inv,
+    return launch(kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, m, pool_slots, lpt, k_inv,
                        v_inv);
-  } else {
-    return PA_ERR_DTYPE;
   }
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_ERR_DTYPE;
 }
 
 extern "C" pa_status pa_kv_append_int4_paged(void* k_cache, void* v_cache, float* v_scales,
@@ -537,9 +534,8 @@ extern "C" pa_status pa_kv_append_int4_paged(void* k_cache, void* v_cache, float
   const dim3 grid = paged_grid(num_seqs, max_tokens_per_seq, lanes);
   auto kernel = src_dtype == PA_BF16 ? kv_append_int4_paged_kernel<PA_BF16>
                                      : kv_append_int4_paged_kernel<PA_F32>;
-  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
+  return launch(kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint8_t*)k_cache,
                      (uint8_t*)v_cache, v_scales, (const uint8_t*)k_new, (const uint8_t*)v_new, m,
                      k_channel_scales, (int64_t)num_blocks * block_size, block_size, n_kv_heads,
                      lanes_per_row);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "../../include/pa.h"
 
 namespace pa {
@@ -128,6 +131,38 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 __device__ __forceinline__ int32_t uniform_load(const int32_t* p, int i) {
   return ((const_i32*)p)[i];
+}
+
+// ---------------------------------------------------------------------------
+// host: launch a kernel and report the status of that launch alone.
+// hipLaunchKernel returns the launch's own error code; an error left behind by
+// an unrelated earlier call (which hipGetLastError would hand back) is not
+// reported as this call's failure.
+// ---------------------------------------------------------------------------
+template <typename... P, size_t... I>
+inline pa_status launch_held(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem,
+                             hipStream_t stream, std::tuple<P...>& held,
+                             std::index_sequence<I...>) {
+  void* argv[] = {(void*)&std::get<I>(held)..., nullptr};
+  return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+template <typename... P, typename... A>
+inline pa_status launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem,
+                        hipStream_t stream, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> held(std::forward<A>(args)...);
+  return launch_held(kernel, grid, block, shmem, stream, held, std::index_sequence_for<P...>{});
+}
+
+// Device id of the calling thread (0 if it cannot be read), for per-device caches.
+constexpr int MAX_DEVICES = 64;
+inline int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) dev = 0;
+  return dev;
 }
 
 }  // namespace pa

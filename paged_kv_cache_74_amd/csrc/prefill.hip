@@ -40,7 +40,7 @@
 //     workgroups are combined by a log-sum-exp merge kernel.
 //   * The next tile's K/V is in registers while a tile is computed; LDS is
 //     double-buffered, one barrier per tile; three workgroups share a CU.
-#include "pa_device.h"
+#include "internal.h"
 
 #include <type_traits>
 
@@ -771,7 +771,8 @@ static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_
 
 template <int CDT, int HD, int G>
 static int pf_resident_wgs() {
-  static int cached = 0;   // per instantiation; the device is assumed not to change
+  static int cache[MAX_DEVICES] = {};   // per device and instantiation
+  int& cached = cache[current_device()];
   if (!cached) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<CDT, HD, G>, 256, 0) !=
@@ -784,8 +785,8 @@ static int pf_resident_wgs() {
 }
 
 template <int CDT, int HD, int G>
-static void pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len, const PfLayout& l,
-                      char* ws, hipStream_t st) {
+static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len,
+                           const PfLayout& l, char* ws, hipStream_t st) {
   const int W = pf_resident_wgs<CDT, HD, G>();
   a.hdr = (const int32_t*)(ws + l.hdr);
   a.seg_cu = (const int32_t*)(ws + l.seg);
@@ -793,24 +794,25 @@ static void pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len, c
   a.wg_start = (const int32_t*)(ws + l.wgs);
   a.part_ml = (float*)(ws + l.ml);
   a.part_o = (float*)(ws + l.o);
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, num_seqs, total_q,
-                     max_q_len, PF_ROWS / G, W,
-                     (int32_t*)(ws + l.hdr), (int32_t*)(ws + l.seq), (int32_t*)(ws + l.seg),
-                     (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs));
-  hipLaunchKernelGGL((prefill_kernel<CDT, HD, G>), dim3(W), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((prefill_merge_kernel<HD, G>),
-                     dim3(a.nseg_max * (PF_ROWS / MergeShape<HD>::ROWS)), dim3(256), 0, st, a, W);
+  pa_status e = launch(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, num_seqs, total_q,
+                       max_q_len, PF_ROWS / G, W, (int32_t*)(ws + l.hdr), (int32_t*)(ws + l.seq),
+                       (int32_t*)(ws + l.seg), (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs));
+  if (e == PA_OK) e = launch(prefill_kernel<CDT, HD, G>, dim3(W), dim3(256), 0, st, a);
+  if (e == PA_OK)
+    e = launch(prefill_merge_kernel<HD, G>, dim3(a.nseg_max * (PF_ROWS / MergeShape<HD>::ROWS)),
+               dim3(256), 0, st, a, W);
+  return e;
 }
 
 template <int CDT, int HD>
-static bool pf_dispatch_g(int G, const PrefillArgs& a, int num_seqs, int total_q, int max_q_len,
-                          const PfLayout& l, char* ws, hipStream_t st) {
+static pa_status pf_dispatch_g(int G, const PrefillArgs& a, int num_seqs, int total_q,
+                               int max_q_len, const PfLayout& l, char* ws, hipStream_t st) {
   switch (G) {
-    case 1: pf_launch<CDT, HD, 1>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
-    case 2: pf_launch<CDT, HD, 2>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
-    case 4: pf_launch<CDT, HD, 4>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
-    case 8: pf_launch<CDT, HD, 8>(a, num_seqs, total_q, max_q_len, l, ws, st); return true;
-    default: return false;
+    case 1: return pf_launch<CDT, HD, 1>(a, num_seqs, total_q, max_q_len, l, ws, st);
+    case 2: return pf_launch<CDT, HD, 2>(a, num_seqs, total_q, max_q_len, l, ws, st);
+    case 4: return pf_launch<CDT, HD, 4>(a, num_seqs, total_q, max_q_len, l, ws, st);
+    case 8: return pf_launch<CDT, HD, 8>(a, num_seqs, total_q, max_q_len, l, ws, st);
+    default: return PA_ERR_UNSUPPORTED;
   }
 }
 
@@ -837,8 +839,12 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, 
     return 0;
   const int G = n_q_heads / n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
-  return pf_layout(num_seqs, pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, G),
-                   (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
+  // the larger of the two plans: matrix-core tiles (bf16 queries) or one
+  // decode row per query (fp32 queries and cache)
+  const size_t mf = pf_layout(num_seqs, pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, G),
+                              (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
+  const size_t rows = prefill_f32_workspace_bytes(total_q, n_kv_heads, G, head_dim, max_context_len);
+  return mf > rows ? mf : rows;
 }
 
 static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32_t* cu_seqlens_q,
@@ -859,12 +865,22 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
     return PA_ERR_UNSUPPORTED;
   const bool int4 = cache_dtype == PA_INT4;
-  if (q_dtype != PA_BF16 || (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 &&
-                             cache_dtype != PA_INT8 && !int4))
+  const bool f32 = q_dtype == PA_F32 && cache_dtype == PA_F32;
+  if (!f32 && (q_dtype != PA_BF16 || (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3 &&
+                                      cache_dtype != PA_INT8 && !int4)))
     return PA_ERR_DTYPE;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
+  if (f32) {
+    if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
+    if (!workspace || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
+    return prefill_f32_rows((float*)out, (const float*)q, cu_seqlens_q, num_seqs, total_q,
+                            k_cache, v_cache, num_blocks, block_size, n_kv_heads, head_dim,
+                            group_size, block_tables, max_blocks_per_seq, context_lens,
+                            max_context_len, causal, scale, workspace, workspace_bytes,
+                            (hipStream_t)stream);
+  }
   if (int4 && (!k_channel_scales || !v_scales)) return PA_ERR_NULL;
   // 8-bit caches (fp8 or int8) carry per-tensor scales
   const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
@@ -906,7 +922,7 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   a.out_scale = fp8 ? v_scale : 1.0f;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  bool (*dispatch)(int, const PrefillArgs&, int, int, int, const PfLayout&, char*, hipStream_t);
+  pa_status (*dispatch)(int, const PrefillArgs&, int, int, int, const PfLayout&, char*, hipStream_t);
   if (cache_dtype == PA_BF16)
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128> : pf_dispatch_g<PA_BF16, 64>;
   else if (cache_dtype == PA_FP8_E4M3)
@@ -915,9 +931,7 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128> : pf_dispatch_g<PA_INT8, 64>;
   else
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT4, 128> : pf_dispatch_g<PA_INT4, 64>;
-  const bool ok = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, st);
-  if (!ok) return PA_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, st);
 }
 
 extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,

@@ -4,12 +4,14 @@
 // HBM, 2.5 PFLOP/s dense bf16): a decode kernel is judged against what reading
 // the same blocks in the same order can reach (and in physical order, for the
 // cost of the order), the prefill kernel against what v_mfma_f32_32x32x16_bf16
-// can reach.  Not part of the attention path.
+// can reach.  Not part of the attention path: built into libpa_probes.so, a
+// library of its own that only the benchmark and its tests load.
 //
 // Every reader folds what it reads into an XOR checksum that it writes out, so
 // the loads cannot be dropped and a test can check that exactly the intended
 // bytes were read.
-#include "pa_device.h"
+#include "../csrc/pa_device.h"
+#include "pa_probes.h"
 
 namespace pa {
 
@@ -107,9 +109,8 @@ extern "C" pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint
   if (bytes < 0 || bytes % 16 != 0 || num_wgs < 1) return PA_ERR_SHAPE;
   if (bytes == 0) return PA_OK;
   if (!buf || !sink) return PA_ERR_NULL;
-  hipLaunchKernelGGL(ceiling_stream_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
-                     (hipStream_t)stream, (const uint8_t*)buf, bytes / 16, sink);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return launch(ceiling_stream_kernel, dim3((unsigned)num_wgs), dim3(256), 0, (hipStream_t)stream,
+                (const uint8_t*)buf, bytes / 16, sink);
 }
 
 extern "C" pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool,
@@ -123,17 +124,15 @@ extern "C" pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_po
   if (!k_pool || !v_pool || !blocks || !sink) return PA_ERR_NULL;
   if (pool_blocks == 0) return PA_ERR_SHAPE;
   // entries outside [0, pool_blocks) read block 0
-  hipLaunchKernelGGL(ceiling_gather_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
-                     (hipStream_t)stream, (const uint8_t*)k_pool, (const uint8_t*)v_pool, blocks,
-                     n, pool_blocks, block_bytes, sink);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return launch(ceiling_gather_kernel, dim3((unsigned)num_wgs), dim3(256), 0, (hipStream_t)stream,
+                (const uint8_t*)k_pool, (const uint8_t*)v_pool, blocks, n, pool_blocks,
+                block_bytes, sink);
 }
 
 extern "C" pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters,
                                           void* stream) {
   if (num_wgs < 1 || iters < 1) return PA_ERR_SHAPE;
   if (!sink) return PA_ERR_NULL;
-  hipLaunchKernelGGL(ceiling_mfma_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
-                     (hipStream_t)stream, iters, sink);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return launch(ceiling_mfma_kernel, dim3((unsigned)num_wgs), dim3(256), 0, (hipStream_t)stream,
+                iters, sink);
 }

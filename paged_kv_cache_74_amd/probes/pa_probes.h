@@ -1,0 +1,51 @@
+/*
+ * pa_probes.h -- measurement probes (libpa_probes.so), not part of the paged
+ * attention library: plain kernels that read whole pool blocks or only issue
+ * matrix-core instructions, so that a benchmark can report what this GPU
+ * reaches for the same bytes or the same instruction mix.  Statuses and
+ * stream convention as in include/pa.h.
+ */
+#ifndef PA_PROBES_H_
+#define PA_PROBES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Measured ceilings.  Each launches num_wgs workgroups of 256 threads on `stream`.
+ *
+ * pa_ceiling_stream_read: reads bytes (a multiple of 16) of buf once,
+ *   contiguously, 16-byte non-temporal loads with 8 in flight per lane; sink
+ *   as below, over the buffer's words.
+ * pa_ceiling_gather_read: reads whole blocks of block_bytes (a multiple of
+ *   16) from k_pool and v_pool with 16-byte non-temporal loads, block
+ *   blocks[i] for i < n in list order (a block table's order is the order a
+ *   paged decode reads them in; 0, 1, 2, ... is a contiguous read); entries
+ *   outside [0, pool_blocks) read block 0.  Workgroup w takes an equal
+ *   contiguous share of the list, and sink[4 w + v] (uint32 [num_wgs * 4])
+ *   receives the XOR of the 32-bit words wave v of workgroup w read, so the
+ *   XOR of all sink entries is the XOR of every word of the listed blocks of
+ *   both pools.
+ * pa_ceiling_mfma_bf16: each of the num_wgs * 4 waves issues iters rounds of 4
+ *   independent v_mfma_f32_32x32x16_bf16 (A = B = 1); sink (float
+ *   [num_wgs * 4]) receives 64 * 16 * iters per wave.  FLOPs per launch:
+ *   num_wgs * 4 * iters * 4 * 32768.
+ */
+pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
+                                 int32_t num_wgs, void* stream);
+pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool, int64_t pool_blocks,
+                                 int32_t block_bytes, const int32_t* blocks, int64_t n,
+                                 uint32_t* sink, int32_t num_wgs, void* stream);
+pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_PROBES_H_ */

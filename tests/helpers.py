@@ -9,21 +9,7 @@ import numpy as np
 import torch
 
 import oracle
-from workloads import POISON, Workload
-
-
-def codes(t, dtype: str) -> np.ndarray:
-    """Raw element codes of a CPU/GPU torch tensor as a numpy array."""
-    t = t.detach()
-    if t.is_cuda:
-        t = t.cpu()
-    if dtype == "f32":
-        return t.contiguous().view(torch.int32).numpy().view(np.uint32)
-    if dtype == "bf16":
-        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    if dtype in ("fp8", "int8"):
-        return t.contiguous().view(torch.uint8).numpy()
-    raise ValueError(dtype)
+from workloads import POISON, Workload, codes  # noqa: F401  (codes re-exported)
 
 
 def poisoned_pool(w: Workload) -> np.ndarray:

@@ -71,6 +71,23 @@ def test_no_undeclared_exports(lib):
     assert exported == set(_declarations()), exported ^ set(_declarations())
 
 
+PROBES_HEADER = os.path.join(ROOT, "paged_kv_cache_74_amd", "probes", "pa_probes.h")
+
+
+def test_measurement_probes_live_in_their_own_library():
+    """libpa.so carries only the method; the benchmark's probes are libpa_probes.so."""
+    from paged_kv_cache_74_amd import probes
+    text = re.sub(r"/\*.*?\*/", "", open(PROBES_HEADER).read(), flags=re.S)
+    declared = set(re.findall(r"\b(pa_\w+)\s*\(", text))
+    assert declared == {"pa_ceiling_stream_read", "pa_ceiling_gather_read", "pa_ceiling_mfma_bf16"}
+    assert not declared & set(_declarations())
+    nm = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    assert {l.split()[-1] for l in nm.splitlines() if " T pa_" in l} == declared
+    lp = probes.lib()
+    assert all(hasattr(lp, n) for n in declared)
+
+
 def test_binding_arity_matches_header(lib):
     for name, n in _declarations().items():
         f = getattr(lib, name)
@@ -151,8 +168,10 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, hd=256) == PA_ERR_UNSUPPORTED
     assert _prefill(lib, g=16) == PA_ERR_UNSUPPORTED
     assert _prefill(lib, bs=3) == PA_ERR_UNSUPPORTED
-    assert _prefill(lib, qdt=F32) == PA_ERR_DTYPE
-    assert _prefill(lib, cdt=F32) == PA_ERR_DTYPE
+    assert _prefill(lib, qdt=F32) == PA_ERR_DTYPE              # (F32, BF16)
+    assert _prefill(lib, cdt=F32) == PA_ERR_DTYPE              # (BF16, F32)
+    assert _prefill(lib, qdt=F32, cdt=FP8) == PA_ERR_DTYPE
+    assert _prefill(lib, qdt=F32, cdt=F32) == PA_ERR_NULL      # (F32, F32) is supported
     assert _prefill(lib, ns=-1) == PA_ERR_SHAPE
     assert _prefill(lib) == PA_ERR_NULL
 
@@ -164,6 +183,9 @@ def test_prefill_scale_checks(lib):
     assert _prefill(lib, scale=-0.1, **d) == PA_ERR_SHAPE
     assert _prefill(lib, scale=float("inf"), **d) == PA_ERR_SHAPE
     assert _prefill(lib, scale=float("nan"), **d) == PA_ERR_SHAPE
+    assert _prefill(lib, qdt=F32, cdt=F32, scale=0.0, **d) == PA_ERR_SHAPE
+    assert _prefill(lib, qdt=F32, cdt=F32, **d) == PA_ERR_WORKSPACE     # no workspace given
+    assert lib.pa_prefill_workspace_bytes(2, 64, 32, 8, 2, 128, 64) > 0
 
 
 def _copy(lib, **kw):

@@ -325,3 +325,38 @@ def test_decode_split_quotients_in_double_are_exact():
         got = np.floor(((xs + 1).astype(np.float64) * float(W) - 1.0) / float(U)).astype(np.int64)
         want = np.array([((int(x) + 1) * int(W) - 1) // int(U) for x in xs], dtype=np.int64)
         assert np.array_equal(got, want), (U, W)
+
+
+def int4_append_lane_reads(lane, total_lanes, lanes_per_row, n_kv, clamp_piece=True):
+    """(token, head, piece) whose source rows and key scales lane `lane` of
+    kv_append_int4_kernel reads.  Idle lanes past the last row take the last
+    lane's row and piece (clamp_piece=False restates the unclamped piece index,
+    which idle lanes pushed past the row)."""
+    lc = min(lane, total_lanes - 1)
+    row = lc // lanes_per_row
+    j = (lc if clamp_piece else lane) - row * lanes_per_row
+    return row // n_kv, row % n_kv, j
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_int4_append_reads_stay_in_bounds(head_dim):
+    """Every lane of the grid (256-lane workgroups, the last one partly idle) reads
+    inside k_new / v_new ([tokens][n_kv][head_dim]) and k_channel_scales
+    ([n_kv][head_dim]), for lane counts that are not multiples of 256."""
+    lpr = head_dim // 8
+    for tokens in (1, 3, 7, 33):
+        for n_kv in (1, 2, 3, 8):
+            total = tokens * n_kv * lpr
+            grid = (total + 255) // 256 * 256
+            src_elems = tokens * n_kv * head_dim
+            bad = 0
+            for lane in range(grid):
+                tok, head, j = int4_append_lane_reads(lane, total, lpr, n_kv)
+                assert 0 <= tok < tokens and 0 <= head < n_kv and 0 <= j < lpr
+                row_elem = (tok * n_kv + head) * head_dim + j * 8
+                assert row_elem + 8 <= src_elems                       # 8 source elements
+                assert head * head_dim + j * 8 + 8 <= n_kv * head_dim   # 8 key scales
+                t2, h2, j2 = int4_append_lane_reads(lane, total, lpr, n_kv, clamp_piece=False)
+                bad += (t2 * n_kv + h2) * head_dim + j2 * 8 + 8 > src_elems
+            # the unclamped piece index reads past the rows whenever lanes are idle
+            assert (bad > 0) == (grid > total)

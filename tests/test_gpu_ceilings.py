@@ -14,8 +14,8 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
-    import paged_kv_cache_74_amd as pa
-    pa.lib()
+    from paged_kv_cache_74_amd import probes
+    probes.lib()
     return "cuda"
 
 
@@ -25,18 +25,18 @@ def _xor(a: np.ndarray) -> int:
 
 @pytest.mark.parametrize("nbytes,wgs", [(16, 1), (10_000_048, 37), (64 << 20, 2048)])
 def test_stream_read_reads_every_word_once(dev, nbytes, wgs):
-    import paged_kv_cache_74_amd as pa
+    from paged_kv_cache_74_amd import probes
     rng = np.random.default_rng(nbytes)
     host = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = torch.as_tensor(host.view(np.int32), device=dev)
     sink = torch.zeros(4 * wgs, dtype=torch.int32, device=dev)
-    pa.pa_ceiling_stream_read(buf, sink, wgs)
+    probes.pa_ceiling_stream_read(buf, sink, wgs)
     torch.cuda.synchronize()
     assert _xor(sink.cpu().numpy()) == _xor(host)
 
 
 def test_gather_read_reads_the_listed_blocks(dev):
-    import paged_kv_cache_74_amd as pa
+    from paged_kv_cache_74_amd import probes
     rng = np.random.default_rng(3)
     nb, bb = 50, 4096                                        # 50 blocks of 4 KiB
     k = rng.integers(0, 1 << 32, (nb, bb // 4), dtype=np.uint64).astype(np.uint32)
@@ -50,15 +50,15 @@ def test_gather_read_reads_the_listed_blocks(dev):
     gk = torch.as_tensor(k.view(np.int32), device=dev)
     gv = torch.as_tensor(v.view(np.int32), device=dev)
     sink = torch.zeros(4 * 64, dtype=torch.int32, device=dev)
-    pa.pa_ceiling_gather_read(gk, gv, torch.as_tensor(blocks, device=dev), sink, 64)
+    probes.pa_ceiling_gather_read(gk, gv, torch.as_tensor(blocks, device=dev), sink, 64)
     torch.cuda.synchronize()
     assert _xor(sink.cpu().numpy()) == want
 
 
 def test_mfma_loop_sums(dev):
-    import paged_kv_cache_74_amd as pa
+    from paged_kv_cache_74_amd import probes
     W, iters = 16, 300
     sink = torch.zeros(4 * W, dtype=torch.float32, device=dev)
-    pa.pa_ceiling_mfma_bf16(sink, W, iters)
+    probes.pa_ceiling_mfma_bf16(sink, W, iters)
     torch.cuda.synchronize()
     assert (sink.cpu().numpy() == 64.0 * 16 * iters).all()

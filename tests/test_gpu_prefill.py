@@ -1,7 +1,8 @@
 """GPU parity of the chunked-prefill kernel (MFMA) against the oracle.
 
 Bars: bf16 / fp8- and int8-KV outputs within 2e-2 absolute and 1e-2 normwise relative
-error per row; a chunk of length 1 must agree with the decode kernel.
+error per row, fp32 outputs within 1e-5 normwise relative error per row; a chunk of
+length 1 must agree with the decode kernel.
 """
 import numpy as np
 import pytest
@@ -55,6 +56,23 @@ def test_prefill_shapes(dev, nq, nkv, hd, bs):
     workloads.draw_values(w, "cpu")
     got, ref = _run(w, dev)
     check_close(got, ref, "bf16", f"prefill {nq}/{nkv}/{hd}/bs{bs}")
+
+
+# (n_q, n_kv, head_dim, block_size) of the fp32 pair: the worked example's heads and
+# blocks (2 / 2 heads, 64 dims, blocks of 4), then grouped heads on bigger blocks
+F32_SHAPES = [(2, 2, 64, 4), (8, 2, 128, 16), (16, 2, 64, 1)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("nq,nkv,hd,bs", F32_SHAPES)
+def test_prefill_f32_pair(dev, nq, nkv, hd, bs, causal):
+    """(F32, F32): each query row runs as a decode row of its chunk; fp32 bar (1e-5)."""
+    w = workloads.mixed_prefill_decode(prior=(0, 9, 40, 3), chunk_lens=(6, 5, 33, 1), n_decode=2,
+                                       dlo=1, dhi=30, seed=3, n_q=nq, n_kv=nkv, hd=hd, bs=bs,
+                                       kv="f32")
+    workloads.draw_values(w, "cpu")
+    got, ref = _run(w, dev, causal)
+    check_close(got, ref, "f32", f"prefill f32 {nq}/{nkv}/{hd}/bs{bs} causal={causal}")
 
 
 @pytest.mark.parametrize("kv", ["fp8", "int8"])

@@ -32,6 +32,22 @@ from typing import Optional
 
 import numpy as np
 
+def codes(t, dtype: str) -> np.ndarray:
+    """Raw element codes of a CPU or GPU torch tensor as a numpy array (a bit view,
+    copied to the host when the tensor lives on the GPU)."""
+    import torch
+    t = t.detach()
+    if t.is_cuda:
+        t = t.cpu()
+    if dtype == "f32":
+        return t.contiguous().view(torch.int32).numpy().view(np.uint32)
+    if dtype == "bf16":
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if dtype in ("fp8", "int8"):
+        return t.contiguous().view(torch.uint8).numpy()
+    raise ValueError(dtype)
+
+
 # Bit patterns used to fill the pool before anything is appended.  They are
 # NaNs, so any read of a slot that no token owns shows up in the results.
 POISON = {"f32": np.uint32(0xFFC0DEAD), "bf16": np.uint16(0xFFC1), "fp8": np.uint8(0x7F),
@@ -291,8 +307,9 @@ def mixed_prefill_decode(prior=(0, 2048, 8192, 32768), chunk=512, n_decode=128,
     rl = np.concatenate([prior, dctx - 1]).astype(np.int32)
     ns = rl.copy()
     nl = np.concatenate([L, np.ones(n_decode, np.int32)]).astype(np.int32)
-    return Workload(name="mixed-prefill-decode", cache_dtype=kv, q_dtype="bf16",
-                    src_dtype="bf16", n_q_heads=n_q, n_kv_heads=n_kv, head_dim=hd,
+    qdt = "f32" if kv == "f32" else "bf16"     # an fp32 cache takes fp32 queries and rows
+    return Workload(name="mixed-prefill-decode", cache_dtype=kv, q_dtype=qdt,
+                    src_dtype=qdt, n_q_heads=n_q, n_kv_heads=n_kv, head_dim=hd,
                     block_size=bs, num_blocks=nb, context_lens=ctx, block_tables=tables,
                     q_lens=nl.copy(), res_start=rs, res_len=rl, new_start=ns, new_len=nl,
                     scale=1.0 / math.sqrt(hd), num_prefill_seqs=P, seed=seed)
