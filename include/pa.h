@@ -311,6 +311,32 @@ pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
                           void* stream);
 
 /*
+ * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device
+ *   memory: code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc.  Same arguments, results and checks as pa_decode, minus
+ *   the workspace: the split partials go to a scratch array of
+ *   PA_NO_ALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ *   on (a device variable, resident until the process ends; its address is
+ *   looked up once per device on the first call there).  The call allocates
+ *   nothing and needs no initialised scratch.
+ *   A call whose partials (pa_decode_workspace_bytes(...) for its sizes) do
+ *   not fit returns PA_ERR_WORKSPACE before anything is enqueued; use
+ *   pa_decode with a workspace then.  All calls on one device share its
+ *   scratch: calls that may overlap on one device (different streams, or
+ *   different host threads without ordering) race and must be serialised by
+ *   the caller.
+ */
+#define PA_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_no_alloc(void* out, const void* q, int q_dtype,
+                             const void* k_cache, const void* v_cache, int cache_dtype,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t group_size,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len, float scale, float k_scale,
+                             float v_scale, int32_t split_tokens, void* stream);
+
+/*
  * pa_copy_blocks -- whole-block copies between paged pools: copy-on-write
  *   within one pool, and swap-out / swap-in between a device pool and a pool
  *   in pinned host memory.

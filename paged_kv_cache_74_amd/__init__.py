@@ -66,6 +66,8 @@ def lib():
         _c("pa_decode_partials", ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I,
            P, I, P, I, I, F, F, I, P, S, P)
         _c("pa_decode_merge", ctypes.c_int, P, ctypes.c_int, P, I, I, I, I, I, I, F, P, S, P)
+        _c("pa_decode_no_alloc", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I,
+           I, P, I, P, I, I, F, F, F, I, P)
         _c("pa_copy_blocks", ctypes.c_int, P, P, I, P, P, I, ctypes.c_int, I, I, I, P, I, P)
         _c("pa_prefill_workspace_bytes", S, I, I, I, I, I, I, I)
         _c("pa_prefill_chunk", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, ctypes.c_int, I, I,
@@ -314,6 +316,31 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         B, max_context_len, scale, k_scale, v_scale, split_tokens, _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+PA_NO_ALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_no_alloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor,
+                       max_context_len: int, scale: float, out: torch.Tensor,
+                       k_scale: float = 1.0, v_scale: float = 1.0, split_tokens: int = 0,
+                       stream=None) -> torch.Tensor:
+    """pa_decode with the library's own scratch: no workspace, and ``out`` must be given,
+    so the call itself allocates nothing."""
+    L = lib()
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out)
+    B, nq, hd = q.shape
+    nb, bs, nkv, hd2 = k_cache.shape
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out: q's shape and dtype")
+    _need(block_tables.dtype == context_lens.dtype == torch.int32, "int32 tables / lengths")
+    _need(block_tables.shape[0] >= B and context_lens.shape[0] >= B, "one table row per sequence")
+    _check("pa_decode_no_alloc", L.pa_decode_no_alloc(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        nb, bs, nkv, hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, max_context_len, scale, k_scale, v_scale, split_tokens, _stream(stream)))
     return out
 
 

@@ -46,6 +46,8 @@
 //   * K/V of the next step are in flight while the current one is computed.
 #include "pa_device.h"
 
+#include <mutex>
+
 namespace pa {
 
 template <int CDT, int HD>
@@ -1714,6 +1716,61 @@ extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* co
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   return launch_merge(out, out_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
                       out_scale, workspace, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_no_alloc: pa_decode with its split partials in a scratch array the
+// library owns, for callers that cannot allocate.  The array is a file-scope
+// device variable: every device the library runs on holds one copy, at its own
+// address, until the process ends.  Host code must never pass the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, and is kept.
+// ---------------------------------------------------------------------------
+namespace pa {
+
+static __device__ __align__(256) uint8_t scratch[PA_NO_ALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch copy (nullptr if it cannot be had).
+static void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_decode_no_alloc(void* out, const void* q, int q_dtype, const void* k_cache,
+                                        const void* v_cache, int cache_dtype, int32_t num_blocks,
+                                        int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                                        int32_t group_size, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t max_context_len, float scale,
+                                        float k_scale, float v_scale, int32_t split_tokens,
+                                        void* stream) {
+  if (cache_dtype == PA_INT4) return PA_ERR_DTYPE;
+  pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len,
+                             split_tokens);
+  if (e != PA_OK) return e;
+  if (num_seqs == 0) return PA_OK;
+  // the partials this call needs, against the scratch's fixed size (no HIP call yet)
+  const WsLayout l = ws_layout(
+      entries_bound(num_seqs, n_kv_heads, group_size, max_context_len, split_tokens), group_size,
+      head_dim);
+  if (l.total > PA_NO_ALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return PA_ERR_HIP;
+  return decode_impl(out, true, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks, block_size,
+                     n_kv_heads, head_dim, group_size, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, k_scale, v_scale,
+                     split_tokens, ws, PA_NO_ALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" pa_status pa_decode_int4(void* out, const void* q, int q_dtype, const void* k_cache,

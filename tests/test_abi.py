@@ -234,3 +234,19 @@ def test_int4_argument_checks(lib):
     assert dec() == PA_ERR_NULL
     assert _copy(lib, cdt=INT4, bs=1, nkv=1, hd=8) == PA_ERR_UNSUPPORTED   # 4-byte blocks
     assert _copy(lib, cdt=INT4) == PA_ERR_NULL
+
+
+def test_decode_no_alloc_checks(lib):
+    """Host checks of the allocation-free decode, before any HIP call."""
+    call = lambda **kw: lib.pa_decode_no_alloc(
+        None, None, BF16, None, None, kw.get("cdt", BF16), 8, 16, 8, 128, kw.get("g", 4), None,
+        256, None, kw.get("ns", 2), kw.get("maxc", 4096), 0.1, 1.0, 1.0, 0, None)
+    assert call(ns=0) == PA_OK
+    assert call(g=3) == PA_ERR_UNSUPPORTED
+    assert call(cdt=pa.PA_INT4) == PA_ERR_DTYPE
+    assert call(ns=1 << 16) == PA_ERR_WORKSPACE           # partials beyond the fixed scratch
+    assert pa.pa_decode_workspace_bytes(1 << 16, 32, 8, 128, 4096, 0) > pa.PA_NO_ALLOC_SCRATCH_BYTES
+    # the binding's constant is the header's
+    text = open(HEADER).read()
+    assert "#define PA_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert pa.PA_NO_ALLOC_SCRATCH_BYTES == 64 << 20
