@@ -62,8 +62,8 @@ def test_mixed_step_one_launch(dev, kv):
 
 @pytest.mark.parametrize("nq,nkv,hd,bs", [(4, 4, 128, 16), (16, 2, 64, 32), (32, 4, 128, 1)])
 def test_mixed_step_interleaved_order(dev, nq, nkv, hd, bs):
-    """Decode rows before, between and after the chunks: the result does not
-    depend on where a sequence sits in the batch."""
+    """Decode rows before, between and after the chunks: every order matches the
+    oracle, and each order's result is the same run after run."""
     from gpu_harness import to_f64, varlen
     w = workloads.mixed_prefill_decode(prior=(0, 40, 300), chunk_lens=(50, 130, 33), n_decode=9,
                                        dlo=1, dhi=300, seed=3, n_q=nq, n_kv=nkv, hd=hd, bs=bs)
@@ -75,9 +75,14 @@ def test_mixed_step_interleaved_order(dev, nq, nkv, hd, bs):
     got = to_f64(varlen(dw, order))
     pk, pv = oracle_pools(w)
     check_close(got, _oracle_all(w, pk, pv), "bf16", f"mixed interleaved {nq}/{nkv}/{hd}/bs{bs}")
-    # bit-identical to the batch in its drawn order: each row's arithmetic is the same
+    # the batch in its drawn order: within the bar of the oracle as well, and
+    # deterministic run to run.  The two orders place the sequences at other
+    # points of the balanced work split, so a segment may be cut into pieces at
+    # other key tiles; results then agree within tolerance, not bit for bit
+    ref = _oracle_all(w, pk, pv)
     same = to_f64(varlen(dw))
-    assert np.array_equal(got, same)
+    check_close(same, ref, "bf16", f"mixed drawn order {nq}/{nkv}/{hd}/bs{bs}")
+    assert np.array_equal(same, to_f64(varlen(dw)))
 
 
 def test_mixed_step_full_size_sampled(dev):
