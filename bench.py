@@ -79,7 +79,9 @@ def byte_model(w):
     append = n_new * nkv * (hd * (sb + eb) * 2 + (4 if w.cache_dtype == "int4" else 0)) + n_new * 8
     slots = n_new * (8 + 4) + B * 8
     return {"kv_logical": kv_logical, "kv_unique": kv_unique, "split_kernel": split,
-            "step": split + out_bytes + append + slots, "append": append}
+            "step": split + out_bytes + append + slots, "append": append,
+            # the split kernel that also appends the step's tokens (pa_decode_append)
+            "split_append_kernel": split + append}
 
 
 DECODE_SOURCES = ("paged_kv_cache_74_amd/csrc/decode.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
@@ -441,6 +443,9 @@ def main():
     ap.add_argument("--two-call-append", action="store_true",
                     help="append through pa_slot_mapping + pa_kv_append[_int4] instead of the "
                          "one-launch pa_kv_append[_int4]_paged")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode workloads: append in its own launch (pa_kv_append_paged) before "
+                         "pa_decode_partials, instead of pa_decode_append_partials")
     ap.add_argument("--one-launch", action="store_true",
                     help="mixed workload: chunks and decode rows in one pa_prefill_chunk call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -529,9 +534,25 @@ def main():
     # long chunks among many one-token rows (the mixed step) most of that grid
     # is idle, and the two calls are faster (915 against 920 us per step).
     two_calls = args.two_call_append or max_new * len(w.new_len) > 4 * n_new
+    # a decode step whose new token per sequence is the last of its context: the
+    # split kernel appends it (pa_decode_append_partials), one launch fewer
+    fused = (not P and not int4 and not args.separate_append and not args.two_call_append
+             and bool((w.new_len == 1).all()) and bool((w.new_start == w.context_lens - 1).all()))
 
     def step(i, ev=None, pev=None):
         kc, vc, vsc = pools[i % len(pools)]
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            pa.pa_decode_append_partials(q, kc, vc, new_k, new_v, tables, ctx, maxc, w.scale, ws,
+                                         w.k_scale, w.v_scale, args.split_tokens,
+                                         slot_mapping=slots)
+            if ev is not None:
+                ev[1].record(stream)
+            pa.pa_decode_merge(out, ctx, w.n_kv_heads, maxc, ws,
+                               w.v_scale if w.cache_dtype in ("fp8", "int8") else 1.0,
+                               args.split_tokens)
+            return
         if two_calls:
             pa.pa_slot_mapping(dw.tables, new_cu, new_start, w.block_size, n_new, out=slots)
             if int4:
@@ -593,9 +614,10 @@ def main():
     ms_step = wall * 1e3 / args.steps
     step_gbs = bm["step"] / (ms_step * 1e-3) / 1e9
     ctx_tokens = float(w.context_lens[list(w.decode_rows)].sum())
+    split_bytes = bm["split_append_kernel"] if fused else bm["split_kernel"]
     if not one:
         split_avg = float(split_ms.mean())
-        achieved = bm["split_kernel"] / (split_avg * 1e-3) / 1e9
+        achieved = split_bytes / (split_avg * 1e-3) / 1e9
         log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s); split kernel avg {split_avg * 1e3:.1f} us "
             f"(p10 {np.percentile(split_ms, 10) * 1e3:.1f}, p90 {np.percentile(split_ms, 90) * 1e3:.1f}) "
             f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; "
@@ -675,7 +697,8 @@ def main():
             "workload": f"{w.name}: " + ("paged step, one attention launch (slot map + KV append + "
                                          "chunks and decode rows in pa_prefill_chunk)" if one else
                                          "paged decode step (slot map + KV append + split-K decode + merge)"),
-            "append": "pa_slot_mapping + pa_kv_append" if two_calls else
+            "append": "in the split kernel (pa_decode_append_partials)" if fused else
+                      "pa_slot_mapping + pa_kv_append" if two_calls else
                       "pa_kv_append_paged (slot map and append in one launch)",
             "batch": B, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.cache_dtype,
@@ -691,7 +714,8 @@ def main():
         "bytes_per_step": {"algorithmic_unique": bm["step"], "kv_unique": bm["kv_unique"],
                            "kv_logical": bm["kv_logical"]},
         "roofline": prefill_rec if one else {
-            "kernel": f"{decode_kernel(w)} (pa_decode_partials)",
+            "kernel": f"{decode_kernel(w)} (" + ("pa_decode_append_partials: append + split"
+                                                 if fused else "pa_decode_partials") + ")",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -701,7 +725,7 @@ def main():
             "avg_launch_us": round(split_avg * 1e3, 2),
             "launch_us_p10_p50_p90": [round(float(np.percentile(split_ms, q)) * 1e3, 2)
                                       for q in (10, 50, 90)],
-            "algorithmic_bytes_per_launch": bm["split_kernel"],
+            "algorithmic_bytes_per_launch": split_bytes,
         },
         "cpu_baseline": cpu,
         "measured_ceilings": ceil,

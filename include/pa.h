@@ -311,6 +311,60 @@ pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
                           void* stream);
 
 /*
+ * pa_decode_append / pa_decode_append_partials -- the decode step's append and
+ *   attention in one call: every sequence's newest token (position
+ *   context_lens[s] - 1, the token this step added) is written to its cache slot
+ *   and attended to.
+ *   Source: "KV Cache: the memory bottleneck of LLM inference", section 1.1
+ *   (step t appends k_t, v_t, then attends over K_{1:t}, V_{1:t}); slot
+ *   addressing of "3.3 Batching and memory management", section
+ *   "PagedAttention: the block table"; attention as in pa_decode.
+ *
+ *   Equivalent to pa_kv_append_paged (one token per sequence, start_pos =
+ *   context_lens[s] - 1, cu_tokens = 0, 1, ..., num_seqs) followed by pa_decode
+ *   (or pa_decode_partials): the same pools, slots and outputs, bit for bit.
+ *   Where the split kernel stages whole rows (bf16, fp8 and int8 caches with
+ *   blocks of 16 tokens or more) the append happens inside the attention
+ *   launch: the workgroup that reads a sequence's newest token takes it from
+ *   k_new / v_new and writes it to its slot.  Elsewhere the rows are written
+ *   by a launch of their own first.
+ *
+ *   k_new, v_new  [num_seqs][n_kv_heads][head_dim] of src_dtype, 16-byte aligned
+ *   src_dtype     = cache_dtype for F32 and BF16 caches; F32 or BF16 for
+ *                 FP8_E4M3 and INT8 caches (encoded with k_scale / v_scale as
+ *                 pa_kv_append does); INT4 caches: PA_ERR_DTYPE
+ *   slot_mapping  int64 [num_seqs] (may be NULL): the slot each token was
+ *                 written to, -1 for a negative table entry, a position past the
+ *                 table row or a sequence with context 0 (nothing appended)
+ *   k_cache, v_cache are written (the appended slots only); other arguments
+ *   as in pa_decode / pa_decode_partials.  pa_decode_append_partials also takes
+ *   v_scale (for the encode); pa_decode_merge applies it as out_scale.
+ */
+pa_status pa_decode_append(void* out, const void* q, int q_dtype,
+                           void* k_cache, void* v_cache, int cache_dtype,
+                           int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                           int32_t head_dim, int32_t group_size,
+                           const void* k_new, const void* v_new, int src_dtype,
+                           int64_t* slot_mapping,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, float scale, float k_scale, float v_scale,
+                           int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+pa_status pa_decode_append_partials(const void* q, int q_dtype,
+                                    void* k_cache, void* v_cache, int cache_dtype,
+                                    int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t group_size,
+                                    const void* k_new, const void* v_new, int src_dtype,
+                                    int64_t* slot_mapping,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t max_context_len, float scale, float k_scale,
+                                    float v_scale, int32_t split_tokens, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device
  *   memory: code under HIP graph capture, tight serving loops, harnesses that
  *   forbid hipMalloc.  Same arguments, results and checks as pa_decode, minus

@@ -68,6 +68,10 @@ def lib():
         _c("pa_decode_merge", ctypes.c_int, P, ctypes.c_int, P, I, I, I, I, I, I, F, P, S, P)
         _c("pa_decode_no_alloc", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I,
            I, P, I, P, I, I, F, F, F, I, P)
+        _c("pa_decode_append", ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I, I, I,
+           P, P, ctypes.c_int, P, P, I, P, I, I, F, F, F, I, P, S, P)
+        _c("pa_decode_append_partials", ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int, I, I, I,
+           I, I, P, P, ctypes.c_int, P, P, I, P, I, I, F, F, F, I, P, S, P)
         _c("pa_copy_blocks", ctypes.c_int, P, P, I, P, P, I, ctypes.c_int, I, I, I, P, I, P)
         _c("pa_prefill_workspace_bytes", S, I, I, I, I, I, I, I)
         _c("pa_prefill_chunk", ctypes.c_int, P, P, ctypes.c_int, P, I, I, I, P, P, ctypes.c_int, I, I,
@@ -355,6 +359,58 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_cont
         _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv,
         hd, nq // nkv, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
         max_context_len, scale, k_scale, split_tokens, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _append_args(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, slot_mapping):
+    _dev(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens)
+    B, nq, hd = q.shape
+    nb, bs, nkv, hd2 = k_cache.shape
+    _need(hd == hd2 and nq % nkv == 0, "head shapes")
+    _need(k_new.shape == v_new.shape == (B, nkv, hd) and k_new.dtype == v_new.dtype,
+          "new K/V: [num_seqs, n_kv, hd], one token per sequence")
+    _need(block_tables.dtype == context_lens.dtype == torch.int32, "int32 tables / lengths")
+    if slot_mapping is not None:
+        _dev(slot_mapping)
+        _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() >= B, "slot_mapping: int64 [B]")
+    return B, nq, hd, nb, bs, nkv
+
+
+def pa_decode_append(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                     max_context_len: int, scale: float, k_scale: float = 1.0,
+                     v_scale: float = 1.0, out=None, ws=None, split_tokens: int = 0,
+                     slot_mapping=None, stream=None) -> torch.Tensor:
+    """Append every sequence's newest token (position context_lens[s] - 1) from
+    k_new / v_new [B, n_kv, hd], then decode; returns out [B, n_q, hd]."""
+    L = lib()
+    B, nq, hd, nb, bs, nkv = _append_args(q, k_cache, v_cache, k_new, v_new, block_tables,
+                                          context_lens, slot_mapping)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    if ws is None:
+        ws = workspace(pa_decode_workspace_bytes(B, nq, nkv, hd, max_context_len, split_tokens),
+                       q.device)
+    _check("pa_decode_append", L.pa_decode_append(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb,
+        bs, nkv, hd, nq // nkv, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, max_context_len, scale,
+        k_scale, v_scale, split_tokens, _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def pa_decode_append_partials(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                              max_context_len: int, scale: float, ws, k_scale: float = 1.0,
+                              v_scale: float = 1.0, split_tokens: int = 0, slot_mapping=None,
+                              stream=None) -> None:
+    """pa_decode_append's append and split phase; pa_decode_merge finishes it."""
+    L = lib()
+    B, nq, hd, nb, bs, nkv = _append_args(q, k_cache, v_cache, k_new, v_new, block_tables,
+                                          context_lens, slot_mapping)
+    _check("pa_decode_append_partials", L.pa_decode_append_partials(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), nb, bs, nkv,
+        hd, nq // nkv, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, max_context_len, scale,
+        k_scale, v_scale, split_tokens, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def pa_decode_merge(out, context_lens, n_kv_heads: int, max_context_len, ws,

@@ -109,7 +109,60 @@ struct DecodeArgs {
   // table row s).  The fp32 chunked prefill runs each query row as a decode
   // row of its own sequence.
   const int32_t* table_row;
+  // The appending decode: token context_lens[s] - 1 of every sequence is
+  // k_new[s] / v_new[s] ([num_seqs][n_kv][HD] of the source dtype), written to
+  // its slot (as pa_kv_append writes it) by the workgroup that reads it
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  int src_f32;               // source dtype: F32 (1) or BF16 (0)
+  float k_inv, v_inv;        // 8-bit caches: 1 / scale, binary32
+  int64_t* slots_out;        // optional: the appended tokens' slots
 };
+
+// 16 cache bytes of a new token row from its source elements, starting at
+// source element e0: a bit copy (F32 or BF16 cache from the same dtype) or 16
+// codes encoded as pa_kv_append encodes them (FP8_E4M3 or INT8 cache).
+template <int CDT>
+__device__ __forceinline__ uint4 new_chunk(const uint8_t* src, int64_t e0, bool src_f32, float inv) {
+  if constexpr (CDT == PA_F32) {
+    return *(const uint4*)(src + e0 * 4);
+  } else if constexpr (CDT == PA_BF16) {
+    return *(const uint4*)(src + e0 * 2);
+  } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (src_f32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 x = *(const uint4*)(src + (e0 + 4 * q) * 4);
+        const uint32_t v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[q] |= encode8<CDT>(bits_f32(v[e]) * inv) << (8 * e);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 x = *(const uint4*)(src + (e0 + 8 * q) * 2);
+        const uint32_t v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = encode8<CDT>(bf16lo_f32(v[e]) * inv);
+          const uint32_t hi = encode8<CDT>(bf16hi_f32(v[e]) * inv);
+          w[2 * q + (e >> 1)] |= (lo | (hi << 8)) << (16 * (e & 1));
+        }
+      }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Slot of token p of a sequence through its table row, or -1 (a negative
+// entry, or p past the row).
+__device__ __forceinline__ int64_t row_slot(const int32_t* row, int max_blocks, int block_size,
+                                            int bs_log2, int p) {
+  if (p < 0 || (p >> bs_log2) >= max_blocks) return -1;
+  const int32_t blk = row[p >> bs_log2];
+  return blk >= 0 ? (int64_t)blk * block_size + (p & (block_size - 1)) : -1;
+}
 
 template <class L>
 struct Frag {
@@ -912,7 +965,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int CDT, int HD, int G, int NBUF, bool STAGED>
+template <int CDT, int HD, int G, int NBUF, bool STAGED, bool APPEND>
 __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kvh, int st0,
                                               int st1, int64_t slot, uint8_t* vl, int wv,
                                               uint8_t* stage) {
@@ -1099,6 +1152,46 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     // loaded value outlives its buffer, so each wait covers exactly the step
     // being staged.
     const MfStageMap<ML> sm = mf_stage_map<ML>(a, wv, lane);
+    // The appending decode: the run that reads the sequence's last token
+    // (position ctx - 1, row tn of step xs) takes its K/V from k_new / v_new.
+    // The lanes that stage that row's chunks encode them, write them to the
+    // token's slot in the cache and, once the step is staged, over the stale
+    // row in LDS; nothing else in the launch reads the slot.
+    uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;
+    uint32_t npos = 0;
+    bool nhave = false;
+    int xs = -1;
+    if constexpr (APPEND) {
+      if (end == ctx) {
+        const int p = ctx - 1;
+        const int tn = p & 15;
+        xs = (p - begin) >> 4;
+        const int rc_log2 = __builtin_ctz((unsigned)(a.hw * ML::ROW / 16));
+        const int rc = 1 << rc_log2;
+        int cc = 0;
+#pragma unroll
+        for (int k = 0; k < ML::LIN; ++k) {
+          const int q = (k * a.hw + wv) * 64 + lane;
+          if ((q >> rc_log2) == tn) { nhave = true; cc = q & (rc - 1); }
+        }
+        const int64_t pslot = row_slot(table, a.max_blocks, a.block_size, a.bs_log2, p);
+        if (nhave) {
+          constexpr int EB = ML::EBITS / 8;
+          const int64_t e0 = ((int64_t)s * a.n_kv + (kvh - wv)) * HD + 16 * cc / EB;
+          const uint8_t* ksrc = a.k_new;
+          const uint8_t* vsrc = a.v_new;
+          nk = new_chunk<CDT>(ksrc, e0, a.src_f32 != 0, a.k_inv);
+          nv = new_chunk<CDT>(vsrc, e0, a.src_f32 != 0, a.v_inv);
+          npos = (uint32_t)(16 * (tn * rc + (cc ^ tn)));
+          if (pslot >= 0 && pslot < (int64_t)a.num_blocks * a.block_size) {
+            const int64_t off = pslot * a.tok_stride + (int64_t)(kvh - wv) * ML::ROW + 16 * cc;
+            *(uint4*)((uint8_t*)a.k_cache + off) = nk;
+            *(uint4*)((uint8_t*)a.v_cache + off) = nv;
+          }
+        }
+        if (a.slots_out && kvh - wv == 0 && wv == 0 && lane == 0) a.slots_out[s] = pslot;
+      }
+    }
     float* vsl = (float*)(stage + 4 * ML::STAGE) + wv * 16 + 4 * j;   // + parity * 16 * DECODE_MAX_HW
     const int64_t hg_off = (int64_t)(kvh - wv) * ML::ROW;   // the head group's first row byte
     const __amdgpu_buffer_rsrc_t tr = make_rsrc(table, (jlast + 1) * 4);
@@ -1140,6 +1233,12 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
       if constexpr (CDT == PA_INT4) {
         if (r == 0)
           *(float4*)(vsl + (x & 1) * 16 * DECODE_MAX_HW) = make_float4(f.vs[0], f.vs[1], f.vs[2], f.vs[3]);
+      }
+      if constexpr (APPEND) {   // the new token's row over the stale one (same lane, after it)
+        if (x == xs && nhave) {
+          *(uint4*)(sk + npos) = nk;
+          *(uint4*)(sk + ML::STAGE + npos) = nv;
+        }
       }
     };
     auto run = [&](int x) {
@@ -1207,7 +1306,7 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 #ifndef DECODE_MF_MIN_WGS
 #define DECODE_MF_MIN_WGS 1   // workgroups per CU the register budget must allow
 #endif
-template <int CDT, int HD, int G, int NBUF, bool STAGED>
+template <int CDT, int HD, int G, int NBUF, bool STAGED, bool APPEND>
 __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_mfma_kernel(DecodeArgs a) {
   using ML = MfLayout<CDT, HD>;
   // per-wave V slices (none when bf16 V is read from the stage), then (staged)
@@ -1222,6 +1321,11 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   int pre, U;
   unit_counts(a.context_lens, a.num_seqs, a.nhg, 0, &pre, &U);
   if (w == 0 && threadIdx.x == 0) *(int2*)a.header = make_int2(W, a.hw);   // for the merge
+  if constexpr (APPEND) {   // sequences without tokens append nothing: slot -1
+    if (w == 0 && a.slots_out)
+      for (int i = threadIdx.x; i < a.num_seqs; i += blockDim.x)
+        if (a.context_lens[i] <= 0) a.slots_out[i] = -1;
+  }
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
   int s, before;
@@ -1230,21 +1334,27 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   const int rr = (int)u0 - before;
   int hg = rr / steps0;
   int step = rr % steps0;
-  int64_t u = u0;
   uint8_t* vl = lds + (SLICES ? wv * ML::WAVE_LDS : 0);
-  while (true) {
-    const int steps = steps_of(uniform_load(a.context_lens, s));
-    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
-    const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
-    decode_run_mf<CDT, HD, G, NBUF, STAGED>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv,
-                                            vl, wv, lds + SLICES);
-    u += run_end - step;
-    if (u >= u1) break;
+  auto run = [&](int rs, int rhg, int first, int last) {
+    const int64_t slot = (int64_t)w + (int64_t)rs * a.nhg + rhg;
+    decode_run_mf<CDT, HD, G, NBUF, STAGED, APPEND>(a, rs, rhg * a.hw + wv, first, last,
+                                                    slot * a.hw + wv, vl, wv, lds + SLICES);
+  };
+  auto next_segment = [&]() {
     step = 0;
     if (++hg == a.nhg) {               // next sequence that has tokens
       hg = 0;
       do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
     }
+  };
+  int64_t u = u0;
+  while (true) {
+    const int steps = steps_of(uniform_load(a.context_lens, s));
+    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
+    run(s, hg, step, run_end);
+    u += run_end - step;
+    if (u >= u1) break;
+    next_segment();
   }
 }
 
@@ -1473,7 +1583,7 @@ static int64_t resident_wgs_mf(int hw) {
   if (!cached[hw]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>, 64 * hw, 0) != hipSuccess ||
+            &per_cu, decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED, false>, 64 * hw, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     const int target = (DECODE_WAVES_PER_CU + hw - 1) / hw;
@@ -1483,14 +1593,53 @@ static int64_t resident_wgs_mf(int hw) {
   return cached[hw];
 }
 
+// The split is sized by the plain kernel in both cases, so the appending
+// launch cuts the work at the same points (bit-identical results).
 template <int CDT, int HD, int G, bool STAGED>
 static pa_status launch_mf(const DecodeArgs& a, int split_tokens, int64_t bound, hipStream_t st) {
   DecodeArgs b = a;
   int64_t W = split_tokens <= 0 ? resident_wgs_mf<CDT, HD, G, STAGED>(a.hw) : bound;
   if (W > bound) W = bound;
   b.num_wgs = (int)W;
-  return launch(decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED>, dim3((unsigned)W),
+  if constexpr (STAGED) {
+    if (a.k_new)
+      return launch(decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED, true>, dim3((unsigned)W),
+                    dim3(64 * a.hw), 0, st, b);
+  }
+  return launch(decode_mfma_kernel<CDT, HD, G, mf_nbuf(CDT), STAGED, false>, dim3((unsigned)W),
                 dim3(64 * a.hw), 0, st, b);
+}
+
+// The appending decode on paths that do not stage whole rows: the new tokens
+// go to their slots in a launch of their own first.  Workgroup (s, y, K/V)
+// writes 16-byte chunks of sequence s's token context_lens[s] - 1.
+template <int CDT>
+__global__ __launch_bounds__(256) void append_rows_kernel(DecodeArgs a, int chunks_per_row) {
+  constexpr int EB = CDT == PA_F32 ? 4 : CDT == PA_BF16 ? 2 : 1;
+  const int s = blockIdx.x;
+  const bool is_v = blockIdx.z != 0;
+  const int64_t slot = row_slot(a.block_tables + (int64_t)s * a.max_blocks, a.max_blocks,
+                                a.block_size, a.bs_log2, a.context_lens[s] - 1);
+  if (!is_v && blockIdx.y == 0 && threadIdx.x == 0 && a.slots_out) a.slots_out[s] = slot;
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * a.block_size) return;
+  uint8_t* dst = (uint8_t*)(is_v ? a.v_cache : a.k_cache) + slot * a.tok_stride;
+  const int64_t row0 = (int64_t)s * (a.tok_stride / EB);   // first source element of the row
+  for (int c = blockIdx.y * 256 + threadIdx.x; c < chunks_per_row; c += gridDim.y * 256)
+    *(uint4*)(dst + 16 * c) = new_chunk<CDT>(is_v ? a.v_new : a.k_new, row0 + 16 * c / EB,
+                                              a.src_f32 != 0, is_v ? a.v_inv : a.k_inv);
+}
+
+template <int CDT>
+static pa_status append_rows(DecodeArgs& a, hipStream_t st) {
+  if constexpr (CDT == PA_INT4) {
+    return PA_ERR_DTYPE;
+  } else {
+    const int chunks = (int)(a.tok_stride / 16);
+    const dim3 grid((unsigned)a.num_seqs, (unsigned)((chunks + 255) / 256), 2);
+    const pa_status e = launch(append_rows_kernel<CDT>, grid, dim3(256), 0, st, a, chunks);
+    a.k_new = a.v_new = nullptr;   // appended: the decode reads them from the cache
+    return e;
+  }
 }
 
 template <int CDT, int HD, int G>
@@ -1505,7 +1654,11 @@ static pa_status launch_split(DecodeArgs a, int split_tokens, int max_context_le
     if (mf) {
       if constexpr (mf_stageable_layout<CDT, HD>() && DECODE_MF_STAGED) {
         if (mf_staged_ok(MfLayout<CDT, HD>::ROW, hw))
-          return launch_mf<CDT, HD, G, true>(a, split_tokens, bound, st);
+          return launch_mf<CDT, HD, G, true>(a, split_tokens, bound, st);   // appends in the kernel
+      }
+      if (a.k_new) {
+        const pa_status e = append_rows<CDT>(a, st);
+        if (e != PA_OK) return e;
       }
       return launch_mf<CDT, HD, G, false>(a, split_tokens, bound, st);
     }
@@ -1513,6 +1666,10 @@ static pa_status launch_split(DecodeArgs a, int split_tokens, int max_context_le
   int64_t W = split_tokens <= 0 ? resident_wgs<CDT, HD, G>(hw) : bound;
   if (W > bound) W = bound;
   a.num_wgs = (int)W;
+  if (a.k_new) {
+    const pa_status e = append_rows<CDT>(a, st);
+    if (e != PA_OK) return e;
+  }
   return launch(decode_split_kernel<CDT, HD, G, DECODE_NBUF>, dim3((unsigned)W), dim3(64 * hw), 0,
                 st, a);
 }
@@ -1608,7 +1765,9 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
                              size_t workspace_bytes, void* stream,
                              const float* k_channel_scales = nullptr,
                              const float* v_token_scales = nullptr,
-                             const int32_t* table_row = nullptr) {
+                             const int32_t* table_row = nullptr,
+                             const void* k_new = nullptr, const void* v_new = nullptr,
+                             int src_dtype = -1, int64_t* slots_out = nullptr) {
   pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len, split_tokens);
   if (e != PA_OK) return e;
   if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
@@ -1629,6 +1788,16 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   // 8-bit caches (fp8 or int8) carry per-tensor scales
   const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
   if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f))) return PA_ERR_SHAPE;
+  const bool append = src_dtype >= 0;
+  if (append) {
+    // the append's pairs: a bit copy for F32 and BF16 caches, an encode from
+    // F32 or BF16 rows for FP8_E4M3 and INT8 caches (INT4: pa_kv_append_int4)
+    const bool src_ok = fp8 ? (src_dtype == PA_F32 || src_dtype == PA_BF16)
+                            : (!int4 && src_dtype == cache_dtype);
+    if (!src_ok) return PA_ERR_DTYPE;
+    if (!k_new || !v_new) return PA_ERR_NULL;
+    if (((uintptr_t)k_new | (uintptr_t)v_new) & 15) return PA_ERR_SHAPE;
+  }
 
   char* base = (char*)workspace;
   DecodeArgs a;
@@ -1657,6 +1826,12 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.k_ch_scale = k_channel_scales;
   a.v_tok_scale = v_token_scales;
   a.table_row = table_row;
+  a.k_new = append ? (const uint8_t*)k_new : nullptr;
+  a.v_new = append ? (const uint8_t*)v_new : nullptr;
+  a.src_f32 = src_dtype == PA_F32;
+  a.k_inv = fp8 ? 1.0f / k_scale : 1.0f;   // one binary32 division each, as pa_kv_append
+  a.v_inv = fp8 ? 1.0f / v_scale : 1.0f;
+  a.slots_out = append ? slots_out : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   if (cache_dtype == PA_BF16) e = dispatch_hd<PA_BF16>(head_dim, G, a, split_tokens, max_context_len, st);
@@ -1697,6 +1872,45 @@ extern "C" pa_status pa_decode_partials(const void* q, int q_dtype, const void* 
                      block_size, n_kv_heads, head_dim, group_size, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
                      1.0f, split_tokens, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_append(void* out, const void* q, int q_dtype, void* k_cache,
+                                      void* v_cache, int cache_dtype, int32_t num_blocks,
+                                      int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t group_size, const void* k_new, const void* v_new,
+                                      int src_dtype, int64_t* slot_mapping,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t max_context_len, float scale, float k_scale,
+                                      float v_scale, int32_t split_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (src_dtype < 0) return PA_ERR_DTYPE;
+  return decode_impl(out, true, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, n_kv_heads, head_dim, group_size, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
+                     v_scale, split_tokens, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     nullptr, k_new, v_new, src_dtype, slot_mapping);
+}
+
+extern "C" pa_status pa_decode_append_partials(const void* q, int q_dtype, void* k_cache,
+                                               void* v_cache, int cache_dtype, int32_t num_blocks,
+                                               int32_t block_size, int32_t n_kv_heads,
+                                               int32_t head_dim, int32_t group_size,
+                                               const void* k_new, const void* v_new,
+                                               int src_dtype, int64_t* slot_mapping,
+                                               const int32_t* block_tables,
+                                               int32_t max_blocks_per_seq,
+                                               const int32_t* context_lens, int32_t num_seqs,
+                                               int32_t max_context_len, float scale,
+                                               float k_scale, float v_scale,
+                                               int32_t split_tokens, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  if (src_dtype < 0) return PA_ERR_DTYPE;
+  return decode_impl(nullptr, false, q, q_dtype, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, n_kv_heads, head_dim, group_size, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale, k_scale,
+                     v_scale, split_tokens, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     nullptr, k_new, v_new, src_dtype, slot_mapping);
 }
 
 extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* context_lens,

@@ -72,47 +72,6 @@ __device__ __forceinline__ SegRange seg_range(const SegMap& m, int s) {
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// e4m3 (OCP e4m3fn) encoder: saturate to +-448, round half to even, NaN -> 0x7F.
-// Integer-only, so the result never depends on the device's float modes.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = f32_bits(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;                 // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;         // |x| >= 448 (and inf): saturate
-  const int e = (int)(a >> 23) - 127;                // unbiased binary32 exponent
-  const uint32_t m = (a & 0x7fffffu) | 0x800000u;    // 24-bit significand (normal input)
-  // value = m * 2^(e-23).  Normal e4m3 (e >= -6) keeps 3 fraction bits:
-  // q = m >> 20 in [8, 16); subnormal e4m3 counts units of 2^-9: q = m >> (14 - e).
-  const int shift = e >= -6 ? 20 : 14 - e;
-  if (shift >= 26) return sign;                      // below a quarter unit: +-0
-  const uint32_t q = m >> shift;
-  const uint32_t rem = m & ((1u << shift) - 1u);
-  const uint32_t half = 1u << (shift - 1);
-  const uint32_t r = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
-  // Normal: code = (e + 7) * 8 + (r - 8); r == 16 carries into the exponent.
-  // Subnormal: code = r (r == 8 is the smallest normal, code 0x08).
-  const uint32_t code = e >= -6 ? (uint32_t)((e + 7) * 8) + r - 8u : r;
-  return sign | code;
-}
-
-// int8 encoder: round half to even, clamp to [-127, 127], NaN -> 0.  (The
-// clamp before the rounding changes no result: every value beyond +-127 ends
-// at +-127 either way.)
-__device__ __forceinline__ uint32_t f32_to_int8(float x) {
-  if (!(x == x)) return 0u;
-  const float r = __builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
-  return (uint32_t)(int32_t)r & 0xffu;
-}
-
-template <int DST>
-__device__ __forceinline__ uint32_t encode8(float x) {
-  if constexpr (DST == PA_FP8_E4M3) return f32_to_e4m3(x);
-  else return f32_to_int8(x);
-}
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming 16-byte read of source rows (read once, not kept in cache).
