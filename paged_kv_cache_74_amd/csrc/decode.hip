@@ -811,7 +811,7 @@ struct MfLayout {
   static constexpr int DPP = PS * 8 / EBITS;     // dims per piece
   static constexpr int NT = HD / 32;             // QK MFMAs (16x16x32) per step
   static constexpr int NB = HD / 16;             // PV MFMAs (16x16x16) per step
-  static constexpr int VROW = HD * 2 + 32;       // LDS bytes per token row of V (bf16, padded)
+  static constexpr int VROW = HD * 2;            // LDS bytes per token row of V (bf16)
   static constexpr int WAVE_LDS = 16 * VROW;
   // staged loads: 16-byte chunks per lane per step, and the bytes of one
   // tensor's stage (16 tokens of up to DECODE_MAX_HW heads)
@@ -838,6 +838,22 @@ __host__ __device__ inline bool mf_staged_ok(int row_bytes, int hw) {
 #ifndef DECODE_MF_AUX
 #define DECODE_MF_AUX DECODE_LOAD_AUX
 #endif
+// A wave's V slice (16 token rows of bf16) is swizzled: 16-byte chunk c of
+// token row t sits at chunk c ^ vslice_g(t) of the row.  The slice writes put
+// one chunk of each of 16 rows, the transposed reads take two adjacent chunks
+// of 4 (8) consecutive rows per 16 (32) lanes; with this map both spread over
+// every LDS bank (a padded row could serve only one of the two: the padding of
+// 32 bytes left two rows on each bank group of the writes).
+template <int HD>
+__device__ __forceinline__ int vslice_g(int t) {
+  if constexpr (HD == 128) return ((t & 7) << 1) | ((t >> 3) & 1);
+  else return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
+}
+template <int HD>
+__device__ __forceinline__ uint32_t vslice_off(int t, int byte) {
+  return (uint32_t)(t * 2 * HD + 16 * ((byte >> 4) ^ vslice_g<HD>(t)) + (byte & 15));
+}
+
 // First dim of the 8 dims that MFMA t of a step takes from lane group j.
 template <class ML>
 __device__ __forceinline__ int mf_dim0(int t, int j) {
@@ -1042,6 +1058,15 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
   // the wave needs no V slice of its own.
   constexpr bool VDIRECT = STAGED && CDT == PA_BF16;
   uint32_t vrd[VDIRECT ? ML::NB : 1];
+  // otherwise the slice's write offsets (token r, this lane's dims of MFMA t)
+  // and transposed-read offsets (tokens 4j .. 4j+3, dims 16 b + r)
+  uint32_t vwo[VDIRECT ? 1 : ML::NT], vro[VDIRECT ? 1 : ML::NB];
+  if constexpr (!VDIRECT) {
+#pragma unroll
+    for (int t = 0; t < ML::NT; ++t) vwo[t] = vslice_off<HD>(r, 2 * mf_dim0<ML>(t, j));
+#pragma unroll
+    for (int b = 0; b < ML::NB; ++b) vro[b] = vslice_off<HD>(4 * j + (r >> 2), 32 * b + 8 * (r & 3));
+  }
   if constexpr (VDIRECT) {
     constexpr int CPR = ML::ROW / 16;        // 16-byte chunks of one head's row
     const int rc = a.hw * CPR;
@@ -1062,11 +1087,10 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_k8<CDT>(fk + DW8 * t), qb[t], sc, 0, 0, 0);
     // V rows (bf16) into this wave's LDS slice: token r, this lane's dims
     if constexpr (!VDIRECT) {
-      uint8_t* row = vl + r * ML::VROW;
 #pragma unroll
       for (int t = 0; t < ML::NT; ++t) {
         const mf_bf16x8_t v8 = mf_k8<CDT>(fv + DW8 * t);
-        *(uint4*)(row + 2 * mf_dim0<ML>(t, j)) = __builtin_bit_cast(uint4, v8);
+        *(uint4*)(vl + vwo[t]) = __builtin_bit_cast(uint4, v8);
       }
     }
     // softmax of column r over the step's 16 tokens
@@ -1108,12 +1132,11 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
     }
     const mf_s4_t pa4 = __builtin_bit_cast(mf_s4_t, make_uint2(P0, P1));
     // V^T blocks: lane (j, r) gets tokens 4j .. 4j+3 of LDS column 16 b + r
-    const uint8_t* rd = vl + (4 * j + (r >> 2)) * ML::VROW + (r & 3) * 8;
 #pragma unroll
     for (int b = 0; b < ML::NB; ++b) {
       const uint8_t* src;
       if constexpr (VDIRECT) src = vsrc + vrd[b];
-      else src = rd + 32 * b;
+      else src = vl + vro[b];
       const mf_s4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) mf_s4_t*)src);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb, acc[b], 0, 0, 0);

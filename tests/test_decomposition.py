@@ -360,3 +360,53 @@ def test_int4_append_reads_stay_in_bounds(head_dim):
                 bad += (t2 * n_kv + h2) * head_dim + j2 * 8 + 8 > src_elems
             # the unclamped piece index reads past the rows whenever lanes are idle
             assert (bad > 0) == (grid > total)
+
+
+def vslice_off(hd, t, byte):
+    """Byte of (token row t, byte) in a wave's swizzled V slice of the matrix-core
+    decode: 16-byte chunk c of row t at chunk c ^ g(t)."""
+    g = (((t & 7) << 1) | ((t >> 3) & 1)) if hd == 128 else ((((t >> 1) & 3) << 1) | ((t >> 3) & 1))
+    return t * 2 * hd + 16 * ((byte >> 4) ^ g) + (byte & 15)
+
+
+def mf_dim0(t, j, hd, ebits):
+    dpj = hd // 4
+    ps = min(dpj * ebits // 8, 16)
+    dpp = ps * 8 // ebits
+    cpp = dpp // 8
+    return (j + 4 * (t // cpp)) * dpp + 8 * (t % cpp)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("ebits", [8, 4])
+def test_decode_vslice_swizzle(hd, ebits):
+    """The V slice map is a bijection of each row's bytes; the slice writes (16 lanes,
+    16 bytes each) and the transposed reads (32 lanes, 8 bytes each) touch 16 and 32
+    different 16- / 8-byte bank groups of the 64 x 4-byte banks; and every lane's
+    transposed read finds the bytes the writing lane put there."""
+    rb = 2 * hd
+    for t in range(16):
+        assert sorted(vslice_off(hd, t, b) for b in range(rb)) == list(range(t * rb, (t + 1) * rb))
+    written = {}
+    for tt in range(hd // 32):
+        for grp in range(4):
+            groups = []
+            for lane in range(16 * grp, 16 * grp + 16):
+                j, r = lane >> 4, lane & 15
+                byte = 2 * mf_dim0(tt, j, hd, ebits)
+                off = vslice_off(hd, r, byte)
+                groups.append((off // 16) % 16)
+                for k in range(16):
+                    written[vslice_off(hd, r, byte + k)] = (r, byte + k)
+            assert len(set(groups)) == 16
+    for b in range(hd // 16):
+        for grp in range(2):
+            slots = []
+            for lane in range(32 * grp, 32 * grp + 32):
+                j, r = lane >> 4, lane & 15
+                row, byte = 4 * j + (r >> 2), 32 * b + 8 * (r & 3)
+                off = vslice_off(hd, row, byte)
+                slots.append((off // 8) % 32)
+                for k in range(8):
+                    assert written[vslice_off(hd, row, byte + k)] == (row, byte + k)
+            assert len(set(slots)) == 32
