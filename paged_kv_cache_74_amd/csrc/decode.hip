@@ -786,7 +786,7 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
 //   * staged (STAGED): the workgroup's waves load the step's rows of all its
 //     heads together, each instruction covering 1 KiB of whole token rows in
 //     order, write them to a double-buffered LDS stage (16-byte chunks XOR-
-//     swizzled by token, so neither the writes nor the per-head reads conflict)
+//     swizzled by token, so its writes and reads meet no bank conflicts)
 //     and each wave reads its head's pieces back from there.  One barrier per
 //     step; a step is written to the stage one step before it is read.  Long
 //     runs of whole rows stream from HBM faster than per-head pieces.
@@ -838,16 +838,29 @@ __host__ __device__ inline bool mf_staged_ok(int row_bytes, int hw) {
 #ifndef DECODE_MF_AUX
 #define DECODE_MF_AUX DECODE_LOAD_AUX
 #endif
-// A wave's V slice (16 token rows of bf16) is swizzled: 16-byte chunk c of
-// token row t sits at chunk c ^ vslice_g(t) of the row.  The slice writes put
-// one chunk of each of 16 rows, the transposed reads take two adjacent chunks
-// of 4 (8) consecutive rows per 16 (32) lanes; with this map both spread over
-// every LDS bank (a padded row could serve only one of the two: the padding of
-// 32 bytes left two rows on each bank group of the writes).
+// LDS bank groups, as the SQ bank-conflict counter shows them on gfx950: a
+// 16-byte access (ds_read_b128 / ds_write_b128) is served 8 lanes at a time,
+// free of conflicts when the 8 chunks differ in bits 4..6 of their addresses
+// (a 128-byte window); ds_read_b64_tr_b16 is served 32 lanes at a time, free
+// when the 32 pieces differ in bits 3..7 (a 256-byte window).
+//
+// Rows of 16 tokens in LDS (the load stage, a wave's V slice) keep 16-byte
+// chunk c of token row t at chunk c ^ row_g(t).  Over any 8 consecutive rows
+// row_g takes 8 different values mod 8 (so one chunk of 8 rows, the slice
+// writes and the stage's per-head reads, fills a 128-byte window) and 8
+// different values of row_g / 2 (so a 32-byte pair of chunks of 8 rows, the
+// transposed reads, fills a 256-byte window); whole 128-byte runs of one row
+// (the stage writes) stay whole.  (t ^ c alone left two rows per pair of
+// chunks in the transposed reads; t << 1 alone, two rows per window in the
+// slice writes.)
+__device__ __forceinline__ int row_g(int t) { return ((t & 7) << 1) | ((t >> 2) & 1); }
+// A wave's V slice (16 token rows of bf16): rows of 256 bytes (head_dim 128)
+// take row_g; rows of 128 bytes (head_dim 64) sit two to a 256-byte window,
+// so t & 7 spreads both kinds of access there.
 template <int HD>
 __device__ __forceinline__ int vslice_g(int t) {
-  if constexpr (HD == 128) return ((t & 7) << 1) | ((t >> 3) & 1);
-  else return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
+  if constexpr (HD == 128) return row_g(t);
+  else return t & 7;
 }
 template <int HD>
 __device__ __forceinline__ uint32_t vslice_off(int t, int byte) {
@@ -963,12 +976,12 @@ __device__ __forceinline__ MfStageMap<ML> mf_stage_map(const DecodeArgs& a, int 
     const int q = (k * a.hw + wv) * 64 + lane;   // chunk of the step, in memory order
     const int t = q >> rc_log2, c = q & (rc - 1);
     m.goff[k] = (uint32_t)(t * (int)a.tok_stride + 16 * c);
-    m.wpos[k] = (uint32_t)(16 * (t * rc + (c ^ t)));
+    m.wpos[k] = (uint32_t)(16 * (t * rc + (c ^ row_g(t))));
   }
 #pragma unroll
   for (int k = 0; k < ML::NP; ++k) {
     const int c = wv * (ML::ROW / 16) + j + 4 * k;   // piece k of lane group j, head wv
-    m.rpos[k] = (uint32_t)(16 * (r * rc + (c ^ r)));
+    m.rpos[k] = (uint32_t)(16 * (r * rc + (c ^ row_g(r))));
   }
   return m;
 }
@@ -1074,7 +1087,7 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
 #pragma unroll
     for (int b = 0; b < ML::NB; ++b) {
       const int c = wv * CPR + 2 * b + ((r >> 1) & 1);   // chunk of bytes 32 b + 8 (r % 4)
-      vrd[b] = (uint32_t)(16 * (t * rc + (c ^ t)) + 8 * (r & 1));
+      vrd[b] = (uint32_t)(16 * (t * rc + (c ^ row_g(t))) + 8 * (r & 1));
     }
   }
 
@@ -1205,7 +1218,7 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
           const uint8_t* vsrc = a.v_new;
           nk = new_chunk<CDT>(ksrc, e0, a.src_f32 != 0, a.k_inv);
           nv = new_chunk<CDT>(vsrc, e0, a.src_f32 != 0, a.v_inv);
-          npos = (uint32_t)(16 * (tn * rc + (cc ^ tn)));
+          npos = (uint32_t)(16 * (tn * rc + (cc ^ row_g(tn))));
           if (pslot >= 0 && pslot < (int64_t)a.num_blocks * a.block_size) {
             const int64_t off = pslot * a.tok_stride + (int64_t)(kvh - wv) * ML::ROW + 16 * cc;
             *(uint4*)((uint8_t*)a.k_cache + off) = nk;

@@ -245,6 +245,41 @@ def test_prefill_planner_workgroup_starts():
                 assert tile == x - cu[g]
 
 
+def row_g(t):
+    """Chunk swizzle of token row t in the decode kernel's LDS rows."""
+    return ((t & 7) << 1) | ((t >> 2) & 1)
+
+
+# LDS bank groups as gfx950's SQ_LDS_BANK_CONFLICT counter shows them (one access
+# pattern per probe kernel): 16-byte accesses are served 8 lanes at a time and
+# conflict unless the 8 chunks differ in address bits 4..6; ds_read_b64_tr_b16 is
+# served 32 lanes at a time and conflicts unless the 32 pieces differ in bits 3..7.
+def b128_conflict_free(offsets):
+    return all(len({(o >> 4) & 7 for o in offsets[g:g + 8]}) == 8 for g in range(0, 64, 8))
+
+
+def tr64_conflict_free(offsets):
+    return all(len({(o >> 3) & 31 for o in offsets[g:g + 32]}) == 32 for g in (0, 32))
+
+
+def test_bank_model_separates_the_measured_patterns():
+    """The model above reproduces what the counter showed: a conflict for the
+    slice writes with row swizzle ((t & 7) << 1) | (t >> 3), for rows padded to
+    288 bytes, and for transposed reads of a stage swizzled by c ^ t; none for
+    row_g, linear runs or the padded rows' transposed reads."""
+    lanes = [(l >> 4, l & 15) for l in range(64)]
+    old_g = lambda t: ((t & 7) << 1) | ((t >> 3) & 1)
+    assert not b128_conflict_free([r * 256 + 16 * ((2 * j) ^ old_g(r)) for j, r in lanes])
+    assert not b128_conflict_free([r * 288 + 32 * j for j, r in lanes])
+    assert b128_conflict_free([r * 256 + 16 * ((2 * j) ^ row_g(r)) for j, r in lanes])
+    assert b128_conflict_free([16 * l for l in range(64)])
+    tr = lambda j, r: (4 * j + (r >> 2), (r >> 1) & 1, 8 * (r & 1))
+    assert not tr64_conflict_free([t * 1024 + 16 * (cb ^ t) + h for t, cb, h in (tr(j, r) for j, r in lanes)])
+    assert tr64_conflict_free([t * 1024 + 16 * (cb ^ row_g(t)) + h for t, cb, h in (tr(j, r) for j, r in lanes)])
+    assert tr64_conflict_free([t * 288 + 16 * cb + h for t, cb, h in (tr(j, r) for j, r in lanes)])
+    assert tr64_conflict_free([8 * l for l in range(64)])
+
+
 def stage_maps(hw, row):
     """The staged decode load maps for one head group: per (wave, lane, k) the
     (token, 16-byte chunk) a lane loads and the stage slot it writes, and per
@@ -256,14 +291,14 @@ def stage_maps(hw, row):
             for k in range(row // 64):
                 q = (k * hw + wv) * 64 + lane
                 t, c = q // rc, q % rc
-                loads[(wv, lane, k)] = ((t, c), t * rc + (c ^ t))
+                loads[(wv, lane, k)] = ((t, c), t * rc + (c ^ row_g(t)))
     reads = {}
     for wv in range(hw):
         for lane in range(64):
             j, r = lane >> 4, lane & 15
             for k in range(row // 64):
                 c = wv * (row // 16) + j + 4 * k
-                reads[(wv, lane, k)] = ((r, c), r * rc + (c ^ r))
+                reads[(wv, lane, k)] = ((r, c), r * rc + (c ^ row_g(r)))
     return rc, loads, reads
 
 
@@ -272,8 +307,9 @@ def stage_maps(hw, row):
 def test_decode_stage_maps(hw, row):
     """Every chunk of a step is loaded once, lands in a distinct stage slot, and
     each lane reads back the piece of its own head that the per-head layout
-    gives it (token r, chunk j + 4k of head wv's row); neither the writes nor
-    the reads of 16 consecutive lanes share a 16-byte bank group."""
+    gives it (token r, chunk j + 4k of head wv's row); the stage writes, the
+    per-head reads and (bf16 rows) the transposed V reads meet no bank conflict
+    in the model above."""
     rc, loads, reads = stage_maps(hw, row)
     assert (hw * row) % 256 == 0 and row >= 64          # where the kernel stages
     chunks = [tc for tc, _ in loads.values()]
@@ -285,22 +321,23 @@ def test_decode_stage_maps(hw, row):
     for table in (loads, reads):
         for wv in range(hw):
             for k in range(row // 64):
-                for g in range(4):
-                    banks = [table[(wv, lane, k)][1] % 16 for lane in range(16 * g, 16 * g + 16)]
-                    assert len(set(banks)) == 16, (wv, k, g)
+                assert b128_conflict_free([16 * table[(wv, lane, k)][1] for lane in range(64)])
     if row % 128 == 0:
         # bf16 rows: the transposed V reads go to the stage directly.  Lane
         # (j, r) of head wv, block b wants the 8 bytes at 32 b + 8 (r % 4) of
         # token 4 j + r / 4's row: chunk 2 b + (r / 2) % 2, half r % 2.
         cpr = row // 16
         for wv in range(hw):
-            for lane in range(64):
-                j, r = lane >> 4, lane & 15
-                t = 4 * j + (r >> 2)
-                for b in range(row // 32):
+            for b in range(row // 32):
+                offs = []
+                for lane in range(64):
+                    j, r = lane >> 4, lane & 15
+                    t = 4 * j + (r >> 2)
                     c = wv * cpr + 2 * b + ((r >> 1) & 1)
-                    pos = t * rc + (c ^ t)
+                    pos = t * rc + (c ^ row_g(t))
                     assert slots[pos] == (t, c), (wv, lane, b)
+                    offs.append(16 * pos + 8 * (r & 1))
+                assert tr64_conflict_free(offs), (wv, b)
 
 
 def test_decode_split_quotients_in_double_are_exact():
@@ -365,7 +402,7 @@ def test_int4_append_reads_stay_in_bounds(head_dim):
 def vslice_off(hd, t, byte):
     """Byte of (token row t, byte) in a wave's swizzled V slice of the matrix-core
     decode: 16-byte chunk c of row t at chunk c ^ g(t)."""
-    g = (((t & 7) << 1) | ((t >> 3) & 1)) if hd == 128 else ((((t >> 1) & 3) << 1) | ((t >> 3) & 1))
+    g = row_g(t) if hd == 128 else (t & 7)
     return t * 2 * hd + 16 * ((byte >> 4) ^ g) + (byte & 15)
 
 
@@ -380,33 +417,29 @@ def mf_dim0(t, j, hd, ebits):
 @pytest.mark.parametrize("hd", [64, 128])
 @pytest.mark.parametrize("ebits", [8, 4])
 def test_decode_vslice_swizzle(hd, ebits):
-    """The V slice map is a bijection of each row's bytes; the slice writes (16 lanes,
-    16 bytes each) and the transposed reads (32 lanes, 8 bytes each) touch 16 and 32
-    different 16- / 8-byte bank groups of the 64 x 4-byte banks; and every lane's
-    transposed read finds the bytes the writing lane put there."""
+    """The V slice map is a bijection of each row's bytes; the slice writes (16
+    bytes a lane) and the transposed reads (8 bytes a lane) meet no bank conflict
+    in the model above; and every lane's transposed read finds the bytes the
+    writing lane put there."""
     rb = 2 * hd
     for t in range(16):
         assert sorted(vslice_off(hd, t, b) for b in range(rb)) == list(range(t * rb, (t + 1) * rb))
     written = {}
     for tt in range(hd // 32):
-        for grp in range(4):
-            groups = []
-            for lane in range(16 * grp, 16 * grp + 16):
-                j, r = lane >> 4, lane & 15
-                byte = 2 * mf_dim0(tt, j, hd, ebits)
-                off = vslice_off(hd, r, byte)
-                groups.append((off // 16) % 16)
-                for k in range(16):
-                    written[vslice_off(hd, r, byte + k)] = (r, byte + k)
-            assert len(set(groups)) == 16
+        offs = []
+        for lane in range(64):
+            j, r = lane >> 4, lane & 15
+            byte = 2 * mf_dim0(tt, j, hd, ebits)
+            offs.append(vslice_off(hd, r, byte))
+            for k in range(16):
+                written[vslice_off(hd, r, byte + k)] = (r, byte + k)
+        assert b128_conflict_free(offs), tt
     for b in range(hd // 16):
-        for grp in range(2):
-            slots = []
-            for lane in range(32 * grp, 32 * grp + 32):
-                j, r = lane >> 4, lane & 15
-                row, byte = 4 * j + (r >> 2), 32 * b + 8 * (r & 3)
-                off = vslice_off(hd, row, byte)
-                slots.append((off // 8) % 32)
-                for k in range(8):
-                    assert written[vslice_off(hd, row, byte + k)] == (row, byte + k)
-            assert len(set(slots)) == 32
+        offs = []
+        for lane in range(64):
+            j, r = lane >> 4, lane & 15
+            row, byte = 4 * j + (r >> 2), 32 * b + 8 * (r & 3)
+            offs.append(vslice_off(hd, row, byte))
+            for k in range(8):
+                assert written[vslice_off(hd, row, byte + k)] == (row, byte + k)
+        assert tr64_conflict_free(offs), b
