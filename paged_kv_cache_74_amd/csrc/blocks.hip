@@ -10,10 +10,13 @@
 // (which the kernel reads or writes directly over the host link).
 //
 // The copy is bandwidth bound: each workgroup moves one 16 KiB chunk of one
-// block of K or V with 16-byte (8-byte when the block size needs it)
-// non-temporal loads and stores, all of a lane's loads issued before its
-// stores, so a batch of pairs spreads over the whole chip with many reads in
-// flight.
+// block of K or V with 16-byte (8-byte when the block size needs it) loads and
+// stores, all of a lane's loads issued before its stores, so a batch of pairs
+// spreads over the whole chip with many reads in flight.  The loads are
+// non-temporal (the source is read once); the stores are ordinary: measured
+// on 4096 Llama-3 block pairs, 6.3 TB/s of reads plus writes against 5.0 TB/s
+// with non-temporal stores (and 5.4 TB/s for hipMemcpyAsync of the same bytes
+// as one contiguous device-to-device copy).
 #include "pa_device.h"
 
 namespace pa {
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(CB_THREADS) void copy_blocks_kernel(
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int64_t off = base + (int64_t)i * CB_THREADS * VEC;
-    if (off < end) __builtin_nontemporal_store(x[i], (V*)(dst + off));
+    if (off < end) *(V*)(dst + off) = x[i];
   }
 }
 
