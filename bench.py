@@ -410,6 +410,31 @@ def block_copy_bench(args, torch, np, pa):
     step_ms = wall * 1e3 / args.steps
     log(f"{what}: {per_call * 1e3:.1f} us per call -> {gbs:.1f} GB/s through the {bound} "
         f"({gbs / peak:.1%} of {peak:.0f} GB/s)")
+    # measured ceiling: the same bytes as one contiguous copy (device to device, or out to
+    # pinned host memory and back) through torch's copy, timed the same way
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if bound == "hbm":
+        dst = torch.empty_like(src)
+        ops = [lambda: dst.copy_(src)]
+    else:
+        host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        ops = [lambda: host.copy_(src, non_blocking=True), lambda: src.copy_(host, non_blocking=True)]
+    for _ in range(args.warmup):
+        for o in ops:
+            o()
+    torch.cuda.synchronize()
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps * len(ops))]
+    for i in range(args.steps):
+        for j, o in enumerate(ops):
+            e = cev[i * len(ops) + j]
+            e[0].record(stream)
+            o()
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    ceil_gbs = moved / (float(np.mean([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e9
+    log(f"contiguous copy of the same bytes: {ceil_gbs:.1f} GB/s -> the block copy at "
+        f"{gbs / ceil_gbs:.1%} of it")
     rec = {"metric": f"block copy GB/s ({args.workload})", "value": round(moved * len(calls) /
            (step_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
@@ -421,7 +446,9 @@ def block_copy_bench(args, torch, np, pa):
                         "frac": round(gbs / peak, 4), "traffic": None,
                         "avg_launch_us": round(per_call * 1e3, 2),
                         "algorithmic_bytes_per_launch": moved},
-           "cpu_baseline": None}
+           "cpu_baseline": None,
+           "measured_ceiling": {"what": "contiguous copy of the same bytes (torch copy_)",
+                                "gbs": round(ceil_gbs, 2), "frac": round(gbs / ceil_gbs, 4)}}
     print(json.dumps(rec), flush=True)
 
 

@@ -3,7 +3,8 @@
 Not part of the paged attention library.  Each probe is a plain kernel that
 reads whole pool blocks (in a given order) or a buffer contiguously, or only
 issues bf16 MFMAs, so the benchmark can report what this GPU reaches for the
-same bytes or the same instruction (declarations: probes/pa_probes.h).
+same bytes or the same instruction, or repeats one LDS access pattern for the
+bank-conflict counter (declarations: probes/pa_probes.h).
 Argument marshalling only, as in the main binding.
 """
 from __future__ import annotations
@@ -30,7 +31,8 @@ def lib():
         P, I, L64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         for name, args in (("pa_ceiling_stream_read", (P, L64, P, I, P)),
                            ("pa_ceiling_gather_read", (P, P, L64, I, P, L64, P, I, P)),
-                           ("pa_ceiling_mfma_bf16", (P, I, I, P))):
+                           ("pa_ceiling_mfma_bf16", (P, I, I, P)),
+                           ("pa_probe_lds_pattern", (P, I, I, P, I, P))):
             f = getattr(_lib, name)
             f.restype = ctypes.c_int
             f.argtypes = list(args)
@@ -71,3 +73,18 @@ def pa_ceiling_mfma_bf16(sink: torch.Tensor, num_wgs: int, iters: int, stream=No
     _need(sink.dtype == torch.float32 and sink.numel() >= 4 * num_wgs, "sink: float32 [4 W]")
     _check("pa_ceiling_mfma_bf16", lib().pa_ceiling_mfma_bf16(_ptr(sink), num_wgs, iters,
                                                               _stream(stream)))
+
+
+LDS_KINDS = {"write_b128": 0, "read_b128": 1, "read_b64_tr_b16": 2, "read_b64": 3}
+
+
+def pa_probe_lds_pattern(offsets: torch.Tensor, kind: str, iters: int, sink: torch.Tensor,
+                         num_wgs: int, stream=None) -> None:
+    """One LDS access pattern per launch; offsets: int32/uint32 [64] byte offsets per lane,
+    sink: 4-byte [num_wgs]."""
+    _dev(offsets, sink)
+    _need(offsets.numel() == 64 and offsets.element_size() == 4, "offsets: 4-byte [64]")
+    _need(sink.numel() >= num_wgs and sink.element_size() == 4, "sink: 4-byte [num_wgs]")
+    _need(kind in LDS_KINDS, f"kind: one of {sorted(LDS_KINDS)}")
+    _check("pa_probe_lds_pattern", lib().pa_probe_lds_pattern(
+        _ptr(offsets), LDS_KINDS[kind], iters, _ptr(sink), num_wgs, _stream(stream)))

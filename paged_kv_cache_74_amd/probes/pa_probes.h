@@ -2,7 +2,8 @@
  * pa_probes.h -- measurement probes (libpa_probes.so), not part of the paged
  * attention library: plain kernels that read whole pool blocks or only issue
  * matrix-core instructions, so that a benchmark can report what this GPU
- * reaches for the same bytes or the same instruction mix.  Statuses and
+ * reaches for the same bytes or the same instruction mix, and one that repeats
+ * a single LDS access pattern for the bank-conflict counter.  Statuses and
  * stream convention as in include/pa.h.
  */
 #ifndef PA_PROBES_H_
@@ -43,6 +44,20 @@ pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool, int64_t
                                  int32_t block_bytes, const int32_t* blocks, int64_t n,
                                  uint32_t* sink, int32_t num_wgs, void* stream);
 pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters, void* stream);
+
+/*
+ * pa_probe_lds_pattern: LDS bank groups, one access pattern per launch, read
+ * with the SQ_LDS_BANK_CONFLICT counter.  num_wgs workgroups of one wave;
+ * each fills a 16 KiB LDS area (16-bit element k = (k * 40503) mod 2^16),
+ * then repeats iters times one access per lane at byte offsets[lane]
+ * (uint32 [64], device; clamped into the area and aligned down to the access
+ * size): kind 0 ds_write_b128, 1 ds_read_b128, 2 ds_read_b64_tr_b16,
+ * 3 ds_read_b64.  sink[w] (uint32 [num_wgs]) receives, for reads, the XOR of
+ * every 16-bit element the wave read when iters is odd (0 when even), and
+ * 0 for writes.
+ */
+pa_status pa_probe_lds_pattern(const uint32_t* offsets, int32_t kind, int32_t iters,
+                               uint32_t* sink, int32_t num_wgs, void* stream);
 
 #ifdef __cplusplus
 }

@@ -62,3 +62,31 @@ def test_mfma_loop_sums(dev):
     probes.pa_ceiling_mfma_bf16(sink, W, iters)
     torch.cuda.synchronize()
     assert (sink.cpu().numpy() == 64.0 * 16 * iters).all()
+
+
+def _lds_elements_xor(offsets, nbytes):
+    """XOR of the 16-bit elements a wave reads: each lane's nbytes at its offset, the LDS
+    area holding element k = (k * 40503) mod 2^16."""
+    x = 0
+    for o in offsets:
+        for k in range(o // 2, (o + nbytes) // 2):
+            x ^= (k * 40503) & 0xFFFF
+    return x
+
+
+def test_lds_pattern_probe_reads_what_each_lane_addresses(dev):
+    """Every read pattern of the bank-group probe (odd repeat count) returns the XOR of the
+    elements at the lanes' offsets; writes return 0.  The transposed read spreads the same
+    elements over other lanes, so its wave XOR is the same."""
+    from paged_kv_cache_74_amd import probes
+    from paged_kv_cache_74_amd.probes import lds_banks
+    size = {"read_b128": 16, "read_b64_tr_b16": 8, "read_b64": 8}
+    W = 4
+    sink = torch.zeros(W, dtype=torch.int32, device=dev)
+    for name, kind, offs in lds_banks.patterns() + [("b64 linear", "read_b64", [8 * l for l in range(64)])]:
+        probes.pa_probe_lds_pattern(torch.tensor(offs, dtype=torch.int32, device=dev), kind, 3,
+                                    sink, W)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        want = 0 if kind == "write_b128" else _lds_elements_xor(offs, size[kind])
+        assert (got == want).all(), (name, got, want)
