@@ -2,10 +2,12 @@
 """Benchmark of the paged-KV decode step on one MI355X.
 
 One step = the whole hot path over one batch: slot mapping of the step's new
-tokens and KV append (scatter into the paged pool), in one launch
+tokens and KV append (scatter into the paged pool), then paged decode attention
+(split kernel + log-sum-exp merge).  A decode step whose one new token per
+sequence is the last of its context appends inside the split kernel
+(pa_decode_append_partials); otherwise the append runs first, in one launch
 (pa_kv_append_paged) when the step's segments are short, else as two calls
-(--two-call-append forces the two calls), then paged decode attention (split
-kernel + log-sum-exp merge).  Default workload: Llama-3-8B-shaped GQA
+(--separate-append / --two-call-append force those forms).  Default workload: Llama-3-8B-shaped GQA
 decode -- batch 64, 32 query / 8 KV heads, head_dim 128, block 16, bf16,
 context lengths ~ U{2048..8192}, 19 sequences sharing an 800-token prefix
 through shared physical blocks, one appended token per sequence.
