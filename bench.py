@@ -476,7 +476,8 @@ def main():
                     help="decode workloads: append in its own launch (pa_kv_append_paged) before "
                          "pa_decode_partials, instead of pa_decode_append_partials")
     ap.add_argument("--one-launch", action="store_true",
-                    help="mixed workload: chunks and decode rows in one pa_prefill_chunk call")
+                    help="mixed workload: chunks and decode rows in one pa_prefill_chunk call "
+                         "(its query-length-1 rows take the decode kernel's path inside the call)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for scaling HBM counters)")
     args = ap.parse_args()
@@ -548,7 +549,7 @@ def main():
         log("--one-launch needs a workload with prefill chunks (mixed)")
         sys.exit(2)
     if P:
-        # one launch: the whole batch (chunks, then the decode rows as chunks of
+        # one call: the whole batch (chunks, then the decode rows as chunks of
         # one query); else the chunks only, the decode rows going to pa_decode
         PB = w.num_seqs if one else P
         pf_cu = i32(w.cu(w.q_lens[:PB]), dev)
@@ -657,7 +658,7 @@ def main():
         fl = prefill_flops(w, range(PB))
         pf_avg = float(prefill_ms.mean())
         tf = fl / (pf_avg * 1e-3) / 1e12
-        what = ("pa_prefill_chunk: chunks and decode rows, one launch" if one
+        what = ("pa_prefill_chunk: chunks and decode rows in one call" if one
                 else "pa_prefill_chunk")
         prefill_rec = {"kernel": f"prefill_kernel ({what})", "bound": "mfma",
                        "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -671,15 +672,15 @@ def main():
         log(f"prefill avg {pf_avg * 1e3:.1f} us -> {tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
             f"of the bf16 MFMA peak ({fl / 1e9:.1f} GFLOP)")
         if one:
-            # lower bound of the one launch: the chunks' flops at the MFMA peak
+            # lower bound of the one call: the chunks' flops at the MFMA peak
             # plus the decode rows' bytes at the HBM peak
             t_min = (prefill_flops(w) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
                      + bm["split_kernel"] / (HBM_PEAK_GBS * 1e9))
             prefill_rec["serial_bound_us"] = round(t_min * 1e6, 2)
             prefill_rec["frac_of_serial_bound"] = round(t_min / (pf_avg * 1e-3), 4)
-            log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s), one launch; bound "
+            log(f"step {ms_step * 1e3:.1f} us ({step_gbs:.0f} GB/s), one call; bound "
                 f"{t_min * 1e6:.1f} us (chunk flops at the MFMA peak + decode bytes at the HBM peak) "
-                f"= {t_min / (pf_avg * 1e-3):.1%} of the launch")
+                f"= {t_min / (pf_avg * 1e-3):.1%} of the call")
 
     ceil = None
     if not args.no_ceilings:

@@ -216,7 +216,8 @@ pa_status pa_decode(void* out, const void* q, int q_dtype,
 
 /*
  * pa_prefill_workspace_bytes -- scratch needed by pa_prefill_chunk (0 for an
- * empty batch or unsupported head counts), for either dtype pair.  It grows
+ * empty batch or unsupported head counts), for either dtype pair and any block
+ * size (it includes the split partials of the rows of length 1).  It grows
  * with num_seqs and total_q, not with num_seqs times max_q_len: a batch of
  * many decode rows beside a few long chunks needs little.  The call must pass the same
  * num_seqs, total_q and max_q_len.
@@ -239,12 +240,15 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *   and attends to keys j <= T_s - L_s + i when causal != 0, to all j < T_s
  *   otherwise:
  *     out[row][h][:] = sum_j softmax_j(scale * q[row][h] . K_s[j][h/g]) V_s[j][h/g][:].
- *   A decode row is the special case L_s = 1, so one call (one attention
- *   launch, plus a small planning launch and a merge launch) serves a mixed
+ *   A decode row is the special case L_s = 1, so one call serves a mixed
  *   step: prefill chunks and decode rows side by side, in any order -- the
  *   engine's view in "From PagedAttention to Chunked Prefill", section 3.2.
- *   Work is spread over the device in equal shares of 32-key tiles; a short
- *   chunk occupies only the matrix-core rows it needs.
+ *   Inside the call a planning launch lists the chunks' work, the tile launch
+ *   spreads it over the device in equal shares of 32-key tiles, and a merge
+ *   launch combines split tiles.  With blocks of 16 tokens or more the rows
+ *   of length 1 are left out of the tiles and run on pa_decode's split and
+ *   merge launches instead (whole token rows streamed through the matrix
+ *   cores; the planner lists them on the device, so the host reads nothing).
  *
  *   (q, cache) dtype pairs: (BF16, BF16), (BF16, FP8_E4M3), (BF16, INT8) on
  *   the matrix cores, and (F32, F32), where each query row runs as a decode

@@ -109,6 +109,10 @@ struct DecodeArgs {
   // table row s).  The fp32 chunked prefill runs each query row as a decode
   // row of its own sequence.
   const int32_t* table_row;
+  // matrix-core kernel and merge: the q and out row of sequence s (a query row
+  // of a ragged batch; -1: the sequence has no row here), NULL: row s.  The
+  // chunked prefill runs its query-length-1 rows through this path.
+  const int32_t* row_map;
   // The appending decode: token context_lens[s] - 1 of every sequence is
   // k_new[s] / v_new[s] ([num_seqs][n_kv][HD] of the source dtype), written to
   // its slot (as pa_kv_append writes it) by the workgroup that reads it
@@ -1013,7 +1017,8 @@ __device__ __forceinline__ void decode_run_mf(const DecodeArgs& a, int s, int kv
   mf_bf16x8_t qb[ML::NT];
   {
     const int h = r < G ? r : 0;
-    const uint8_t* qp = a.q + ((int64_t)s * n_q + (int64_t)kvh * G + h) * HD * 2;
+    const int64_t qr = a.row_map ? uniform_load(a.row_map, s) : s;
+    const uint8_t* qp = a.q + (qr * n_q + (int64_t)kvh * G + h) * HD * 2;
 #pragma unroll
     for (int t = 0; t < ML::NT; ++t) {
       const int d0 = mf_dim0<ML>(t, j);
@@ -1399,7 +1404,7 @@ template <int HD, int G, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ header, int num_seqs,
-    int n_kv, float v_scale) {
+    int n_kv, float v_scale, const int32_t* __restrict__ row_map) {
   constexpr int DPT = HD / 64;   // dims per thread
   const int n_q = n_kv * G;
   const int hw = header[1];
@@ -1410,7 +1415,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int hg = kvh / hw, wv = kvh % hw;
   const int t = threadIdx.x;
   const int steps = steps_of(context_lens[s]);
-  const int64_t row = (int64_t)s * n_q + h;
+  const int64_t orow = row_map ? row_map[s] : s;   // wave-uniform: the block is one wave
+  if (orow < 0) return;
+  const int64_t row = orow * n_q + h;
   float acc[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
@@ -1683,6 +1690,7 @@ static pa_status launch_split(DecodeArgs a, int split_tokens, int max_context_le
   constexpr bool MF = (DECODE_MFMA_MASK >> CDT) & 1;
   const int hw = heads_per_wg(CDT, a.n_kv, G);
   const bool mf = MF && a.block_size >= 16;
+  if (a.row_map && !mf) return PA_ERR_UNSUPPORTED;   // the vector kernel reads row s
   const int64_t bound = wgs_bound(hw, a.num_seqs, a.n_kv, max_context_len, split_tokens);
   a.hw = hw;
   a.nhg = a.n_kv / hw;
@@ -1733,21 +1741,23 @@ static pa_status dispatch_hd(int hd, int G, const DecodeArgs& a, int split_token
 // The merge reads the wave count the split kernel used from the workspace.
 template <int HD, int G, bool BF16>
 static pa_status launch_merge_t(void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
-                                int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+                                int num_seqs, int n_kv, float out_scale, const int32_t* row_map,
+                                hipStream_t st) {
   const char* base = (const char*)ws;
   return launch(decode_merge_kernel<HD, G, BF16>, dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
                 dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
-                ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale);
+                ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale, row_map);
 }
 
 template <int HD, bool BF16>
 static pa_status merge_g(int G, void* out, const WsLayout& l, const void* ws, const int32_t* ctx,
-                         int num_seqs, int n_kv, float out_scale, hipStream_t st) {
+                         int num_seqs, int n_kv, float out_scale, const int32_t* row_map,
+                         hipStream_t st) {
   switch (G) {
-    case 1: return launch_merge_t<HD, 1, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
-    case 2: return launch_merge_t<HD, 2, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
-    case 4: return launch_merge_t<HD, 4, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
-    case 8: return launch_merge_t<HD, 8, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, st);
+    case 1: return launch_merge_t<HD, 1, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, row_map, st);
+    case 2: return launch_merge_t<HD, 2, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, row_map, st);
+    case 4: return launch_merge_t<HD, 4, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, row_map, st);
+    case 8: return launch_merge_t<HD, 8, BF16>(out, l, ws, ctx, num_seqs, n_kv, out_scale, row_map, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -1782,12 +1792,13 @@ static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int 
 
 static pa_status launch_merge(void* out, int out_dtype, const int32_t* context_lens, int num_seqs,
                               int n_kv, int G, int head_dim, const WsLayout& l, float out_scale,
-                              const void* workspace, hipStream_t st) {
+                              const void* workspace, hipStream_t st,
+                              const int32_t* row_map = nullptr) {
   if (out_dtype == PA_BF16)
-    return head_dim == 128 ? merge_g<128, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
-                           : merge_g<64, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
-  return head_dim == 128 ? merge_g<128, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st)
-                         : merge_g<64, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, st);
+    return head_dim == 128 ? merge_g<128, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, row_map, st)
+                           : merge_g<64, true>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, row_map, st);
+  return head_dim == 128 ? merge_g<128, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, row_map, st)
+                         : merge_g<64, false>(G, out, l, workspace, context_lens, num_seqs, n_kv, out_scale, row_map, st);
 }
 
 // Both phases of decode; merge == false runs the partials phase only.
@@ -1803,7 +1814,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
                              const float* v_token_scales = nullptr,
                              const int32_t* table_row = nullptr,
                              const void* k_new = nullptr, const void* v_new = nullptr,
-                             int src_dtype = -1, int64_t* slots_out = nullptr) {
+                             int src_dtype = -1, int64_t* slots_out = nullptr,
+                             const int32_t* row_map = nullptr) {
   pa_status e = check_common(num_seqs, n_kv_heads, group_size, head_dim, max_context_len, split_tokens);
   if (e != PA_OK) return e;
   if (num_blocks < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
@@ -1862,6 +1874,7 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.k_ch_scale = k_channel_scales;
   a.v_tok_scale = v_token_scales;
   a.table_row = table_row;
+  a.row_map = row_map;
   a.k_new = append ? (const uint8_t*)k_new : nullptr;
   a.v_new = append ? (const uint8_t*)v_new : nullptr;
   a.src_f32 = src_dtype == PA_F32;
@@ -1877,7 +1890,7 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   else e = dispatch_hd<PA_F32>(head_dim, G, a, split_tokens, max_context_len, st);
   if (e != PA_OK || !merge) return e;
   return launch_merge(out, q_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
-                      fp8 ? v_scale : 1.0f, workspace, st);
+                      fp8 ? v_scale : 1.0f, workspace, st, row_map);
 }
 
 extern "C" pa_status pa_decode(void* out, const void* q, int q_dtype, const void* k_cache,
@@ -2088,6 +2101,26 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   }
   row_ctx[r] = n;     // rows outside every chunk: no keys, zero output
   row_seq[r] = lo;
+}
+
+size_t prefill_decode_rows_workspace_bytes(int num_seqs, int n_kv, int G, int head_dim) {
+  if (num_seqs <= 0) return 0;
+  return ws_layout(entries_bound(num_seqs, n_kv, G, 0, 0), G, head_dim).total;
+}
+
+pa_status prefill_decode_rows(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              int cache_dtype, int num_blocks, int block_size, int n_kv,
+                              int head_dim, int G, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* row_ctx,
+                              const int32_t* row_map, int num_seqs, int max_context_len,
+                              float scale, float k_scale, float v_scale,
+                              const float* k_channel_scales, const float* v_token_scales,
+                              void* workspace, size_t workspace_bytes, hipStream_t st) {
+  return decode_impl(out, true, q, PA_BF16, k_cache, v_cache, cache_dtype, num_blocks, block_size,
+                     n_kv, head_dim, G, block_tables, max_blocks_per_seq, row_ctx, num_seqs,
+                     max_context_len, scale, k_scale, v_scale, 0, workspace, workspace_bytes, st,
+                     k_channel_scales, v_token_scales, nullptr, nullptr, nullptr, -1, nullptr,
+                     row_map);
 }
 
 size_t prefill_f32_workspace_bytes(int total_q, int n_kv, int G, int head_dim,

@@ -17,4 +17,19 @@ pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens
                            const int32_t* context_lens, int max_context_len, int causal,
                            float scale, void* workspace, size_t workspace_bytes, hipStream_t st);
 
+// decode.hip: the query-length-1 rows of a chunked-prefill batch on the
+// matrix-core decode path.  row_ctx[s] is sequence s's context when its chunk
+// is one query long and 0 otherwise; row_map[s] is that query's row of q and
+// out, or -1 (the merge writes no output for the sequence).  Needs
+// block_size >= 16 and a bf16 query; the workspace holds the split partials.
+size_t prefill_decode_rows_workspace_bytes(int num_seqs, int n_kv, int G, int head_dim);
+pa_status prefill_decode_rows(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              int cache_dtype, int num_blocks, int block_size, int n_kv,
+                              int head_dim, int G, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* row_ctx,
+                              const int32_t* row_map, int num_seqs, int max_context_len,
+                              float scale, float k_scale, float v_scale,
+                              const float* k_channel_scales, const float* v_token_scales,
+                              void* workspace, size_t workspace_bytes, hipStream_t st);
+
 }  // namespace pa

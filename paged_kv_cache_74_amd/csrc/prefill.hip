@@ -40,6 +40,10 @@
 //     workgroups are combined by a log-sum-exp merge kernel.
 //   * The next tile's K/V is in registers while a tile is computed; LDS is
 //     double-buffered, one barrier per tile; three workgroups share a CU.
+//   * Rows of length 1 (decode rows in the batch) would use one wave in four
+//     and 4 of the 32 query columns of a tile.  With blocks of 16 tokens or
+//     more the planner leaves them out of the tiles and lists them for the
+//     decode kernel's path (decode.hip), which the call runs after the tiles.
 #include "internal.h"
 
 #include <type_traits>
@@ -185,14 +189,18 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
                                                             int32_t* __restrict__ seq_seg0_g,
                                                             int32_t* __restrict__ seg_cu,
                                                             int4* __restrict__ seg_desc,
-                                                            int32_t* __restrict__ wg_start) {
+                                                            int32_t* __restrict__ wg_start,
+                                                            int32_t* __restrict__ drow_ctx,
+                                                            int32_t* __restrict__ drow_map) {
   __shared__ int64_t wsum[32];
   __shared__ int32_t seq_seg0_l[PF_PREP_LDS_SEQS + 1];
   const int t = threadIdx.x;
   const bool in_lds = num_seqs <= PF_PREP_LDS_SEQS;
   int32_t* seq_seg0 = in_lds ? seq_seg0_l : seq_seg0_g;
+  // with drow_ctx given, rows of length 1 go to the decode path: no segments here
   auto qtiles = [&](int s) {
     const int L = max(0, a.cu_q[s + 1] - a.cu_q[s]);
+    if (drow_ctx && L == 1) return 0;
     return (int)(((int64_t)L + QB - 1) / QB);
   };
   // 1. segments per sequence
@@ -206,6 +214,14 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
     cs += (int64_t)a.n_kv * qtiles(s);
   }
   bad = __syncthreads_or(bad);
+  if (drow_ctx) {   // the decode path's rows (none for a batch that breaks its bounds)
+    for (int s = s0; s < s1; ++s) {
+      const int c0 = a.cu_q[s];
+      const bool one = !bad && a.cu_q[s + 1] - c0 == 1;
+      drow_ctx[s] = one ? a.context_lens[s] : 0;
+      drow_map[s] = one ? c0 : -1;
+    }
+  }
   int64_t nseg_all;
   const int64_t cs_end = block_scan_1024(cs, wsum, &nseg_all);
   if (bad) nseg_all = a.nseg_max + (int64_t)1;
@@ -752,10 +768,14 @@ static int pf_cu_count() {
 
 constexpr int PF_MAX_WGS_PER_CU = 4;   // bounds the workspace (LDS allows at most 4)
 
+// The workspace: the plan and partials of the tile kernel, then the rows of
+// length 1 for the decode path (their contexts and q/out rows, and the decode
+// split's partials).
 struct PfLayout {
-  size_t hdr, seq, seg, desc, wgs, ml, o, total;
+  size_t hdr, seq, seg, desc, wgs, ml, o, drow_ctx, drow_map, dws, dws_bytes, total;
 };
-static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_dim) {
+static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_dim, int n_kv,
+                          int G) {
   PfLayout l;
   const size_t slots = (size_t)(wgs + nseg);
   l.hdr = 0;
@@ -765,7 +785,11 @@ static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_
   l.wgs = l.desc + pf_align((size_t)nseg * 16);
   l.ml = l.wgs + pf_align((size_t)wgs * 2 * 4);
   l.o = l.ml + pf_align(slots * PF_ROWS * 2 * 4);
-  l.total = l.o + pf_align(slots * PF_ROWS * head_dim * 4);
+  l.drow_ctx = l.o + pf_align(slots * PF_ROWS * head_dim * 4);
+  l.drow_map = l.drow_ctx + pf_align((size_t)num_seqs * 4);
+  l.dws = l.drow_map + pf_align((size_t)num_seqs * 4);
+  l.dws_bytes = prefill_decode_rows_workspace_bytes((int)num_seqs, n_kv, G, head_dim);
+  l.total = l.dws + pf_align(l.dws_bytes);
   return l;
 }
 
@@ -786,7 +810,7 @@ static int pf_resident_wgs() {
 
 template <int CDT, int HD, int G>
 static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len,
-                           const PfLayout& l, char* ws, hipStream_t st) {
+                           const PfLayout& l, char* ws, bool route, hipStream_t st) {
   const int W = pf_resident_wgs<CDT, HD, G>();
   a.hdr = (const int32_t*)(ws + l.hdr);
   a.seg_cu = (const int32_t*)(ws + l.seg);
@@ -796,7 +820,9 @@ static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_l
   a.part_o = (float*)(ws + l.o);
   pa_status e = launch(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, num_seqs, total_q,
                        max_q_len, PF_ROWS / G, W, (int32_t*)(ws + l.hdr), (int32_t*)(ws + l.seq),
-                       (int32_t*)(ws + l.seg), (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs));
+                       (int32_t*)(ws + l.seg), (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs),
+                       route ? (int32_t*)(ws + l.drow_ctx) : nullptr,
+                       route ? (int32_t*)(ws + l.drow_map) : nullptr);
   if (e == PA_OK) e = launch(prefill_kernel<CDT, HD, G>, dim3(W), dim3(256), 0, st, a);
   if (e == PA_OK)
     e = launch(prefill_merge_kernel<HD, G>, dim3(a.nseg_max * (PF_ROWS / MergeShape<HD>::ROWS)),
@@ -806,12 +832,13 @@ static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_l
 
 template <int CDT, int HD>
 static pa_status pf_dispatch_g(int G, const PrefillArgs& a, int num_seqs, int total_q,
-                               int max_q_len, const PfLayout& l, char* ws, hipStream_t st) {
+                               int max_q_len, const PfLayout& l, char* ws, bool route,
+                               hipStream_t st) {
   switch (G) {
-    case 1: return pf_launch<CDT, HD, 1>(a, num_seqs, total_q, max_q_len, l, ws, st);
-    case 2: return pf_launch<CDT, HD, 2>(a, num_seqs, total_q, max_q_len, l, ws, st);
-    case 4: return pf_launch<CDT, HD, 4>(a, num_seqs, total_q, max_q_len, l, ws, st);
-    case 8: return pf_launch<CDT, HD, 8>(a, num_seqs, total_q, max_q_len, l, ws, st);
+    case 1: return pf_launch<CDT, HD, 1>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
+    case 2: return pf_launch<CDT, HD, 2>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
+    case 4: return pf_launch<CDT, HD, 4>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
+    case 8: return pf_launch<CDT, HD, 8>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -842,7 +869,8 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, 
   // the larger of the two plans: matrix-core tiles (bf16 queries) or one
   // decode row per query (fp32 queries and cache)
   const size_t mf = pf_layout(num_seqs, pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, G),
-                              (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim).total;
+                              (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim, n_kv_heads,
+                              G).total;
   const size_t rows = prefill_f32_workspace_bytes(total_q, n_kv_heads, G, head_dim, max_context_len);
   return mf > rows ? mf : rows;
 }
@@ -893,8 +921,8 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   if (nseg * (PF_ROWS / 4) >= ((int64_t)1 << 31) ||
       nseg * ((int64_t)max_context_len / PF_BN + 1) >= ((int64_t)1 << 31))
     return PA_ERR_SHAPE;
-  const PfLayout l =
-      pf_layout(num_seqs, nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim);
+  const PfLayout l = pf_layout(num_seqs, nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim,
+                               n_kv_heads, group_size);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   // a block's rows are addressed with 32-bit offsets
   if ((int64_t)block_size * n_kv_heads * head_dim * 2 >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
@@ -922,7 +950,8 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   a.out_scale = fp8 ? v_scale : 1.0f;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  pa_status (*dispatch)(int, const PrefillArgs&, int, int, int, const PfLayout&, char*, hipStream_t);
+  pa_status (*dispatch)(int, const PrefillArgs&, int, int, int, const PfLayout&, char*, bool,
+                        hipStream_t);
   if (cache_dtype == PA_BF16)
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_BF16, 128> : pf_dispatch_g<PA_BF16, 64>;
   else if (cache_dtype == PA_FP8_E4M3)
@@ -931,7 +960,19 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT8, 128> : pf_dispatch_g<PA_INT8, 64>;
   else
     dispatch = head_dim == 128 ? pf_dispatch_g<PA_INT4, 128> : pf_dispatch_g<PA_INT4, 64>;
-  return dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, st);
+  // Rows of length 1 (decode rows in the batch) take the decode kernel's path
+  // when the blocks allow it (16 tokens or more): whole token rows streamed
+  // through the matrix cores, where the tile kernel would give such a row one
+  // wave in four and 4 of its 32 query columns.  The planner lists them; the
+  // tile kernel skips them.
+  const bool route = block_size >= 16;
+  pa_status e = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, route, st);
+  if (e != PA_OK || !route) return e;
+  return prefill_decode_rows(out, q, k_cache, v_cache, cache_dtype, num_blocks, block_size,
+                             n_kv_heads, head_dim, group_size, block_tables, max_blocks_per_seq,
+                             (const int32_t*)(ws + l.drow_ctx), (const int32_t*)(ws + l.drow_map),
+                             num_seqs, max_context_len, scale, k_scale, v_scale,
+                             k_channel_scales, v_scales, ws + l.dws, l.dws_bytes, st);
 }
 
 extern "C" pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,

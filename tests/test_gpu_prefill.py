@@ -92,7 +92,7 @@ def test_prefill_peaked_scores(dev):
 
 
 def test_prefill_length_one_matches_decode(dev):
-    """Decode rows run through the chunk kernel (L = 1) agree with pa_decode."""
+    """Rows of length 1 through pa_prefill_chunk agree with pa_decode."""
     import paged_kv_cache_74_amd as pa
     from gpu_harness import DeviceWorkload, i32, to_f64
     w = workloads.draw_values(workloads.small(3), "cpu")
@@ -104,6 +104,8 @@ def test_prefill_length_one_matches_decode(dev):
     pf = to_f64(pa.pa_prefill_chunk(dw.q, dw.k_cache, dw.v_cache, i32(np.arange(B + 1), dev),
                                     dw.tables, dw.ctx, 1, int(w.context_lens.max()), w.scale))
     assert np.abs(pf - dec).max() <= 1e-2
+    if w.block_size >= 16:   # the call runs rows of length 1 on pa_decode's own path
+        assert np.array_equal(pf, dec)
     pk, pv = oracle_pools(w)
     from helpers import oracle_decode
     check_close(pf, oracle_decode(w, pk, pv), "bf16", "prefill L=1")
