@@ -201,10 +201,11 @@ def draw_values(w: Workload, device: str = "cpu") -> Workload:
         # per-tensor scales: amax / 448 (largest finite e4m3 magnitude) or amax / 127, fp32
         import torch
         top = np.float32(448.0 if w.cache_dtype == "fp8" else 127.0)
-        ka = torch.maximum(w.res_k.float().abs().amax(), w.new_k.float().abs().amax()) if w.new_k.numel() else w.res_k.float().abs().amax()
-        va = torch.maximum(w.res_v.float().abs().amax(), w.new_v.float().abs().amax()) if w.new_v.numel() else w.res_v.float().abs().amax()
-        w.k_scale = float(np.float32(float(ka)) / top)
-        w.v_scale = float(np.float32(float(va)) / top)
+        def amax(*ts):   # over the rows there are (a batch of empty contexts has none: scale 1)
+            m = [t.float().abs().amax() for t in ts if t.numel()]
+            return float(torch.stack(m).max()) if m else float(top)
+        w.k_scale = float(np.float32(amax(w.res_k, w.new_k)) / top)
+        w.v_scale = float(np.float32(amax(w.res_v, w.new_v)) / top)
     if w.cache_dtype == "int4":
         # per-channel key scales (the caller's calibration): amax over every key
         # of the workload per (KV head, channel) / 7, fp32
