@@ -1,7 +1,9 @@
-"""GPU edge cases of decode through the C-ABI, against the oracle: sequences with
+"""GPU edge cases through the C-ABI, against the oracle.  Decode: sequences with
 an empty context beside full ones (their output rows must be exactly zero), a
 batch whose contexts are all empty, the largest block size (256 tokens), and the
-appending decode over empty contexts (no slot, slot -1).
+appending decode over empty contexts (no slot, slot -1).  Prefill: chunks of 0
+and 1 queries beside longer ones, causal or not, with and without the decode path
+for the rows of length 1.
 
 Bars as elsewhere: bf16 / 8-bit outputs within 2e-2 absolute and 1e-2 normwise
 relative error per row; a zero reference row must come back exactly zero (the
@@ -110,3 +112,26 @@ def test_decode_append_over_empty_contexts(dev):
     assert np.array_equal(got, ref_out)
     assert torch.equal(two.k_cache.view(torch.int16), dw.k_cache.view(torch.int16))
     assert torch.equal(two.v_cache.view(torch.int16), dw.v_cache.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("bs", [16, 4])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_empty_and_single_query_chunks(dev, kv, bs, causal):
+    """Chunks of 0 queries (a sequence with no rows in the batch), 1 query (run on the
+    decode path when blocks hold 16 tokens or more) and a few queries, over prior
+    contexts of 0 to 400 tokens, in one pa_prefill_chunk call."""
+    from gpu_harness import DeviceWorkload, prefill, to_f64
+    from helpers import oracle_prefill
+    print(f"edge prefill {kv} bs{bs} causal={causal}", flush=True)
+    w = workloads.mixed_prefill_decode(prior=(10, 0, 50, 400, 64), chunk_lens=(0, 7, 0, 1, 33),
+                                       n_decode=3, dlo=1, dhi=90, seed=5, n_q=16, n_kv=4, hd=128,
+                                       bs=bs, kv=kv)
+    workloads.draw_values(w, "cpu")
+    w.causal = causal
+    dw = DeviceWorkload(w, dev)
+    dw.append_resident()
+    dw.append_new()
+    got = to_f64(prefill(dw))
+    pk, pv = oracle_pools(w)
+    check_close(got, oracle_prefill(w, pk, pv), "bf16", f"prefill edge {kv} bs{bs} causal={causal}")
