@@ -159,13 +159,15 @@ def test_prefill_split_covers_every_tile_once(seed):
 PF_ROWS, PF_BN = 128, 32
 
 
-def prefill_plan(lens, ctx, n_kv, G, causal):
+def prefill_plan(lens, ctx, n_kv, G, causal, route=False):
     """The prefill planner's segment list: for each sequence, each KV head, each
-    query tile of QB = 128 / G queries; per segment the key tiles its last query needs."""
+    query tile of QB = 128 / G queries; per segment the key tiles its last query needs.
+    With route (blocks of 16 tokens or more) a sequence of one query has no segment:
+    it goes to the decode path instead (prefill_decode_rows)."""
     QB = PF_ROWS // G
     segs = []
     for s, (L, T) in enumerate(zip(lens, ctx)):
-        nq = -(-L // QB)
+        nq = 0 if route and L == 1 else -(-L // QB)
         for kvh in range(n_kv):
             for qt in range(nq):
                 last = min(L, (qt + 1) * QB) - 1
@@ -214,6 +216,66 @@ def test_prefill_plan_covers_every_row_once(seed):
         if sum(tiles):
             for W in (1, 3, 64, 1000):
                 replay_prefill(tiles, W)
+
+
+def decode_row_lists(lens, ctx):
+    """The planner's lists for the decode path: per sequence, the context when its
+    chunk is one query long (else 0) and that query's row of q and out (else -1)."""
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    row_ctx = [T if L == 1 else 0 for L, T in zip(lens, ctx)]
+    row_map = [cu[s] if L == 1 else -1 for s, L in enumerate(lens)]
+    return row_ctx, row_map
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_plan_with_decode_rows_covers_every_row_once(seed):
+    """With the rows of length 1 on the decode path, every (sequence, query, head)
+    row is computed exactly once: by a segment of the tile kernel or, for a
+    one-query chunk, by the decode split over row_ctx / row_map (whose units are
+    the sequence's whole context, the key range a one-query chunk sees, causal or
+    not).  The decode merge writes exactly the mapped rows."""
+    rng = random.Random(400 + seed)
+    for _ in range(200):
+        B = rng.randint(1, 12)
+        n_kv = rng.choice([1, 2, 8])
+        G = rng.choice([1, 2, 4, 8])
+        QB = PF_ROWS // G
+        causal = rng.random() < 0.7
+        lens = [rng.choice([0, 1, 1, 1, 2, QB, QB + 1, rng.randint(1, 400)]) for _ in range(B)]
+        ctx = [L + rng.choice([0, 0, 1, 31, 32, rng.randint(0, 500)]) for L in lens]
+        segs = prefill_plan(lens, ctx, n_kv, G, causal, route=True)
+        assert len(segs) <= nseg_bound(B, sum(lens), max(lens), n_kv, G)
+        row_ctx, row_map = decode_row_lists(lens, ctx)
+        cu = [0]
+        for L in lens:
+            cu.append(cu[-1] + L)
+        seen = {}
+        for g, (s, kvh, qt, tiles) in enumerate(segs):
+            assert lens[s] != 1
+            for rr in range(PF_ROWS):
+                qi, h = qt * QB + rr // G, rr % G
+                if qi < lens[s]:
+                    key = (cu[s] + qi, kvh * G + h)
+                    assert key not in seen
+                    seen[key] = ("tile", g)
+        for s in range(B):
+            if row_map[s] < 0:
+                assert row_ctx[s] == 0
+                continue
+            assert lens[s] == 1 and row_map[s] == cu[s] and row_ctx[s] == ctx[s]
+            # one query at position T - 1 sees keys [0, T): causal or not, the decode range
+            last_key = ctx[s] - 1
+            assert (ctx[s] - lens[s] + 0 if causal else ctx[s] - 1) == last_key
+            for h in range(n_kv * G):
+                key = (row_map[s], h)
+                assert key not in seen
+                seen[key] = ("decode", s)
+        assert len(seen) == sum(lens) * n_kv * G
+        # the mapped output rows are distinct rows of out
+        mapped = [r for r in row_map if r >= 0]
+        assert len(set(mapped)) == len(mapped) and all(0 <= r < sum(lens) for r in mapped)
 
 
 def test_prefill_planner_workgroup_starts():
