@@ -268,6 +268,9 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
  *                 rows are addressed with 32-bit offsets), else PA_ERR_SHAPE
  *   group_size    1, 2, 4 or 8
  *   scale         positive and finite, else PA_ERR_SHAPE
+ *   max_context_len  upper bound of the T_s; with block_size >= 16,
+ *                 num_seqs * n_kv_heads * ceil(max_context_len / 16) below 2^31
+ *                 (the decode path's units), else PA_ERR_SHAPE
  *   workspace     at least pa_prefill_workspace_bytes(...) bytes (may be NULL if 0)
  */
 pa_status pa_prefill_chunk(void* out, const void* q, int q_dtype,

@@ -966,6 +966,11 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   // wave in four and 4 of its 32 query columns.  The planner lists them; the
   // tile kernel skips them.
   const bool route = block_size >= 16;
+  // the decode path counts its 16-token units in 32-bit integers; checked here,
+  // before anything is enqueued
+  if (route && (int64_t)num_seqs * n_kv_heads * (((int64_t)max_context_len + 15) / 16) >=
+                   ((int64_t)1 << 31))
+    return PA_ERR_SHAPE;
   pa_status e = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, route, st);
   if (e != PA_OK || !route) return e;
   return prefill_decode_rows(out, q, k_cache, v_cache, cache_dtype, num_blocks, block_size,
