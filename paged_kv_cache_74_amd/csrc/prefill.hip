@@ -35,9 +35,13 @@
 //     slice, taken on the raw scores), O get rescaled and the slice's weights get taken
 //     again.  The result does not depend on which max is used.
 //   * Work is balanced like the decode kernel: a unit is one 32-key tile of one
-//     segment (sequence, KV head, 128-row query tile); each resident workgroup
-//     takes an equal contiguous range of units, and segments split between
-//     workgroups are combined by a log-sum-exp merge kernel.
+//     segment (sequence, KV head, 128-row query tile), and each resident
+//     workgroup takes a contiguous range of units; segments split between
+//     workgroups are combined by a log-sum-exp merge kernel.  Every segment
+//     also counts a few start-up units (its query load, pipeline fill and
+//     output store), and the ranges are weighted by the round in which a
+//     workgroup was dispatched to its CU (see pf_wt), so that workgroups
+//     finish together rather than merely holding equal tile counts.
 //   * The next tile's K/V is in registers while a tile is computed; LDS is
 //     double-buffered, one barrier per tile; three workgroups share a CU.
 //   * Rows of length 1 (decode rows in the batch) would use one wave in four
@@ -61,6 +65,15 @@ constexpr int PF_WAVES = 4;
 constexpr int PF_ROWS = 32 * PF_WAVES;   // query rows per workgroup
 constexpr int PF_BN = 32;                // keys per tile
 constexpr int PF_LOG2_TSUM = 12;
+// Start-up units per segment: a piece of a segment also loads the segment's
+// queries, waits for its first tile and stores its rows, which measured as
+// about three tiles' time (a workgroup given 28 short causal segments took
+// 515 us against 385 us for one given 1-2 long ones, at equal tile counts).
+// They are units of the split that hold no tile.
+#ifndef PF_SEG_OV
+#define PF_SEG_OV 3
+#endif
+constexpr int PF_OV = PF_SEG_OV;
 constexpr float PF_TSUM_MAX = (float)(1 << PF_LOG2_TSUM);
 
 struct PrefillArgs {
@@ -74,7 +87,9 @@ struct PrefillArgs {
   const int32_t* hdr;        // {segments, key tiles in all}, written by the prep kernel
   const int32_t* seg_cu;     // [segments + 1] prefix sums of key tiles per segment
   const int4* seg_desc;      // [segments] {sequence, KV head, query tile, key tiles}
-  const int32_t* wg_start;   // [num_wgs][2] first (segment, tile) of each workgroup
+  const int32_t* wg_start;   // [num_wgs][2] first (segment, unit) of each workgroup
+  const int32_t* wg_begin;   // [num_wgs + 1] workgroup w takes units [wg_begin[w], wg_begin[w + 1])
+  const int32_t* seg_w0;     // [segments] the workgroup holding a segment's first unit
   float* part_o;             // [slots][PF_ROWS][HD]   slot = workgroup + segment
   float* part_ml;            // [slots][PF_ROWS][2]
   int64_t tok_stride;        // bytes between consecutive tokens of a block
@@ -84,6 +99,7 @@ struct PrefillArgs {
   int n_kv;
   int max_blocks;
   int nseg_max;              // bound on the segments of the batch (workspace size)
+  int cus;                   // compute units of the device (weights of the work split)
   int causal;
   float score_scale;         // scale * k_scale * log2(e)
   float out_scale;           // v_scale for 8-bit caches, else 1
@@ -126,9 +142,40 @@ __device__ __forceinline__ int seg_tiles(int L, int T, int qt, int QB, int causa
   return visible > 0 ? (visible + PF_BN - 1) / PF_BN : 0;
 }
 
-__device__ __forceinline__ int64_t pf_begin(int w, int64_t U, int W) { return (int64_t)w * U / W; }
-__device__ __forceinline__ int pf_owner(int64_t x, int64_t U, int W) {
-  return (int)(((x + 1) * W - 1) / U);
+// Weights of the work split.  With R resident workgroups per CU the grid is
+// dispatched in R rounds (blocks [r C, (r + 1) C) in round r), and the waves of
+// the R workgroups sharing a SIMD are issued oldest first: measured with equal
+// tile counts on the mixed step (three per CU), workgroups of rounds 0, 1 and 2
+// took 385, 403 and 435 us on average.  A workgroup of round r therefore takes
+// a share of the units proportional to pf_wt(r) (with these weights the three
+// rounds finished at 404, 405 and 412 us).  In the XCD-local work order
+// (xcd_local_order) workgroup w = x M + k, M = W / 8, was block 8 k + x, of
+// round k / (C / 8).  The weights only move split points; any other dispatch
+// order gives the same results, only less evenly timed.
+#ifndef PF_WT
+#define PF_WT 64, 60, 53, 50
+#endif
+__device__ __forceinline__ int pf_wt(int r) {
+  constexpr int t[4] = {PF_WT};
+  return t[r < 4 ? r : 3];
+}
+// sum of the split weights of workgroups [0, w) in the work order (equal
+// weights when the grid is not R whole rounds of 8-XCD-divisible CUs)
+__device__ __forceinline__ int64_t pf_wsum(int w, int W, int C) {
+  const bool rounds = PREFILL_XCD_LOCAL && C > 0 && C % PF_XCDS == 0 && W % C == 0 && W / C <= 4 &&
+                      W % PF_XCDS == 0;
+  if (!rounds) return (int64_t)w * 64;
+  const int M = W / PF_XCDS, P = C / PF_XCDS, R = W / C;
+  int64_t perx = 0;
+  for (int r = 0; r < R; ++r) perx += (int64_t)P * pf_wt(r);
+  const int q = w / M, k = w - q * M, rk = k / P;
+  int64_t acc = q * perx;
+  for (int r = 0; r < rk; ++r) acc += (int64_t)P * pf_wt(r);
+  return acc + (int64_t)(k - rk * P) * pf_wt(rk);
+}
+// first unit of workgroup w: floor(U S(w) / S(W)), S the weight prefix sum
+__device__ __forceinline__ int64_t pf_split_begin(int w, int64_t U, int W, int C) {
+  return U * pf_wsum(w, W, C) / pf_wsum(W, W, C);
 }
 
 // Segments of the ragged batch, in order: for each sequence s, for each KV
@@ -171,18 +218,21 @@ __device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t* wsum, int
 //      scan gives every sequence its first segment (seq_seg0, kept in LDS
 //      when the batch has at most PF_PREP_LDS_SEQS sequences);
 //   2. each thread takes a contiguous range of segments, writes their
-//      descriptors {sequence, KV head, query tile, key tiles} and sums the
-//      tiles; a scan gives the tile prefix sums seg_cu;
-//   3. each thread gives every workgroup whose first unit falls in one of its
-//      segments that (segment, tile): workgroup w starts at unit
-//      floor(w U / W), which lies in the segment of tiles [c, c + n) exactly
-//      when ceil(c W / U) <= w < ceil((c + n) W / U).
+//      descriptors {sequence, KV head, query tile, key tiles} and sums their
+//      units (key tiles plus PF_OV start-up units for a segment with tiles);
+//      a scan gives the unit prefix sums seg_cu;
+//   3. the split: wg_begin[w] = pf_split_begin(w), the first unit of
+//      workgroup w (kept in LDS for the searches below);
+//   4. for each workgroup with units, the (segment, unit offset) holding its
+//      first unit, and for each segment the workgroup holding its first unit
+//      (seg_w0, read by the merge): binary searches over seg_cu and wg_begin.
 // A batch whose offsets disagree with total_q and max_q_len (an offset
 // outside [0, total_q], a decreasing offset or a chunk longer than max_q_len),
 // which could need more segments than the workspace was sized for or reach
 // rows outside q and out, or one with 2^31 key tiles or more, is given no
 // work: {0, 0} in the header.
 constexpr int PF_PREP_LDS_SEQS = 4095;
+constexpr int PF_PREP_LDS_WGS = 2048;
 __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int num_seqs, int total_q,
                                                             int max_q_len, int QB,
                                                             int num_wgs, int32_t* __restrict__ hdr,
@@ -190,10 +240,13 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
                                                             int32_t* __restrict__ seg_cu,
                                                             int4* __restrict__ seg_desc,
                                                             int32_t* __restrict__ wg_start,
+                                                            int32_t* __restrict__ wg_begin,
+                                                            int32_t* __restrict__ seg_w0,
                                                             int32_t* __restrict__ drow_ctx,
                                                             int32_t* __restrict__ drow_map) {
   __shared__ int64_t wsum[32];
   __shared__ int32_t seq_seg0_l[PF_PREP_LDS_SEQS + 1];
+  __shared__ int32_t wgb_l[PF_PREP_LDS_WGS + 1];
   const int t = threadIdx.x;
   const bool in_lds = num_seqs <= PF_PREP_LDS_SEQS;
   int32_t* seq_seg0 = in_lds ? seq_seg0_l : seq_seg0_g;
@@ -255,7 +308,7 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
       const int kvh = local / nq, qt = local % nq;
       const int n = seg_tiles(L, a.context_lens[s], qt, QB, a.causal);
       seg_desc[g] = make_int4(s, kvh, qt, n);
-      ct += n;
+      ct += n > 0 ? n + PF_OV : 0;
     }
   }
   int64_t U_all;
@@ -263,25 +316,50 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
   const bool ok = U_all < ((int64_t)1 << 31);
   const int64_t U = ok ? U_all : 0;
   const int nseg_used = ok ? nseg : 0;
-  // 3. the thread's segments: their prefix sums and the workgroups starting in them
+  // 3. the thread's segments' prefix sums; the split
   if (ok) {
     int64_t c = ct_end - ct;
     for (int g = g0; g < g1; ++g) {
       seg_cu[g] = (int)c;
-      const int n = seg_desc[g].w;
-      if (n > 0) {
-        const int64_t wlo = (c * num_wgs + U - 1) / U;
-        const int64_t whi = min((int64_t)num_wgs, ((c + n) * num_wgs + U - 1) / U);
-        for (int64_t w = wlo; w < whi; ++w) {
-          wg_start[2 * w] = g;
-          wg_start[2 * w + 1] = (int)(w * U / num_wgs - c);
-        }
+      c += seg_desc[g].w > 0 ? seg_desc[g].w + PF_OV : 0;
+    }
+  }
+  if (t == 0) seg_cu[nseg_used] = (int)U;
+  const bool wgb_in_lds = num_wgs <= PF_PREP_LDS_WGS;
+  const int32_t* wgb = wgb_in_lds ? wgb_l : wg_begin;
+  for (int w = t; w <= num_wgs; w += 1024) {
+    const int x = (int)pf_split_begin(w, U, num_wgs, a.cus);
+    wg_begin[w] = x;
+    if (wgb_in_lds) wgb_l[w] = x;
+  }
+  __threadfence_block();
+  __syncthreads();
+  // 4. each workgroup's first (segment, unit): the segment whose units hold
+  //    its first unit (a segment of no units is never chosen); and each
+  //    segment's first workgroup, for the merge
+  if (U > 0) {
+    for (int w = t; w < num_wgs; w += 1024) {
+      const int x = wgb[w];
+      if (x >= wgb[w + 1]) continue;            // no units
+      int lo = 0, hi = nseg_used;               // seg_cu[lo] <= x < seg_cu[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seg_cu[mid] <= x) lo = mid; else hi = mid;
       }
-      c += n;
+      wg_start[2 * w] = lo;
+      wg_start[2 * w + 1] = x - seg_cu[lo];
+    }
+    for (int g = g0; g < min(g1, nseg_used); ++g) {
+      const int c = seg_cu[g];
+      int lo = 0, hi = num_wgs;                 // wgb[lo] <= c < wgb[hi] = U
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (wgb[mid] <= c) lo = mid; else hi = mid;
+      }
+      seg_w0[g] = lo;
     }
   }
   if (t == 0) {
-    seg_cu[nseg_used] = (int)U;
     hdr[0] = nseg_used;
     hdr[1] = (int)U;
   }
@@ -450,24 +528,20 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   const int64_t blk_bytes = (int64_t)a.block_size * a.tok_stride;
 
   const int jmax = min((T - 1) >> a.bs_log2, a.max_blocks - 1);
-  auto gload = [&](int t, TileRegs& R) {
+  // table entries of tile t (blocks of 16 tokens or more): read a tile ahead of
+  // the tile's loads, so their scalar loads return while a tile is computed
+  auto tab = [&](int t, int& b0, int& b1) {
     if (a.block_size >= 16) {
-      // the tile spans at most two blocks; their table entries are read
-      // wave-uniformly (scalar loads, which do not wait behind the K/V loads
-      // in flight; a vector load of both entries issued a tile ahead, with the
-      // K/V loads, measured 7% slower).  Keys past the context read stale
-      // rows of the last block (never outside it): their scores are masked
-      // and their V rows zeroed when stored
       const int jlo = min((t * PF_BN) >> a.bs_log2, jmax);
-      int blo = uniform_load(table, jlo);
-      blo = (unsigned)blo < (unsigned)a.num_blocks ? blo : 0;
+      b0 = uniform_load(table, jlo);
+      b1 = uniform_load(table, min(jlo + 1, jmax));
+    }
+  };
+  auto gload = [&](int t, int blo, int b1, TileRegs& R) {
+    if (a.block_size >= 16) {
+      b1 = a.block_size != 16 ? blo : b1;
       const int inb = (t * PF_BN) & (a.block_size - 1);   // first key's offset in its block
-      int b1 = blo, inb1 = inb + 16;                        // block and offset of key 16
-      if (a.block_size == 16) {
-        b1 = uniform_load(table, min(jlo + 1, jmax));
-        b1 = (unsigned)b1 < (unsigned)a.num_blocks ? b1 : 0;
-        inb1 = 0;
-      }
+      const int inb1 = a.block_size == 16 ? 0 : inb + 16;
       const int64_t off0 = blo * blk_bytes + inb * a.tok_stride;
       const int64_t off1 = b1 * blk_bytes + inb1 * a.tok_stride;
       const int32_t nb0 = (int32_t)(blk_bytes - inb * a.tok_stride);
@@ -631,13 +705,26 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   // tiles below tfull hold only keys that every row of the segment sees
   const int tfull = min(T, a.causal ? first_pos + 1 : T) / PF_BN;
   TileRegs R0;
-  gload(t0, R0);
+  int nb0 = 0, nb1 = 0;
+  tab(t0, nb0, nb1);
+  nb0 = (unsigned)nb0 < (unsigned)a.num_blocks ? nb0 : 0;
+  nb1 = (unsigned)nb1 < (unsigned)a.num_blocks ? nb1 : 0;
+  gload(t0, nb0, nb1, R0);
+  tab(min(t0 + 1, t1 - 1), nb0, nb1);
+  nb0 = (unsigned)nb0 < (unsigned)a.num_blocks ? nb0 : 0;
+  nb1 = (unsigned)nb1 < (unsigned)a.num_blocks ? nb1 : 0;
   int boff = 0;
   auto tile = [&](int t, auto masked) {
     sstore(R0, lds + boff, t);
-    gload(min(t + 1, t1 - 1), R0);
+    gload(min(t + 1, t1 - 1), nb0, nb1, R0);
     __syncthreads();
+    tab(min(t + 2, t1 - 1), nb0, nb1);
     if (wave_ok) compute(lds + boff, t, masked);
+    // ids outside the pool read block 0 (their keys are past the context or
+    // the table breaks its contract); checked here, after the tile, where the
+    // scalar loads have long returned
+    nb0 = (unsigned)nb0 < (unsigned)a.num_blocks ? nb0 : 0;
+    nb1 = (unsigned)nb1 < (unsigned)a.num_blocks ? nb1 : 0;
     boff ^= BUF;
   };
   const int tm = max(t0, min(t1, tfull));
@@ -683,25 +770,31 @@ __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillAr
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LD::BUF];
   const int W = gridDim.x;
   const int wg = xcd_local_order(blockIdx.x, W);
-  const int64_t U = uniform_load(a.hdr, 1);
-  const int64_t u0 = pf_begin(wg, U, W), u1 = pf_begin(wg + 1, U, W);
+  const int64_t u0 = uniform_load(a.wg_begin, wg), u1 = uniform_load(a.wg_begin, wg + 1);
   if (u0 >= u1) return;
   int g = a.wg_start[2 * wg];
-  int tile = a.wg_start[2 * wg + 1];
+  int off = a.wg_start[2 * wg + 1];
   int64_t u = u0;
+  // segment g holds units [seg_cu[g], seg_cu[g + 1]): PF_OV start-up units,
+  // then its key tiles; a range that holds only start-up units of a segment
+  // computes nothing there
   while (true) {
-    const int nt = uniform_load(a.seg_cu, g + 1) - uniform_load(a.seg_cu, g);
-    const int end = (int)min((int64_t)nt, tile + (u1 - u));
-    prefill_piece<CDT, HD, G>(a, g, tile, end, nt, wg, lds);
-    u += end - tile;
+    const int nu = uniform_load(a.seg_cu, g + 1) - uniform_load(a.seg_cu, g);
+    const int end = (int)min((int64_t)nu, off + (u1 - u));
+    const int tb = max(off - PF_OV, 0), te = max(end - PF_OV, 0);
+    if (te > tb) prefill_piece<CDT, HD, G>(a, g, tb, te, nu - PF_OV, wg, lds);
+    u += end - off;
     if (u >= u1) break;
     do { ++g; } while (uniform_load(a.seg_cu, g + 1) == uniform_load(a.seg_cu, g));
-    tile = 0;
+    off = 0;
   }
 }
 
 // Combine the pieces of segments split between workgroups (segments done by
-// one workgroup were written directly).  Workgroup (g, part) takes 256 / (HD / 4)
+// one workgroup were written directly).  The workgroups holding a segment's
+// units are seg_w0[g], seg_w0[g] + 1, ... up to the one whose range passes the
+// segment's end; each contributes the key tiles of its range (a range inside
+// the start-up units contributes none).  Workgroup (g, part) takes 256 / (HD / 4)
 // rows of segment g; each row is read by HD / 4 consecutive lanes (four dims
 // each), so every load and store of a wave covers whole rows, and each
 // thread merges one row slice in a single online pass over the pieces.
@@ -721,9 +814,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
   if (g >= a.hdr[0]) return;
   const int64_t c0 = a.seg_cu[g], c1 = a.seg_cu[g + 1];
   if (c1 <= c0) return;
-  const int64_t U = a.hdr[1];
-  const int w0 = pf_owner(c0, U, num_wgs), w1 = pf_owner(c1 - 1, U, num_wgs);
-  if (w0 == w1) return;
+  const int w0 = a.seg_w0[g];
+  if (a.wg_begin[w0 + 1] >= c1) return;          // one workgroup wrote the whole segment
   const int4 dsc = a.seg_desc[g];
   const int s = dsc.x, kvh = dsc.y, qt = dsc.z;
   const int q0 = a.cu_q[s];
@@ -735,9 +827,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
   if (qi >= L) return;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float M = -INFINITY, lsum = 0.0f;
-#pragma unroll 4
-  for (int w = w0; w <= w1; ++w) {
-    if (pf_begin(w, U, num_wgs) >= pf_begin(w + 1, U, num_wgs)) continue;   // empty workgroup
+  const int nt = (int)(c1 - c0) - PF_OV;
+  for (int w = w0; w < num_wgs; ++w) {
+    const int64_t wb = a.wg_begin[w], we = a.wg_begin[w + 1];
+    if (wb >= c1) break;
+    const int64_t b = max(wb, c0) - c0, e = min(we, c1) - c0;
+    const int64_t tb = max(b - PF_OV, (int64_t)0), te = max(e - PF_OV, (int64_t)0);
+    if (te <= tb) continue;                       // no tile of this segment
+    if (tb == 0 && te == nt) return;              // the whole segment, written directly
     const int64_t row = ((int64_t)w + g) * PF_ROWS + rr;
     const float2 ml = *(const float2*)(a.part_ml + row * 2);
     const float4 o = *(const float4*)(a.part_o + row * HD + d0);
@@ -772,7 +869,7 @@ constexpr int PF_MAX_WGS_PER_CU = 4;   // bounds the workspace (LDS allows at mo
 // length 1 for the decode path (their contexts and q/out rows, and the decode
 // split's partials).
 struct PfLayout {
-  size_t hdr, seq, seg, desc, wgs, ml, o, drow_ctx, drow_map, dws, dws_bytes, total;
+  size_t hdr, seq, seg, desc, wgs, wgb, sw0, ml, o, drow_ctx, drow_map, dws, dws_bytes, total;
 };
 static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_dim, int n_kv,
                           int G) {
@@ -783,7 +880,9 @@ static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_
   l.seg = l.seq + pf_align((size_t)(num_seqs + 1) * 4);
   l.desc = l.seg + pf_align((size_t)(nseg + 1) * 4);
   l.wgs = l.desc + pf_align((size_t)nseg * 16);
-  l.ml = l.wgs + pf_align((size_t)wgs * 2 * 4);
+  l.wgb = l.wgs + pf_align((size_t)wgs * 2 * 4);
+  l.sw0 = l.wgb + pf_align((size_t)(wgs + 1) * 4);
+  l.ml = l.sw0 + pf_align((size_t)nseg * 4);
   l.o = l.ml + pf_align(slots * PF_ROWS * 2 * 4);
   l.drow_ctx = l.o + pf_align(slots * PF_ROWS * head_dim * 4);
   l.drow_map = l.drow_ctx + pf_align((size_t)num_seqs * 4);
@@ -816,11 +915,14 @@ static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_l
   a.seg_cu = (const int32_t*)(ws + l.seg);
   a.seg_desc = (const int4*)(ws + l.desc);
   a.wg_start = (const int32_t*)(ws + l.wgs);
+  a.wg_begin = (const int32_t*)(ws + l.wgb);
+  a.seg_w0 = (const int32_t*)(ws + l.sw0);
   a.part_ml = (float*)(ws + l.ml);
   a.part_o = (float*)(ws + l.o);
   pa_status e = launch(prefill_prep_kernel, dim3(1), dim3(1024), 0, st, a, num_seqs, total_q,
                        max_q_len, PF_ROWS / G, W, (int32_t*)(ws + l.hdr), (int32_t*)(ws + l.seq),
                        (int32_t*)(ws + l.seg), (int4*)(ws + l.desc), (int32_t*)(ws + l.wgs),
+                       (int32_t*)(ws + l.wgb), (int32_t*)(ws + l.sw0),
                        route ? (int32_t*)(ws + l.drow_ctx) : nullptr,
                        route ? (int32_t*)(ws + l.drow_map) : nullptr);
   if (e == PA_OK) e = launch(prefill_kernel<CDT, HD, G>, dim3(W), dim3(256), 0, st, a);
@@ -916,10 +1018,10 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   // the kernel takes row maxima of the unscaled scores
   if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_SHAPE;
   const int64_t nseg = pf_nseg_bound(num_seqs, total_q, max_q_len, n_kv_heads, group_size);
-  // key tiles are counted in 32-bit integers
+  // units (key tiles and start-up units) are counted in 32-bit integers
   // (the merge launches PF_ROWS / 4 workgroups per segment at head_dim 64)
   if (nseg * (PF_ROWS / 4) >= ((int64_t)1 << 31) ||
-      nseg * ((int64_t)max_context_len / PF_BN + 1) >= ((int64_t)1 << 31))
+      nseg * ((int64_t)max_context_len / PF_BN + 1 + PF_OV) >= ((int64_t)1 << 31))
     return PA_ERR_SHAPE;
   const PfLayout l = pf_layout(num_seqs, nseg, (int64_t)pf_cu_count() * PF_MAX_WGS_PER_CU, head_dim,
                                n_kv_heads, group_size);
@@ -945,6 +1047,7 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   a.n_kv = n_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.nseg_max = (int)nseg;
+  a.cus = pf_cu_count();
   a.causal = causal != 0;
   a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.out_scale = fp8 ? v_scale : 1.0f;

@@ -84,50 +84,122 @@ def replay_decode(ctx, n_kv, hw, W):
     assert read == set(written)
 
 
-def replay_prefill(tiles, W):
-    """Prefill: units (segment, 32-key tile); a piece of workgroup w in segment g -> slot w + g."""
-    cu = [0]
-    for t in tiles:
-        cu.append(cu[-1] + t)
-    U, nseg = cu[-1], len(tiles)
-    written, covered = {}, [0] * U
+PF_OV = 3                        # start-up units per segment with tiles (prefill.hip)
+PF_WT = (64, 60, 53, 50)         # split weights of the dispatch rounds (prefill.hip)
+XCDS = 8
+
+
+def pf_wsum(w, W, C, wt=PF_WT):
+    """Sum of the split weights of workgroups [0, w) in the XCD-local work order."""
+    if not (C > 0 and C % XCDS == 0 and W % C == 0 and W // C <= 4 and W % XCDS == 0):
+        return 64 * w
+    M, P, R = W // XCDS, C // XCDS, W // C
+    perx = sum(P * wt[r] for r in range(R))
+    q, k = divmod(w, M)
+    rk = k // P
+    return q * perx + sum(P * wt[r] for r in range(rk)) + (k - rk * P) * wt[rk]
+
+
+def pf_split(U, W, C, wt=PF_WT):
+    """wg_begin: workgroup w takes units [b[w], b[w + 1])."""
+    S = pf_wsum(W, W, C, wt)
+    return [U * pf_wsum(w, W, C, wt) // S for w in range(W + 1)]
+
+
+def prefill_planner_starts(cu, wgb):
+    """The planner's step 4: each workgroup's first (segment, unit offset) and
+    each segment's first workgroup, by binary search as the kernel does."""
+    nseg, W, U = len(cu) - 1, len(wgb) - 1, cu[-1]
+    start = {}
     for w in range(W):
-        u0, u1 = begin(w, U, W), begin(w + 1, U, W)
+        x = wgb[w]
+        if x >= wgb[w + 1]:
+            continue
+        lo, hi = 0, nseg
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if cu[mid] <= x:
+                lo = mid
+            else:
+                hi = mid
+        start[w] = (lo, x - cu[lo])
+    w0 = {}
+    for g in range(nseg):
+        if cu[g + 1] <= cu[g]:
+            continue
+        lo, hi = 0, W
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if wgb[mid] <= cu[g]:
+                lo = mid
+            else:
+                hi = mid
+        w0[g] = lo
+    return start, w0
+
+
+def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
+    """Prefill: a segment with n key tiles holds n + ov units (start-up units
+    first); workgroup w takes units [wg_begin[w], wg_begin[w + 1]); a piece of
+    workgroup w in segment g -> slot w + g; the merge walks the workgroups from
+    seg_w0[g] and reads the pieces with tiles."""
+    units = [n + ov if n > 0 else 0 for n in tiles]
+    cu = [0]
+    for n in units:
+        cu.append(cu[-1] + n)
+    U, nseg = cu[-1], len(tiles)
+    wgb = pf_split(U, W, C, wt)
+    assert wgb[0] == 0 and wgb[W] == U and all(a <= b for a, b in zip(wgb, wgb[1:]))
+    start, w0 = prefill_planner_starts(cu, wgb)
+    written, covered = {}, [[0] * n for n in tiles]
+    for w in range(W):
+        u0, u1 = wgb[w], wgb[w + 1]
         if u0 >= u1:
             continue
-        g = next(i for i in range(nseg) if cu[i + 1] > u0)
-        tile, u = u0 - cu[g], u0
+        g, off = start[w]
+        assert cu[g] <= u0 < cu[g + 1]
+        u = u0
         while True:
-            end = min(tiles[g], tile + (u1 - u))
-            whole = tile == 0 and end == tiles[g]
-            if not whole:
-                slot = w + g
-                assert slot < W + nseg and slot not in written
-                written[slot] = (g, tile, end)
-            for t in range(tile, end):
-                covered[cu[g] + t] += 1
-            u += end - tile
+            nu = cu[g + 1] - cu[g]
+            end = min(nu, off + (u1 - u))
+            tb, te = max(off - ov, 0), max(end - ov, 0)
+            if te > tb:
+                if not (tb == 0 and te == nu - ov):
+                    slot = w + g
+                    assert slot < W + nseg and slot not in written
+                    written[slot] = (g, tb, te)
+                for t in range(tb, te):
+                    covered[g][t] += 1
+            u += end - off
             if u >= u1:
                 break
-            tile, g = 0, g + 1
-            while tiles[g] == 0:
+            g, off = g + 1, 0
+            while cu[g + 1] == cu[g]:
                 g += 1
-    assert all(c == 1 for c in covered)
+    assert all(c == 1 for row in covered for c in row)
     read = set()
     for g in range(nseg):
-        if tiles[g] == 0:
+        c0, c1 = cu[g], cu[g + 1]
+        if c1 <= c0:
             continue
-        w0, w1 = owner(cu[g], U, W), owner(cu[g + 1] - 1, U, W)
-        if w0 == w1:
-            continue                               # written whole by one workgroup
-        got = 0
-        for w in range(w0, w1 + 1):
-            if begin(w, U, W) >= begin(w + 1, U, W):
-                continue
-            assert (w + g) in written and written[w + g][0] == g
-            got += written[w + g][2] - written[w + g][1]
-            read.add(w + g)
-        assert got == tiles[g]
+        w = w0[g]
+        assert wgb[w] <= c0 < wgb[w + 1]
+        if wgb[w + 1] >= c1:
+            assert (w + g) not in written          # written whole by one workgroup
+            continue
+        got, whole = 0, False
+        while w < W and wgb[w] < c1:
+            b, e = max(wgb[w], c0) - c0, min(wgb[w + 1], c1) - c0
+            tb, te = max(b - ov, 0), max(e - ov, 0)
+            if te > tb:
+                if tb == 0 and te == tiles[g]:
+                    whole = True
+                    break
+                assert written[w + g] == (g, tb, te)
+                got += te - tb
+                read.add(w + g)
+            w += 1
+        assert whole or got == tiles[g]
     assert read == set(written)
 
 
@@ -152,8 +224,10 @@ def test_prefill_split_covers_every_tile_once(seed):
         tiles = [rng.choice([0, 1, 2, 5, rng.randint(1, 40)]) for _ in range(rng.randint(1, 10))]
         if sum(tiles) == 0:
             continue
-        for W in (1, 2, 3, 5, 17, 256):
-            replay_prefill(tiles, W)
+        for W, C in ((1, 0), (2, 0), (3, 0), (5, 0), (17, 0), (256, 0), (768, 256), (24, 8),
+                     (512, 256), (1024, 256), (17, 256), (912, 304)):
+            replay_prefill(tiles, W, C)
+            replay_prefill(tiles, W, C, wt=(7, 5, 3, 1), ov=rng.choice([0, 1, 5]))
 
 
 PF_ROWS, PF_BN = 128, 32
@@ -214,8 +288,8 @@ def test_prefill_plan_covers_every_row_once(seed):
         assert len(seen) == sum(lens) * n_kv * G
         tiles = [t for (_, _, _, t) in segs]
         if sum(tiles):
-            for W in (1, 3, 64, 1000):
-                replay_prefill(tiles, W)
+            for W, C in ((1, 0), (3, 0), (64, 0), (1000, 0), (768, 256)):
+                replay_prefill(tiles, W, C)
 
 
 def decode_row_lists(lens, ctx):
@@ -279,32 +353,41 @@ def test_prefill_plan_with_decode_rows_covers_every_row_once(seed):
 
 
 def test_prefill_planner_workgroup_starts():
-    """The planner gives workgroup w the (segment, tile) holding unit floor(w U / W)
-    by letting each segment [c, c + n) claim w in [ceil(c W / U), ceil((c + n) W / U)):
-    every workgroup is claimed exactly once, by the segment the split expects."""
+    """The planner's binary searches give workgroup w the segment whose units
+    hold its first unit (never a segment of no units) and give each segment the
+    workgroup holding its first unit; with equal weights the split is
+    floor(w U / W), as in the decode kernel."""
     rng = random.Random(300)
     for _ in range(500):
         tiles = [rng.choice([0, 0, 1, 2, 7, rng.randint(1, 60)]) for _ in range(rng.randint(1, 30))]
-        U = sum(tiles)
+        units = [n + PF_OV if n > 0 else 0 for n in tiles]
+        U = sum(units)
         if U == 0:
             continue
-        for W in (1, 2, 3, 7, 64, 768, 1024):
-            claims = {}
-            c = 0
-            for g, n in enumerate(tiles):
-                if n > 0:
-                    for w in range((c * W + U - 1) // U, min(W, ((c + n) * W + U - 1) // U)):
-                        assert w not in claims
-                        claims[w] = (g, w * U // W - c)
-                c += n
-            assert sorted(claims) == list(range(W))
-            cu = [0]
-            for n in tiles:
-                cu.append(cu[-1] + n)
-            for w, (g, tile) in claims.items():
-                x = begin(w, U, W)
-                assert g == next(i for i in range(len(tiles)) if cu[i + 1] > x)
-                assert tile == x - cu[g]
+        cu = [0]
+        for n in units:
+            cu.append(cu[-1] + n)
+        for W, C in ((1, 0), (2, 0), (7, 0), (64, 0), (768, 256), (1024, 256), (768, 0)):
+            wgb = pf_split(U, W, C)
+            if C == 0:
+                assert wgb == [begin(w, U, W) for w in range(W + 1)]
+            start, w0 = prefill_planner_starts(cu, wgb)
+            for w, (g, off) in start.items():
+                assert units[g] > 0 and 0 <= off < units[g] and cu[g] + off == wgb[w]
+            for g, w in w0.items():
+                assert wgb[w] <= cu[g] < wgb[w + 1]
+
+
+def test_prefill_split_weights_follow_the_rounds():
+    """With three rounds of 256 CUs (768 workgroups in the XCD-local order), the
+    workgroups of round r take units in proportion PF_WT[r]."""
+    U, W, C = 10 ** 6, 768, 256
+    wgb = pf_split(U, W, C)
+    share = [wgb[w + 1] - wgb[w] for w in range(W)]
+    for w in range(W):
+        k = w % (W // XCDS)                    # index inside the XCD's range
+        r = k // (C // XCDS)                   # its dispatch round
+        assert abs(share[w] - U * PF_WT[r] / (C * sum(PF_WT[:3]))) <= 1
 
 
 def row_g(t):
