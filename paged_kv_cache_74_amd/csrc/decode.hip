@@ -44,7 +44,7 @@
 //     l is accumulated from the same rounded weights.  fp32 caches take an fp32
 //     FMA path instead (no rounding of the weights).
 //   * K/V of the next step are in flight while the current one is computed.
-#include "pa_device.h"
+#include "internal.h"
 
 #include <mutex>
 
@@ -504,16 +504,26 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
 //
 // A unit is one 16-token step of one (sequence, KV head group) segment, a
 // group being the hw consecutive KV heads that the hw waves of a workgroup
-// take; units are ordered by (sequence, head group, step).  With U units and W
-// resident workgroups, workgroup w processes units [floor(w U / W),
-// floor((w+1) U / W)): every workgroup gets the same amount of work, whatever
-// the mix of context lengths.  Each wave emits one partial (m, l, O) for every
+// take; units are ordered by (sequence, head group, step).  A segment with
+// steps also counts DECODE_SEG_OV start-up units ahead of its steps: a piece
+// of a segment loads its queries, fills its load pipeline and stores its
+// partial, which measured as about four steps' time (on the long-tail step,
+// with 8-bit codes, each further sequence a workgroup touched added 6.5 us to
+// its 280 us, and the launch lasted as long as its workgroups with 5-8
+// sequences).  With U units and W resident workgroups, workgroup w processes
+// units [floor(w U / W), floor((w+1) U / W)): every workgroup gets the same
+// time's worth of work, whatever the mix of context lengths; a range that
+// holds only start-up units of a segment computes nothing there.  Each wave emits one partial (m, l, O) for every
 // segment piece it covers; the piece of workgroup w in segment g is stored in
 // slot w + g (one entry per wave of the group), which is unique because both
 // workgroup and segment boundaries are increasing along the unit order.  The
 // merge kernel finds the workgroups covering a segment from its unit range.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int steps_of(int ctx) { return ctx > 0 ? (ctx + 15) >> 4 : 0; }
+// units of a segment in the split: its steps and the start-up units
+__host__ __device__ __forceinline__ int units_of(int ctx) {
+  return ctx > 0 ? ((ctx + 15) >> 4) + DECODE_SEG_OV : 0;
+}
 
 // Both quotients are taken in double precision instead of 64-bit integer
 // division (a long scalar sequence, on the merge kernel's critical path).  They
@@ -536,7 +546,7 @@ __device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int
                                             int s, int* pre, int* all) {
   int a = 0, b = 0;
   for (int i = threadIdx.x & 63; i < num_seqs; i += 64) {
-    const int v = nhg * steps_of(ctx[i]);
+    const int v = nhg * units_of(ctx[i]);
     b += v;
     if (i < s) a += v;
   }
@@ -557,7 +567,7 @@ __device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int
   int carry = 0;
   for (int base = 0; base < num_seqs; base += 64) {
     const int i = base + lane;
-    const int v = i < num_seqs ? nhg * steps_of(ctx[i]) : 0;
+    const int v = i < num_seqs ? nhg * units_of(ctx[i]) : 0;
     int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -743,19 +753,20 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
   if (u0 >= u1) return;
   int s, before;
   locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
-  const int steps0 = steps_of(uniform_load(a.context_lens, s));
+  const int len0 = units_of(uniform_load(a.context_lens, s));
   const int r = (int)u0 - before;
-  int hg = r / steps0;
-  int step = r % steps0;
+  int hg = r / len0;
+  int off = r % len0;                  // unit offset in the segment
   int64_t u = u0;
   while (true) {
-    const int steps = steps_of(uniform_load(a.context_lens, s));
-    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
+    const int len = units_of(uniform_load(a.context_lens, s));
+    const int end = (int)min((int64_t)len, off + (u1 - u));
+    const int sb = max(off - DECODE_SEG_OV, 0), se = max(end - DECODE_SEG_OV, 0);   // steps
     const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
-    decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, step, run_end, slot * a.hw + wv);
-    u += run_end - step;
+    if (se > sb) decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, sb, se, slot * a.hw + wv);
+    u += end - off;
     if (u >= u1) break;
-    step = 0;
+    off = 0;
     if (++hg == a.nhg) {               // next sequence that has tokens
       hg = 0;
       do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
@@ -1371,10 +1382,10 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   if (u0 >= u1) return;
   int s, before;
   locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
-  const int steps0 = steps_of(uniform_load(a.context_lens, s));
+  const int len0 = units_of(uniform_load(a.context_lens, s));
   const int rr = (int)u0 - before;
-  int hg = rr / steps0;
-  int step = rr % steps0;
+  int hg = rr / len0;
+  int off = rr % len0;                 // unit offset in the segment
   uint8_t* vl = lds + (SLICES ? wv * ML::WAVE_LDS : 0);
   auto run = [&](int rs, int rhg, int first, int last) {
     const int64_t slot = (int64_t)w + (int64_t)rs * a.nhg + rhg;
@@ -1382,7 +1393,7 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
                                                     slot * a.hw + wv, vl, wv, lds + SLICES);
   };
   auto next_segment = [&]() {
-    step = 0;
+    off = 0;
     if (++hg == a.nhg) {               // next sequence that has tokens
       hg = 0;
       do { ++s; } while (steps_of(uniform_load(a.context_lens, s)) == 0);
@@ -1390,10 +1401,11 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   };
   int64_t u = u0;
   while (true) {
-    const int steps = steps_of(uniform_load(a.context_lens, s));
-    const int run_end = (int)min((int64_t)steps, step + (u1 - u));
-    run(s, hg, step, run_end);
-    u += run_end - step;
+    const int len = units_of(uniform_load(a.context_lens, s));
+    const int end = (int)min((int64_t)len, off + (u1 - u));
+    const int sb = max(off - DECODE_SEG_OV, 0), se = max(end - DECODE_SEG_OV, 0);   // steps
+    if (se > sb) run(s, hg, sb, se);
+    u += end - off;
     if (u >= u1) break;
     next_segment();
   }
@@ -1427,7 +1439,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (steps > 0) {
     const int64_t U = Ui;
     const int num_wgs = header[0];
-    const int64_t g0 = (int64_t)pre + (int64_t)hg * steps;
+    // the segment's steps are units [g0, g0 + steps), after its start-up units;
+    // w0 holds its first step, so its piece exists
+    const int64_t g0 = (int64_t)pre + (int64_t)hg * (steps + DECODE_SEG_OV) + DECODE_SEG_OV;
     const int g = s * nhg + hg;
     const int w0 = wave_of(g0, U, num_wgs), w1 = wave_of(g0 + steps - 1, U, num_wgs);
     const int npc = w1 - w0 + 1;
@@ -1536,7 +1550,7 @@ static int heads_per_wg(int cache_dtype, int n_kv, int G) {
 // total context (for tests).
 static int64_t wgs_bound(int hw, int num_seqs, int n_kv, int max_context_len, int split_tokens) {
   if (split_tokens <= 0) return ((int64_t)device_cu_count() * MAX_WAVES_PER_CU + hw - 1) / hw;
-  const int64_t units = (int64_t)num_seqs * (n_kv / hw) * steps_of(max_context_len);
+  const int64_t units = (int64_t)num_seqs * (n_kv / hw) * units_of(max_context_len);
   const int64_t per = (split_tokens + 15) / 16;
   int64_t w = (units + per - 1) / per;
   if (w < 1) w = 1;
@@ -1785,7 +1799,7 @@ static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int 
   if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
     return PA_ERR_UNSUPPORTED;
   // units are counted in 32-bit integers
-  if ((int64_t)num_seqs * n_kv_heads * steps_of(max_context_len) >= (int64_t)1 << 31)
+  if ((int64_t)num_seqs * n_kv_heads * units_of(max_context_len) >= (int64_t)1 << 31)
     return PA_ERR_SHAPE;
   return PA_OK;
 }
@@ -2137,7 +2151,7 @@ pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens
                            const int32_t* context_lens, int max_context_len, int causal,
                            float scale, void* workspace, size_t workspace_bytes,
                            hipStream_t st) {
-  if ((int64_t)total_q * n_kv * steps_of(max_context_len) >= (int64_t)1 << 31) return PA_ERR_SHAPE;
+  if ((int64_t)total_q * n_kv * units_of(max_context_len) >= (int64_t)1 << 31) return PA_ERR_SHAPE;
   const size_t rows = align256((size_t)total_q * 4);
   if (workspace_bytes < prefill_f32_workspace_bytes(total_q, n_kv, G, head_dim, max_context_len))
     return PA_ERR_WORKSPACE;

@@ -6,6 +6,11 @@
 
 namespace pa {
 
+// decode.hip: start-up units per (sequence, KV head group) segment of the
+// decode work split (units are 16-token steps); prefill.hip checks its
+// decode rows' unit count with it.
+constexpr int DECODE_SEG_OV = 4;
+
 // decode.hip: chunked prefill over an fp32 cache, each query row run as a
 // decode row of its chunk's sequence on the vector decode kernel.
 size_t prefill_f32_workspace_bytes(int total_q, int n_kv, int G, int head_dim,

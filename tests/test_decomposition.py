@@ -27,38 +27,46 @@ def owner(x, U, W):
     return ((x + 1) * W - 1) // U
 
 
-def replay_decode(ctx, n_kv, hw, W):
-    """Decode: units (sequence, head group, 16-token step), hw waves per workgroup."""
+DEC_OV = 4                       # start-up units per decode segment (internal.h)
+
+
+def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV):
+    """Decode: units (sequence, head group, 16-token step), hw waves per
+    workgroup; a segment with steps holds its steps after ov start-up units."""
     B, nhg = len(ctx), n_kv // hw
     cu = [0]
     for c in ctx:
-        cu.append(cu[-1] + nhg * steps_of(c))
+        cu.append(cu[-1] + nhg * (steps_of(c) + ov if c > 0 else 0))
     U = cu[-1]
     entries = (W + B * nhg) * hw
-    written, covered = {}, [0] * (U * hw)
+    written, covered = {}, [0] * (sum(nhg * steps_of(c) for c in ctx) * hw)
+    scu = [0]
+    for c in ctx:
+        scu.append(scu[-1] + nhg * steps_of(c))
     for w in range(W):
         u0, u1 = begin(w, U, W), begin(w + 1, U, W)
         if u0 >= u1:
             continue
         s = next(i for i in range(B) if cu[i + 1] > u0)
-        st = steps_of(ctx[s])
-        hg, step = (u0 - cu[s]) // st, (u0 - cu[s]) % st
+        ln = steps_of(ctx[s]) + ov
+        hg, off = (u0 - cu[s]) // ln, (u0 - cu[s]) % ln
         u = u0
         while True:
             steps = steps_of(ctx[s])
-            end = min(steps, step + (u1 - u))
-            assert end > step
+            end = min(steps + ov, off + (u1 - u))
+            sb, se = max(off - ov, 0), max(end - ov, 0)
             slot = w + s * nhg + hg
-            for wv in range(hw):
-                e = slot * hw + wv
-                assert 0 <= e < entries and e not in written
-                written[e] = (s, hg * hw + wv, step, end)
-                for t in range(step, end):
-                    covered[(cu[s] + hg * steps + t) * hw + wv] += 1
-            u += end - step
+            if se > sb:
+                for wv in range(hw):
+                    e = slot * hw + wv
+                    assert 0 <= e < entries and e not in written
+                    written[e] = (s, hg * hw + wv, sb, se)
+                    for t in range(sb, se):
+                        covered[(scu[s] + hg * steps + t) * hw + wv] += 1
+            u += end - off
             if u >= u1:
                 break
-            step, hg = 0, hg + 1
+            off, hg = 0, hg + 1
             if hg == nhg:
                 hg, s = 0, s + 1
                 while steps_of(ctx[s]) == 0:
@@ -71,9 +79,11 @@ def replay_decode(ctx, n_kv, hw, W):
             continue
         for kvh in range(n_kv):
             hg, wv = kvh // hw, kvh % hw
-            g0, g = cu[s] + hg * st, s * nhg + hg
+            g0, g = cu[s] + hg * (st + ov) + ov, s * nhg + hg   # first step's unit
+            w0, w1 = owner(g0, U, W), owner(g0 + st - 1, U, W)
+            assert (w0 + g) * hw + wv in written             # the merge's dummy piece exists
             got = 0
-            for w in range(owner(g0, U, W), owner(g0 + st - 1, U, W) + 1):
+            for w in range(w0, w1 + 1):
                 if begin(w, U, W) >= begin(w + 1, U, W):
                     continue                       # an empty workgroup holds no piece
                 e = (w + g) * hw + wv
@@ -215,6 +225,7 @@ def test_decode_split_covers_every_unit_once(seed):
             continue
         for W in (1, 2, 3, 7, 64, 1000):
             replay_decode(ctx, n_kv, hw, W)
+            replay_decode(ctx, n_kv, hw, W, ov=rng.choice([0, 1, 7]))
 
 
 @pytest.mark.parametrize("seed", range(4))
