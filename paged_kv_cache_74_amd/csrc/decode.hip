@@ -505,12 +505,16 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
 // A unit is one 16-token step of one (sequence, KV head group) segment, a
 // group being the hw consecutive KV heads that the hw waves of a workgroup
 // take; units are ordered by (sequence, head group, step).  A segment with
-// steps also counts DECODE_SEG_OV start-up units ahead of its steps: a piece
-// of a segment loads its queries, fills its load pipeline and stores its
-// partial, which measured as about four steps' time (on the long-tail step,
-// with 8-bit codes, each further sequence a workgroup touched added 6.5 us to
-// its 280 us, and the launch lasted as long as its workgroups with 5-8
-// sequences).  With U units and W resident workgroups, workgroup w processes
+// steps also counts ov start-up units ahead of its steps (decode_seg_ov: 2
+// for 32- and 16-bit caches, 6 for 8- and 4-bit ones): a piece of a segment
+// loads its queries, fills its load pipeline and stores its partial, which is
+// worth more steps where steps carry fewer bytes (on the long-tail step with
+// 8-bit codes, each further sequence a workgroup touched added 6.5 us to its
+// 280 us, and the launch lasted as long as its workgroups with 5-8 sequences;
+// split kernel with 0/2/4/6/8 start-up units, one box: int8 334.9/324.9/
+// 320.2/315.5/313.9 us, int4 259.1/253.0/249.6/249.5/250.0 us, bf16
+// 604.1/594.5/596.6/598.8/598.8 us, Llama-3 211.5/209.6/209.8/209.6/211.9 us).
+// The split kernel writes ov into the workspace header for the merge.  With U units and W resident workgroups, workgroup w processes
 // units [floor(w U / W), floor((w+1) U / W)): every workgroup gets the same
 // time's worth of work, whatever the mix of context lengths; a range that
 // holds only start-up units of a segment computes nothing there.  Each wave emits one partial (m, l, O) for every
@@ -520,9 +524,9 @@ __device__ __forceinline__ int lane_dim(int c, int e) {
 // merge kernel finds the workgroups covering a segment from its unit range.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int steps_of(int ctx) { return ctx > 0 ? (ctx + 15) >> 4 : 0; }
-// units of a segment in the split: its steps and the start-up units
-__host__ __device__ __forceinline__ int units_of(int ctx) {
-  return ctx > 0 ? ((ctx + 15) >> 4) + DECODE_SEG_OV : 0;
+// units of a segment in the split: its steps and ov start-up units
+__host__ __device__ __forceinline__ int units_of(int ctx, int ov) {
+  return ctx > 0 ? ((ctx + 15) >> 4) + ov : 0;
 }
 
 // Both quotients are taken in double precision instead of 64-bit integer
@@ -543,10 +547,10 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
 // Units of the sequences before `s` (pre) and in total (all), one pass of the
 // wave over context_lens (nhg = head groups per sequence).
 __device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int num_seqs, int nhg,
-                                            int s, int* pre, int* all) {
+                                            int ov, int s, int* pre, int* all) {
   int a = 0, b = 0;
   for (int i = threadIdx.x & 63; i < num_seqs; i += 64) {
-    const int v = nhg * units_of(ctx[i]);
+    const int v = nhg * units_of(ctx[i], ov);
     b += v;
     if (i < s) a += v;
   }
@@ -562,12 +566,12 @@ __device__ __forceinline__ void unit_counts(const int32_t* __restrict__ ctx, int
 
 // The sequence holding unit x (0 <= x < U) and the units before it.
 __device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int num_seqs, int nhg,
-                                            int x, int* seq, int* before) {
+                                            int ov, int x, int* seq, int* before) {
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int base = 0; base < num_seqs; base += 64) {
     const int i = base + lane;
-    const int v = i < num_seqs ? nhg * units_of(ctx[i]) : 0;
+    const int v = i < num_seqs ? nhg * units_of(ctx[i], ov) : 0;
     int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -747,21 +751,22 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
   int pre, U;
-  unit_counts(a.context_lens, a.num_seqs, a.nhg, 0, &pre, &U);
-  if (w == 0 && threadIdx.x == 0) *(int2*)a.header = make_int2(W, a.hw);   // for the merge
+  constexpr int OV = decode_seg_ov(CDT);
+  unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
+  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, 0);   // for the merge
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
   int s, before;
-  locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
-  const int len0 = units_of(uniform_load(a.context_lens, s));
+  locate_unit(a.context_lens, a.num_seqs, a.nhg, OV, (int)u0, &s, &before);
+  const int len0 = units_of(uniform_load(a.context_lens, s), OV);
   const int r = (int)u0 - before;
   int hg = r / len0;
   int off = r % len0;                  // unit offset in the segment
   int64_t u = u0;
   while (true) {
-    const int len = units_of(uniform_load(a.context_lens, s));
+    const int len = units_of(uniform_load(a.context_lens, s), OV);
     const int end = (int)min((int64_t)len, off + (u1 - u));
-    const int sb = max(off - DECODE_SEG_OV, 0), se = max(end - DECODE_SEG_OV, 0);   // steps
+    const int sb = max(off - OV, 0), se = max(end - OV, 0);   // steps
     const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
     if (se > sb) decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, sb, se, slot * a.hw + wv);
     u += end - off;
@@ -1371,8 +1376,9 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
   int pre, U;
-  unit_counts(a.context_lens, a.num_seqs, a.nhg, 0, &pre, &U);
-  if (w == 0 && threadIdx.x == 0) *(int2*)a.header = make_int2(W, a.hw);   // for the merge
+  constexpr int OV = decode_seg_ov(CDT);
+  unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
+  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, 0);   // for the merge
   if constexpr (APPEND) {   // sequences without tokens append nothing: slot -1
     if (w == 0 && a.slots_out)
       for (int i = threadIdx.x; i < a.num_seqs; i += blockDim.x)
@@ -1381,8 +1387,8 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
   int s, before;
-  locate_unit(a.context_lens, a.num_seqs, a.nhg, (int)u0, &s, &before);
-  const int len0 = units_of(uniform_load(a.context_lens, s));
+  locate_unit(a.context_lens, a.num_seqs, a.nhg, OV, (int)u0, &s, &before);
+  const int len0 = units_of(uniform_load(a.context_lens, s), OV);
   const int rr = (int)u0 - before;
   int hg = rr / len0;
   int off = rr % len0;                 // unit offset in the segment
@@ -1401,9 +1407,9 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   };
   int64_t u = u0;
   while (true) {
-    const int len = units_of(uniform_load(a.context_lens, s));
+    const int len = units_of(uniform_load(a.context_lens, s), OV);
     const int end = (int)min((int64_t)len, off + (u1 - u));
-    const int sb = max(off - DECODE_SEG_OV, 0), se = max(end - DECODE_SEG_OV, 0);   // steps
+    const int sb = max(off - OV, 0), se = max(end - OV, 0);   // steps
     if (se > sb) run(s, hg, sb, se);
     u += end - off;
     if (u >= u1) break;
@@ -1435,13 +1441,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
   float inv = 0.0f;
   int pre, Ui;
-  unit_counts(context_lens, num_seqs, nhg, s, &pre, &Ui);
+  const int ov = header[2];   // start-up units per segment of the split
+  unit_counts(context_lens, num_seqs, nhg, ov, s, &pre, &Ui);
   if (steps > 0) {
     const int64_t U = Ui;
     const int num_wgs = header[0];
     // the segment's steps are units [g0, g0 + steps), after its start-up units;
     // w0 holds its first step, so its piece exists
-    const int64_t g0 = (int64_t)pre + (int64_t)hg * (steps + DECODE_SEG_OV) + DECODE_SEG_OV;
+    const int64_t g0 = (int64_t)pre + (int64_t)hg * (steps + ov) + ov;
     const int g = s * nhg + hg;
     const int w0 = wave_of(g0, U, num_wgs), w1 = wave_of(g0 + steps - 1, U, num_wgs);
     const int npc = w1 - w0 + 1;
@@ -1550,7 +1557,7 @@ static int heads_per_wg(int cache_dtype, int n_kv, int G) {
 // total context (for tests).
 static int64_t wgs_bound(int hw, int num_seqs, int n_kv, int max_context_len, int split_tokens) {
   if (split_tokens <= 0) return ((int64_t)device_cu_count() * MAX_WAVES_PER_CU + hw - 1) / hw;
-  const int64_t units = (int64_t)num_seqs * (n_kv / hw) * units_of(max_context_len);
+  const int64_t units = (int64_t)num_seqs * (n_kv / hw) * units_of(max_context_len, DECODE_SEG_OV_MAX);
   const int64_t per = (split_tokens + 15) / 16;
   int64_t w = (units + per - 1) / per;
   if (w < 1) w = 1;
@@ -1799,7 +1806,7 @@ static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int 
   if (group_size != 1 && group_size != 2 && group_size != 4 && group_size != 8)
     return PA_ERR_UNSUPPORTED;
   // units are counted in 32-bit integers
-  if ((int64_t)num_seqs * n_kv_heads * units_of(max_context_len) >= (int64_t)1 << 31)
+  if ((int64_t)num_seqs * n_kv_heads * units_of(max_context_len, DECODE_SEG_OV_MAX) >= (int64_t)1 << 31)
     return PA_ERR_SHAPE;
   return PA_OK;
 }
@@ -2151,7 +2158,7 @@ pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens
                            const int32_t* context_lens, int max_context_len, int causal,
                            float scale, void* workspace, size_t workspace_bytes,
                            hipStream_t st) {
-  if ((int64_t)total_q * n_kv * units_of(max_context_len) >= (int64_t)1 << 31) return PA_ERR_SHAPE;
+  if ((int64_t)total_q * n_kv * units_of(max_context_len, DECODE_SEG_OV_MAX) >= (int64_t)1 << 31) return PA_ERR_SHAPE;
   const size_t rows = align256((size_t)total_q * 4);
   if (workspace_bytes < prefill_f32_workspace_bytes(total_q, n_kv, G, head_dim, max_context_len))
     return PA_ERR_WORKSPACE;

@@ -7,9 +7,13 @@
 namespace pa {
 
 // decode.hip: start-up units per (sequence, KV head group) segment of the
-// decode work split (units are 16-token steps); prefill.hip checks its
-// decode rows' unit count with it.
-constexpr int DECODE_SEG_OV = 4;
+// decode work split (units are 16-token steps), by cache dtype; the bound
+// DECODE_SEG_OV_MAX is what the host's unit-count checks use (prefill.hip
+// checks its decode rows' units with it).
+__host__ __device__ constexpr int decode_seg_ov(int cache_dtype) {
+  return cache_dtype == PA_F32 || cache_dtype == PA_BF16 ? 2 : 6;
+}
+constexpr int DECODE_SEG_OV_MAX = 6;
 
 // decode.hip: chunked prefill over an fp32 cache, each query row run as a
 // decode row of its chunk's sequence on the vector decode kernel.

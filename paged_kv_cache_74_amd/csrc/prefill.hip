@@ -1071,7 +1071,7 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   const bool route = block_size >= 16;
   // the decode path counts its 16-token units in 32-bit integers; checked here,
   // before anything is enqueued
-  if (route && (int64_t)num_seqs * n_kv_heads * (((int64_t)max_context_len + 15) / 16 + DECODE_SEG_OV) >=
+  if (route && (int64_t)num_seqs * n_kv_heads * (((int64_t)max_context_len + 15) / 16 + DECODE_SEG_OV_MAX) >=
                    ((int64_t)1 << 31))
     return PA_ERR_SHAPE;
   pa_status e = dispatch(group_size, a, num_seqs, total_q, max_q_len, l, ws, route, st);

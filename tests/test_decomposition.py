@@ -27,10 +27,10 @@ def owner(x, U, W):
     return ((x + 1) * W - 1) // U
 
 
-DEC_OV = 4                       # start-up units per decode segment (internal.h)
+DEC_OV = {"f32": 2, "bf16": 2, "fp8": 6, "int8": 6, "int4": 6}   # decode_seg_ov (internal.h)
 
 
-def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV):
+def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
     """Decode: units (sequence, head group, 16-token step), hw waves per
     workgroup; a segment with steps holds its steps after ov start-up units."""
     B, nhg = len(ctx), n_kv // hw
@@ -225,6 +225,7 @@ def test_decode_split_covers_every_unit_once(seed):
             continue
         for W in (1, 2, 3, 7, 64, 1000):
             replay_decode(ctx, n_kv, hw, W)
+            replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["bf16"])
             replay_decode(ctx, n_kv, hw, W, ov=rng.choice([0, 1, 7]))
 
 
