@@ -536,12 +536,37 @@ __host__ __device__ __forceinline__ int units_of(int ctx, int ov) {
 // least 1/W (1/U) from the next integer, more than the rounding error of the
 // division (half an ulp of a quotient below 2^31 (2^20), at most 2^-23
 // (2^-33)), so the floor of the rounded quotient is the integer quotient.
+//
+// The split is weighted by XCD.  Workgroup w runs on XCD w % 8 (the launch
+// hands workgroups to the eight XCDs round robin), and on MI355X the
+// workgroups of the odd XCDs took 5-8% longer than those of the even ones for
+// the same units (decode split kernel, Llama-3 and long-tail int8 steps, four
+// boxes: odd/even time 1.052-1.084).  With W a multiple of 8 (and at most 2^17,
+// which keeps the quotients below exact), a workgroup of an odd XCD takes
+// DEC_WT_ODD / DEC_WT_EVEN of an even one's share: workgroup w begins at unit
+// floor(U S(w) / S(W)), S(w) the weights of workgroups [0, w).  The weights
+// move split points only.  Exactness with weights: U S(w) < 2^31 * 2^21.1,
+// below 2^53, and a non-integer quotient lies at least 1 / S(W) >= 2^-21.1
+// from an integer, more than the rounding error (2^-22).
+constexpr int DEC_WT_EVEN = 17, DEC_WT_ODD = 16;
+__device__ __forceinline__ bool dec_weighted(int W) { return (W & 7) == 0 && W <= (1 << 17); }
+__device__ __forceinline__ int64_t dec_wsum(int w) {
+  return (int64_t)DEC_WT_EVEN * ((w + 1) >> 1) + (int64_t)DEC_WT_ODD * (w >> 1);
+}
 __device__ __forceinline__ int64_t wave_begin(int w, int64_t U, int W) {
+  if (dec_weighted(W))
+    return (int64_t)__builtin_floor((double)U * (double)dec_wsum(w) / (double)dec_wsum(W));
   return (int64_t)__builtin_floor((double)w * (double)U / (double)W);
 }
-// the wave whose unit range holds unit x (0 <= x < U)
+// the workgroup whose unit range holds unit x (0 <= x < U); with weights the
+// unweighted owner is at most one workgroup off, and is corrected
 __device__ __forceinline__ int wave_of(int64_t x, int64_t U, int W) {
-  return (int)__builtin_floor(((double)(x + 1) * (double)W - 1.0) / (double)U);
+  int w = (int)__builtin_floor(((double)(x + 1) * (double)W - 1.0) / (double)U);
+  if (!dec_weighted(W)) return w;
+  w = min(max(w, 0), W - 1);
+  while (w > 0 && wave_begin(w, U, W) > x) --w;
+  while (w + 1 < W && wave_begin(w + 1, U, W) <= x) ++w;
+  return w;
 }
 
 // Units of the sequences before `s` (pre) and in total (all), one pass of the
@@ -1455,15 +1480,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     // Lane k holds piece w0 + b + k of a sweep over 64 pieces: first the max M
     // of the pieces' m, then each piece's weight 2^(m_k - M), broadcast while
     // every lane sums its dims of the weighted O.  A workgroup with an empty
-    // unit range (only when workgroups outnumber units) holds no piece; it and
+    // unit range (only with fewer units than twice the workgroups) holds no piece; it and
     // the lanes past the last piece get weight 0 and read piece w0's O, which
     // always exists, so the O loads go out four at a time with no tail loop.
     // Most rows have at most 64 pieces: their m and l are loaded once.
     auto entry = [&](int w) -> int64_t { return (((int64_t)w + g) * hw + wv) * G + hl; };
     auto piece_ml = [&](int b, bool* has) -> float2 {
       const int w = w0 + b + t;
-      // with at least as many units as workgroups every workgroup holds a piece
-      *has = w <= w1 && (U >= num_wgs || wave_begin(w, U, num_wgs) < wave_begin(w + 1, U, num_wgs));
+      // with at least twice as many units as workgroups every workgroup holds
+      // a piece (a share is at least 2 * 16 / 17 units)
+      *has = w <= w1 && (U >= 2 * (int64_t)num_wgs ||
+                         wave_begin(w, U, num_wgs) < wave_begin(w + 1, U, num_wgs));
       return *has ? *(const float2*)(part_ml + entry(w) * 2) : make_float2(-INFINITY, 0.0f);
     };
     bool has0;

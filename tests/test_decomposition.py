@@ -10,6 +10,7 @@ collision, a merge that skips or double-counts a piece) fails here without a GPU
 """
 from __future__ import annotations
 
+import math
 import random
 
 import pytest
@@ -28,6 +29,35 @@ def owner(x, U, W):
 
 
 DEC_OV = {"f32": 2, "bf16": 2, "fp8": 6, "int8": 6, "int4": 6}   # decode_seg_ov (internal.h)
+DEC_WT_EVEN, DEC_WT_ODD = 17, 16   # decode split weights by XCD parity (decode.hip)
+
+
+def dec_weighted(W):
+    return W % 8 == 0 and W <= 1 << 17
+
+
+def dec_wsum(w):
+    return DEC_WT_EVEN * ((w + 1) // 2) + DEC_WT_ODD * (w // 2)
+
+
+def dec_begin(w, U, W):
+    """wave_begin: floor(U S(w) / S(W)) in double precision, as the kernel takes it."""
+    if dec_weighted(W):
+        return int(math.floor(float(U) * float(dec_wsum(w)) / float(dec_wsum(W))))
+    return int(math.floor(float(w) * float(U) / float(W)))
+
+
+def dec_owner(x, U, W):
+    """wave_of: the unweighted owner, corrected by single steps."""
+    w = int(math.floor((float(x + 1) * float(W) - 1.0) / float(U)))
+    if not dec_weighted(W):
+        return w
+    w = min(max(w, 0), W - 1)
+    while w > 0 and dec_begin(w, U, W) > x:
+        w -= 1
+    while w + 1 < W and dec_begin(w + 1, U, W) <= x:
+        w += 1
+    return w
 
 
 def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
@@ -44,7 +74,7 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
     for c in ctx:
         scu.append(scu[-1] + nhg * steps_of(c))
     for w in range(W):
-        u0, u1 = begin(w, U, W), begin(w + 1, U, W)
+        u0, u1 = dec_begin(w, U, W), dec_begin(w + 1, U, W)
         if u0 >= u1:
             continue
         s = next(i for i in range(B) if cu[i + 1] > u0)
@@ -72,6 +102,10 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
                 while steps_of(ctx[s]) == 0:
                     s += 1
     assert all(c == 1 for c in covered)
+    b = [dec_begin(w, U, W) for w in range(W + 1)]
+    assert b[0] == 0 and b[W] == U and all(x <= y for x, y in zip(b, b[1:]))
+    if U >= 2 * W:
+        assert all(x < y for x, y in zip(b, b[1:]))   # the merge's shortcut: no empty share
     read = set()
     for s in range(B):
         st = steps_of(ctx[s])
@@ -80,11 +114,11 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
         for kvh in range(n_kv):
             hg, wv = kvh // hw, kvh % hw
             g0, g = cu[s] + hg * (st + ov) + ov, s * nhg + hg   # first step's unit
-            w0, w1 = owner(g0, U, W), owner(g0 + st - 1, U, W)
+            w0, w1 = dec_owner(g0, U, W), dec_owner(g0 + st - 1, U, W)
             assert (w0 + g) * hw + wv in written             # the merge's dummy piece exists
             got = 0
             for w in range(w0, w1 + 1):
-                if begin(w, U, W) >= begin(w + 1, U, W):
+                if dec_begin(w, U, W) >= dec_begin(w + 1, U, W):
                     continue                       # an empty workgroup holds no piece
                 e = (w + g) * hw + wv
                 assert e in written and written[e][:2] == (s, kvh)
@@ -213,6 +247,27 @@ def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
     assert read == set(written)
 
 
+def test_decode_weighted_split_owner_and_exactness():
+    """With the XCD-parity weights, wave_of's corrected owner holds each unit,
+    odd workgroups take 16/17 of an even one's share, and the double-precision
+    quotient equals the integer one up to U < 2^31, W = 2^17."""
+    rng = random.Random(11)
+    for _ in range(200):
+        W = 8 * rng.randint(1, 200)
+        U = rng.randint(1, 60 * W)
+        for x in sorted(rng.sample(range(U), min(U, 300))) + [0, U - 1]:
+            w = dec_owner(x, U, W)
+            assert dec_begin(w, U, W) <= x < dec_begin(w + 1, U, W)
+    W, U = 256, 10 ** 6
+    sh = [dec_begin(w + 1, U, W) - dec_begin(w, U, W) for w in range(W)]
+    even, odd = sum(sh[0::2]), sum(sh[1::2])
+    assert abs(odd / even - DEC_WT_ODD / DEC_WT_EVEN) < 1e-3
+    for U in (2 ** 31 - 1, 2 ** 31 - 12345, 987654321):
+        W = 1 << 17
+        for w in [0, 1, 2, 3, W // 3, W // 2 + 1, W - 2, W - 1, W] + rng.sample(range(W), 200):
+            assert dec_begin(w, U, W) == U * dec_wsum(w) // dec_wsum(W)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_decode_split_covers_every_unit_once(seed):
     rng = random.Random(seed)
@@ -223,7 +278,7 @@ def test_decode_split_covers_every_unit_once(seed):
         ctx = [rng.choice([0, 0, 1, 15, 16, 17, rng.randint(1, 300)]) for _ in range(B)]
         if sum(ctx) == 0:
             continue
-        for W in (1, 2, 3, 7, 64, 1000):
+        for W in (1, 2, 3, 7, 8, 64, 256, 1000, 1024):
             replay_decode(ctx, n_kv, hw, W)
             replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["bf16"])
             replay_decode(ctx, n_kv, hw, W, ov=rng.choice([0, 1, 7]))
