@@ -66,12 +66,15 @@ constexpr int PF_ROWS = 32 * PF_WAVES;   // query rows per workgroup
 constexpr int PF_BN = 32;                // keys per tile
 constexpr int PF_LOG2_TSUM = 12;
 // Start-up units per segment: a piece of a segment also loads the segment's
-// queries, waits for its first tile and stores its rows, which measured as
-// about three tiles' time (a workgroup given 28 short causal segments took
-// 515 us against 385 us for one given 1-2 long ones, at equal tile counts).
-// They are units of the split that hold no tile.
+// queries, waits for its first tile and stores its rows (a workgroup given 28
+// short causal segments took 515 us against 385 us for one given 1-2 long
+// ones, at equal tile counts), and the short causal segments slow the other
+// workgroups on their CU as well: with 3 start-up units the three workgroups
+// on each CU holding them took 450 us against 408 us for the rest of the XCD,
+// with 6 404 against 400 us, with 10 357 against 386 us.  They are units of the
+// split that hold no tile.
 #ifndef PF_SEG_OV
-#define PF_SEG_OV 3
+#define PF_SEG_OV 8
 #endif
 constexpr int PF_OV = PF_SEG_OV;
 constexpr float PF_TSUM_MAX = (float)(1 << PF_LOG2_TSUM);

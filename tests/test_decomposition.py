@@ -128,7 +128,7 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
     assert read == set(written)
 
 
-PF_OV = 3                        # start-up units per segment with tiles (prefill.hip)
+PF_OV = 8                        # start-up units per segment with tiles (prefill.hip)
 PF_WT = (64, 60, 53, 50)         # split weights of the dispatch rounds (prefill.hip)
 XCDS = 8
 
