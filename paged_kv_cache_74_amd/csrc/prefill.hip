@@ -150,13 +150,14 @@ __device__ __forceinline__ int seg_tiles(int L, int T, int qt, int QB, int causa
 // the R workgroups sharing a SIMD are issued oldest first: measured with equal
 // tile counts on the mixed step (three per CU), workgroups of rounds 0, 1 and 2
 // took 385, 403 and 435 us on average.  A workgroup of round r therefore takes
-// a share of the units proportional to pf_wt(r) (with these weights the three
-// rounds finished at 404, 405 and 412 us).  In the XCD-local work order
+// a share of the units proportional to pf_wt(r) (with weights 64, 59, 51 the
+// three rounds finished at 395, 399 and 405 us on average; with 64, 60, 53 at
+// 393, 401 and 410 us).  In the XCD-local work order
 // (xcd_local_order) workgroup w = x M + k, M = W / 8, was block 8 k + x, of
 // round k / (C / 8).  The weights only move split points; any other dispatch
 // order gives the same results, only less evenly timed.
 #ifndef PF_WT
-#define PF_WT 64, 60, 53, 50
+#define PF_WT 64, 59, 50, 47
 #endif
 __device__ __forceinline__ int pf_wt(int r) {
   constexpr int t[4] = {PF_WT};

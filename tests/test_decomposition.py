@@ -129,7 +129,7 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
 
 
 PF_OV = 8                        # start-up units per segment with tiles (prefill.hip)
-PF_WT = (64, 60, 53, 50)         # split weights of the dispatch rounds (prefill.hip)
+PF_WT = (64, 59, 50, 47)         # split weights of the dispatch rounds (prefill.hip)
 XCDS = 8
 
 
