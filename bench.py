@@ -86,8 +86,10 @@ def byte_model(w):
             "split_append_kernel": split + append}
 
 
-DECODE_SOURCES = ("paged_kv_cache_74_amd/csrc/decode.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
-PREFILL_SOURCES = ("paged_kv_cache_74_amd/csrc/prefill.hip", "paged_kv_cache_74_amd/csrc/pa_device.h")
+DECODE_SOURCES = ("paged_kv_cache_74_amd/csrc/decode.hip", "paged_kv_cache_74_amd/csrc/pa_device.h",
+                  "paged_kv_cache_74_amd/csrc/internal.h")
+PREFILL_SOURCES = ("paged_kv_cache_74_amd/csrc/prefill.hip", "paged_kv_cache_74_amd/csrc/pa_device.h",
+                   "paged_kv_cache_74_amd/csrc/internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -153,6 +155,14 @@ def measure_ceilings(w, dw, kc, vc, dev, want_mfma: bool):
         fsink = torch.empty(4 * Wm, dtype=torch.float32, device=dev)
         ms = timed(lambda: probes.pa_ceiling_mfma_bf16(fsink, Wm, iters))
         rec["mfma_bf16_TFLOPs"] = round(Wm * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12, 1)
+        # with one operand from LDS per MFMA, as prefill reads K and V^T: the best
+        # of two and three workgroups per CU (prefill runs three)
+        best = 0.0
+        for Wl in (cus * 2, cus * 3):
+            fs = torch.empty(4 * Wl, dtype=torch.float32, device=dev)
+            ms = timed(lambda: probes.pa_ceiling_mfma_bf16_lds(fs, Wl, iters))
+            best = max(best, Wl * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12)
+        rec["mfma_bf16_lds_operand_TFLOPs"] = round(best, 1)
     return rec
 
 
@@ -696,10 +706,13 @@ def main():
             ceil["split_kernel_frac_of_table_order_read"] = round(logical / tbl, 4)
             msg += f" (split kernel: {logical:.0f} GB/s of logical K/V = {logical / tbl:.1%} of the first)"
         if "mfma_bf16_TFLOPs" in ceil:
-            msg += f", bf16 MFMA loop {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s"
+            msg += (f", bf16 MFMA loop {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s "
+                    f"({ceil['mfma_bf16_lds_operand_TFLOPs']:.0f} with one operand from LDS)")
             if prefill_rec:
                 prefill_rec["frac_of_mfma_loop"] = round(
                     prefill_rec["achieved"] / ceil["mfma_bf16_TFLOPs"], 4)
+                prefill_rec["frac_of_lds_operand_loop"] = round(
+                    prefill_rec["achieved"] / ceil["mfma_bf16_lds_operand_TFLOPs"], 4)
         log(msg)
 
     cpu = None

@@ -32,6 +32,7 @@ def lib():
         for name, args in (("pa_ceiling_stream_read", (P, L64, P, I, P)),
                            ("pa_ceiling_gather_read", (P, P, L64, I, P, L64, P, I, P)),
                            ("pa_ceiling_mfma_bf16", (P, I, I, P)),
+                           ("pa_ceiling_mfma_bf16_lds", (P, I, I, P)),
                            ("pa_probe_lds_pattern", (P, I, I, P, I, P))):
             f = getattr(_lib, name)
             f.restype = ctypes.c_int
@@ -73,6 +74,14 @@ def pa_ceiling_mfma_bf16(sink: torch.Tensor, num_wgs: int, iters: int, stream=No
     _need(sink.dtype == torch.float32 and sink.numel() >= 4 * num_wgs, "sink: float32 [4 W]")
     _check("pa_ceiling_mfma_bf16", lib().pa_ceiling_mfma_bf16(_ptr(sink), num_wgs, iters,
                                                               _stream(stream)))
+
+
+def pa_ceiling_mfma_bf16_lds(sink: torch.Tensor, num_wgs: int, iters: int, stream=None) -> None:
+    """Matrix-core issue rate with one operand read from LDS per MFMA; sink: float32 [num_wgs * 4]."""
+    _dev(sink)
+    _need(sink.dtype == torch.float32 and sink.numel() >= 4 * num_wgs, "sink: float32 [4 W]")
+    _check("pa_ceiling_mfma_bf16_lds", lib().pa_ceiling_mfma_bf16_lds(_ptr(sink), num_wgs, iters,
+                                                                      _stream(stream)))
 
 
 LDS_KINDS = {"write_b128": 0, "read_b128": 1, "read_b64_tr_b16": 2, "read_b64": 3}

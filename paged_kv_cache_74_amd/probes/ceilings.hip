@@ -4,7 +4,8 @@
 // HBM, 2.5 PFLOP/s dense bf16): a decode kernel is judged against what reading
 // the same blocks in the same order can reach (and in physical order, for the
 // cost of the order), the prefill kernel against what v_mfma_f32_32x32x16_bf16
-// can reach.  Not part of the attention path: built into libpa_probes.so, a
+// can reach, with its operands in registers and with one operand read from LDS
+// for every instruction, as the prefill kernel reads K and V^T.  Not part of the attention path: built into libpa_probes.so, a
 // library of its own that only the benchmark and its tests load.
 //
 // Every reader folds what it reads into an XOR checksum that it writes out, so
@@ -104,6 +105,39 @@ __global__ __launch_bounds__(256) void ceiling_mfma_kernel(int iters, float* sin
 
 using namespace pa;
 
+// The prefill kernel's operand traffic without its softmax: every MFMA reads its
+// A operand (32 rows x 16 bf16, 1 KiB per wave) from LDS with one ds_read_b128
+// per lane, as the score (K) and PV (V^T) products do; B stays in registers.
+// Each wave cycles through 16 KiB of LDS, 1 KiB per read, consecutive lanes on
+// consecutive 16-byte chunks (no bank conflicts).
+constexpr int CEIL_LDS_BYTES = 16 * 1024;
+__global__ __launch_bounds__(256) void ceiling_mfma_lds_kernel(int iters, float* sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CEIL_LDS_BYTES];
+  for (int i = threadIdx.x; i < CEIL_LDS_BYTES / 4; i += blockDim.x)
+    ((uint32_t*)lds)[i] = 0x3F803F80u;   // bf16 pairs of 1.0
+  __syncthreads();
+  cbf16x8_t one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = (__bf16)1.0f;
+  cf32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const int lane = threadIdx.x & 63;
+  for (int i = 0; i < iters; ++i) {
+    const int base = ((4 * i) & 15) * 1024 + lane * 16;
+    const cbf16x8_t a0 = *(const cbf16x8_t*)(lds + base);
+    const cbf16x8_t a1 = *(const cbf16x8_t*)(lds + ((base + 1024) & (CEIL_LDS_BYTES - 1)));
+    const cbf16x8_t a2 = *(const cbf16x8_t*)(lds + ((base + 2048) & (CEIL_LDS_BYTES - 1)));
+    const cbf16x8_t a3 = *(const cbf16x8_t*)(lds + ((base + 3072) & (CEIL_LDS_BYTES - 1)));
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, one, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, one, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, one, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, one, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s;
+}
+
 extern "C" pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                                             int32_t num_wgs, void* stream) {
   if (bytes < 0 || bytes % 16 != 0 || num_wgs < 1) return PA_ERR_SHAPE;
@@ -135,4 +169,12 @@ extern "C" pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t 
   if (!sink) return PA_ERR_NULL;
   return launch(ceiling_mfma_kernel, dim3((unsigned)num_wgs), dim3(256), 0, (hipStream_t)stream,
                 iters, sink);
+}
+
+extern "C" pa_status pa_ceiling_mfma_bf16_lds(float* sink, int32_t num_wgs, int32_t iters,
+                                              void* stream) {
+  if (num_wgs < 1 || iters < 1) return PA_ERR_SHAPE;
+  if (!sink) return PA_ERR_NULL;
+  return launch(ceiling_mfma_lds_kernel, dim3((unsigned)num_wgs), dim3(256), 0,
+                (hipStream_t)stream, iters, sink);
 }

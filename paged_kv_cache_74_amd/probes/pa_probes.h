@@ -37,6 +37,10 @@ extern "C" {
  *   independent v_mfma_f32_32x32x16_bf16 (A = B = 1); sink (float
  *   [num_wgs * 4]) receives 64 * 16 * iters per wave.  FLOPs per launch:
  *   num_wgs * 4 * iters * 4 * 32768.
+ * pa_ceiling_mfma_bf16_lds: the same, with each MFMA's A operand (1 KiB per
+ *   wave) read from LDS by one ds_read_b128 per lane (the prefill kernel's
+ *   operand traffic for its score and PV products); LDS holds bf16 1.0, so
+ *   sink receives the same values.  FLOPs per launch as above.
  */
 pa_status pa_ceiling_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                                  int32_t num_wgs, void* stream);
@@ -44,6 +48,7 @@ pa_status pa_ceiling_gather_read(const void* k_pool, const void* v_pool, int64_t
                                  int32_t block_bytes, const int32_t* blocks, int64_t n,
                                  uint32_t* sink, int32_t num_wgs, void* stream);
 pa_status pa_ceiling_mfma_bf16(float* sink, int32_t num_wgs, int32_t iters, void* stream);
+pa_status pa_ceiling_mfma_bf16_lds(float* sink, int32_t num_wgs, int32_t iters, void* stream);
 
 /*
  * pa_probe_lds_pattern: LDS bank groups, one access pattern per launch, read

@@ -80,7 +80,7 @@ def test_measurement_probes_live_in_their_own_library():
     text = re.sub(r"/\*.*?\*/", "", open(PROBES_HEADER).read(), flags=re.S)
     declared = set(re.findall(r"\b(pa_\w+)\s*\(", text))
     assert declared == {"pa_ceiling_stream_read", "pa_ceiling_gather_read", "pa_ceiling_mfma_bf16",
-                        "pa_probe_lds_pattern"}
+                        "pa_ceiling_mfma_bf16_lds", "pa_probe_lds_pattern"}
     assert not declared & set(_declarations())
     nm = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout

@@ -64,6 +64,16 @@ def test_mfma_loop_sums(dev):
     assert (sink.cpu().numpy() == 64.0 * 16 * iters).all()
 
 
+def test_mfma_lds_operand_loop_sums(dev):
+    """The loop with its A operands read from LDS (bf16 1.0) sums as the register loop."""
+    from paged_kv_cache_74_amd import probes
+    W, iters = 16, 300
+    sink = torch.zeros(4 * W, dtype=torch.float32, device=dev)
+    probes.pa_ceiling_mfma_bf16_lds(sink, W, iters)
+    torch.cuda.synchronize()
+    assert (sink.cpu().numpy() == 64.0 * 16 * iters).all()
+
+
 def _lds_elements_xor(offsets, nbytes):
     """XOR of the 16-bit elements a wave reads: each lane's nbytes at its offset, the LDS
     area holding element k = (k * 40503) mod 2^16."""
