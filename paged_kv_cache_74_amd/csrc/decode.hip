@@ -89,7 +89,8 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  int32_t* header;           // {workgroups, waves per workgroup}, written for the merge
+  int32_t* header;           // {workgroups, waves per workgroup, start-up units, units}, for the merge
+  int32_t* seg_w;            // [segments][2]: workgroups that ran a segment's first and last step
   float* part_o;      // [slots][HW][G][HD]   slot = workgroup + segment
   float* part_ml;     // [slots][HW][G][2]
   int64_t tok_stride; // bytes between consecutive tokens of a block (n_kv * ROW)
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
   int pre, U;
   constexpr int OV = decode_seg_ov(CDT);
   unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
-  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, 0);   // for the merge
+  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, U);   // for the merge
   const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
   int s, before;
@@ -792,8 +793,14 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
     const int len = units_of(uniform_load(a.context_lens, s), OV);
     const int end = (int)min((int64_t)len, off + (u1 - u));
     const int sb = max(off - OV, 0), se = max(end - OV, 0);   // steps
-    const int64_t slot = (int64_t)w + (int64_t)s * a.nhg + hg;
-    if (se > sb) decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, sb, se, slot * a.hw + wv);
+    const int64_t g = (int64_t)s * a.nhg + hg;
+    if (se > sb) {
+      decode_run<CDT, HD, G, NBUF>(a, s, hg * a.hw + wv, sb, se, (w + g) * a.hw + wv);
+      if (threadIdx.x == 0) {   // the merge reads the segment's pieces from these
+        if (sb == 0) a.seg_w[2 * g] = w;
+        if (se == len - OV) a.seg_w[2 * g + 1] = w;
+      }
+    }
     u += end - off;
     if (u >= u1) break;
     off = 0;
@@ -1403,7 +1410,7 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   int pre, U;
   constexpr int OV = decode_seg_ov(CDT);
   unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
-  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, 0);   // for the merge
+  if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, U);   // for the merge
   if constexpr (APPEND) {   // sequences without tokens append nothing: slot -1
     if (w == 0 && a.slots_out)
       for (int i = threadIdx.x; i < a.num_seqs; i += blockDim.x)
@@ -1435,7 +1442,14 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
     const int len = units_of(uniform_load(a.context_lens, s), OV);
     const int end = (int)min((int64_t)len, off + (u1 - u));
     const int sb = max(off - OV, 0), se = max(end - OV, 0);   // steps
-    if (se > sb) run(s, hg, sb, se);
+    if (se > sb) {
+      run(s, hg, sb, se);
+      if (threadIdx.x == 0) {   // the merge reads the segment's pieces from these
+        const int64_t g = (int64_t)s * a.nhg + hg;
+        if (sb == 0) a.seg_w[2 * g] = w;
+        if (se == len - OV) a.seg_w[2 * g + 1] = w;
+      }
+    }
     u += end - off;
     if (u >= u1) break;
     next_segment();
@@ -1446,8 +1460,9 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
 template <int HD, int G, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ header, int num_seqs,
-    int n_kv, float v_scale, const int32_t* __restrict__ row_map) {
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ header,
+    const int32_t* __restrict__ seg_w, int num_seqs, int n_kv, float v_scale,
+    const int32_t* __restrict__ row_map) {
   constexpr int DPT = HD / 64;   // dims per thread
   const int n_q = n_kv * G;
   const int hw = header[1];
@@ -1465,17 +1480,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
   float inv = 0.0f;
-  int pre, Ui;
-  const int ov = header[2];   // start-up units per segment of the split
-  unit_counts(context_lens, num_seqs, nhg, ov, s, &pre, &Ui);
   if (steps > 0) {
-    const int64_t U = Ui;
+    const int64_t U = header[3];
     const int num_wgs = header[0];
-    // the segment's steps are units [g0, g0 + steps), after its start-up units;
-    // w0 holds its first step, so its piece exists
-    const int64_t g0 = (int64_t)pre + (int64_t)hg * (steps + ov) + ov;
+    // the workgroups that ran the segment's first and last steps (the split
+    // kernel records them): its pieces are theirs and those of the workgroups
+    // between them; w0's piece always exists
     const int g = s * nhg + hg;
-    const int w0 = wave_of(g0, U, num_wgs), w1 = wave_of(g0 + steps - 1, U, num_wgs);
+    const int w0 = seg_w[2 * g], w1 = seg_w[2 * g + 1];
     const int npc = w1 - w0 + 1;
     // Lane k holds piece w0 + b + k of a sweep over 64 pieces: first the max M
     // of the pieces' m, then each piece's weight 2^(m_k - M), broadcast while
@@ -1607,12 +1619,15 @@ static int64_t entries_bound(int num_seqs, int n_kv, int G, int max_context_len,
 }
 
 struct WsLayout {
-  size_t hdr, ml, o, total;
+  size_t hdr, seg, ml, o, total;
 };
-static WsLayout ws_layout(int64_t entries, int G, int head_dim) {
+// header (256 bytes), the segments' first/last workgroups (two int32 per
+// (sequence, KV head) bound), then the partials
+static WsLayout ws_layout(int64_t entries, int G, int head_dim, int64_t segs) {
   WsLayout l;
   l.hdr = 0;
-  l.ml = 256;
+  l.seg = 256;
+  l.ml = l.seg + align256((size_t)segs * 2 * 4);
   l.o = l.ml + align256((size_t)entries * G * 2 * 4);
   l.total = l.o + align256((size_t)entries * G * head_dim * 4);
   return l;
@@ -1794,7 +1809,8 @@ static pa_status launch_merge_t(void* out, const WsLayout& l, const void* ws, co
   const char* base = (const char*)ws;
   return launch(decode_merge_kernel<HD, G, BF16>, dim3((unsigned)((int64_t)num_seqs * n_kv * G)),
                 dim3(64), 0, st, out, (const float*)(base + l.o), (const float*)(base + l.ml),
-                ctx, (const int32_t*)(base + l.hdr), num_seqs, n_kv, out_scale, row_map);
+                ctx, (const int32_t*)(base + l.hdr), (const int32_t*)(base + l.seg), num_seqs, n_kv,
+                out_scale, row_map);
 }
 
 template <int HD, bool BF16>
@@ -1822,7 +1838,7 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
     return 0;
   const int G = n_q_heads / n_kv_heads;
   return ws_layout(entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G,
-                   head_dim).total;
+                   head_dim, (int64_t)num_seqs * n_kv_heads).total;
 }
 
 static pa_status check_common(int num_seqs, int n_kv_heads, int group_size, int head_dim,
@@ -1879,7 +1895,8 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   if (int4 && (!k_channel_scales || !v_token_scales)) return PA_ERR_NULL;
   const int G = group_size;
   const WsLayout l = ws_layout(
-      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
+      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim,
+      (int64_t)num_seqs * n_kv_heads);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   // 8-bit caches (fp8 or int8) carry per-tensor scales
   const bool fp8 = cache_dtype == PA_FP8_E4M3 || cache_dtype == PA_INT8;
@@ -1903,6 +1920,7 @@ static pa_status decode_impl(void* out, bool merge, const void* q, int q_dtype,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.header = (int32_t*)(base + l.hdr);
+  a.seg_w = (int32_t*)(base + l.seg);
   a.part_ml = (float*)(base + l.ml);
   a.part_o = (float*)(base + l.o);
   const int ebits = cache_dtype == PA_F32 ? 32 : cache_dtype == PA_BF16 ? 16 : int4 ? 4 : 8;
@@ -2023,7 +2041,8 @@ extern "C" pa_status pa_decode_merge(void* out, int out_dtype, const int32_t* co
   if (num_seqs == 0) return PA_OK;
   if (!out || !context_lens) return PA_ERR_NULL;
   const WsLayout l = ws_layout(
-      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim);
+      entries_bound(num_seqs, n_kv_heads, G, max_context_len, split_tokens), G, head_dim,
+      (int64_t)num_seqs * n_kv_heads);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255)) return PA_ERR_WORKSPACE;
   return launch_merge(out, out_dtype, context_lens, num_seqs, n_kv_heads, G, head_dim, l,
                       out_scale, workspace, (hipStream_t)stream);
@@ -2074,7 +2093,7 @@ extern "C" pa_status pa_decode_no_alloc(void* out, const void* q, int q_dtype, c
   // the partials this call needs, against the scratch's fixed size (no HIP call yet)
   const WsLayout l = ws_layout(
       entries_bound(num_seqs, n_kv_heads, group_size, max_context_len, split_tokens), group_size,
-      head_dim);
+      head_dim, (int64_t)num_seqs * n_kv_heads);
   if (l.total > PA_NO_ALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
   void* ws = scratch_address();
   if (!ws) return PA_ERR_HIP;
@@ -2153,7 +2172,7 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
 
 size_t prefill_decode_rows_workspace_bytes(int num_seqs, int n_kv, int G, int head_dim) {
   if (num_seqs <= 0) return 0;
-  return ws_layout(entries_bound(num_seqs, n_kv, G, 0, 0), G, head_dim).total;
+  return ws_layout(entries_bound(num_seqs, n_kv, G, 0, 0), G, head_dim, (int64_t)num_seqs * n_kv).total;
 }
 
 pa_status prefill_decode_rows(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -2175,7 +2194,8 @@ size_t prefill_f32_workspace_bytes(int total_q, int n_kv, int G, int head_dim,
                                    int max_context_len) {
   if (total_q <= 0) return 0;
   return 2 * align256((size_t)total_q * 4) +
-         ws_layout(entries_bound(total_q, n_kv, G, max_context_len, 0), G, head_dim).total;
+         ws_layout(entries_bound(total_q, n_kv, G, max_context_len, 0), G, head_dim,
+                   (int64_t)total_q * n_kv).total;
 }
 
 pa_status prefill_f32_rows(float* out, const float* q, const int32_t* cu_seqlens_q, int num_seqs,

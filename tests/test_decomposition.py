@@ -69,7 +69,7 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
         cu.append(cu[-1] + nhg * (steps_of(c) + ov if c > 0 else 0))
     U = cu[-1]
     entries = (W + B * nhg) * hw
-    written, covered = {}, [0] * (sum(nhg * steps_of(c) for c in ctx) * hw)
+    written, covered, seg_w = {}, [0] * (sum(nhg * steps_of(c) for c in ctx) * hw), {}
     scu = [0]
     for c in ctx:
         scu.append(scu[-1] + nhg * steps_of(c))
@@ -87,6 +87,10 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
             sb, se = max(off - ov, 0), max(end - ov, 0)
             slot = w + s * nhg + hg
             if se > sb:
+                if sb == 0:                            # the kernel records the segment's
+                    seg_w.setdefault((s, hg), [None, None])[0] = w   # first and last
+                if se == steps:                        # steps' workgroups for the merge
+                    seg_w.setdefault((s, hg), [None, None])[1] = w
                 for wv in range(hw):
                     e = slot * hw + wv
                     assert 0 <= e < entries and e not in written
@@ -114,7 +118,8 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
         for kvh in range(n_kv):
             hg, wv = kvh // hw, kvh % hw
             g0, g = cu[s] + hg * (st + ov) + ov, s * nhg + hg   # first step's unit
-            w0, w1 = dec_owner(g0, U, W), dec_owner(g0 + st - 1, U, W)
+            w0, w1 = seg_w[(s, hg)]
+            assert (w0, w1) == (dec_owner(g0, U, W), dec_owner(g0 + st - 1, U, W))
             assert (w0 + g) * hw + wv in written             # the merge's dummy piece exists
             got = 0
             for w in range(w0, w1 + 1):
