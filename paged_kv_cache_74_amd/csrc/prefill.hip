@@ -1071,8 +1071,12 @@ static pa_status prefill_impl(void* out, const void* q, int q_dtype, const int32
   // when the blocks allow it (16 tokens or more): whole token rows streamed
   // through the matrix cores, where the tile kernel would give such a row one
   // wave in four and 4 of its 32 query columns.  The planner lists them; the
-  // tile kernel skips them.
-  const bool route = block_size >= 16;
+  // tile kernel skips them.  A batch declared as num_seqs chunks of max_q_len
+  // (> 1) queries each has no such row, and then the decode path's launches
+  // are not enqueued (about 8 us of empty launches on the mixed step); if its
+  // offsets held a row of length 1 after all, the tile kernel computes it.
+  const bool route = block_size >= 16 &&
+                     !(max_q_len > 1 && (int64_t)total_q == (int64_t)num_seqs * max_q_len);
   // the decode path counts its 16-token units in 32-bit integers; checked here,
   // before anything is enqueued
   if (route && (int64_t)num_seqs * n_kv_heads * (((int64_t)max_context_len + 15) / 16 + DECODE_SEG_OV_MAX) >=

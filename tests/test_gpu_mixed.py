@@ -132,3 +132,28 @@ def test_offsets_past_the_bounds_do_no_work(dev):
                         int(w.context_lens.max()), w.scale, out=out)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_uniform_declaration_with_a_short_row(dev):
+    """A batch declared as num_seqs chunks of max_q_len queries (total_q =
+    num_seqs * max_q_len) runs no decode-row launches; if its offsets end below
+    total_q and hold a row of length 1 after all, the tile kernel computes that
+    row, and every row matches the oracle."""
+    import paged_kv_cache_74_amd as pa
+    from gpu_harness import i32, to_f64
+    w = workloads.mixed_prefill_decode(prior=(0, 40), chunk_lens=(64, 64), n_decode=1, dlo=30,
+                                       dhi=90, seed=9)
+    workloads.draw_values(w, "cpu")
+    dw = _device(w, dev)
+    cu = w.cu(w.q_lens)
+    B, n = w.num_seqs, int(cu[-1])
+    assert list(w.q_lens) == [64, 64, 1]
+    q = torch.zeros((B * 64,) + tuple(dw.q.shape[1:]), dtype=dw.q.dtype, device=dev)
+    q[:n] = dw.q
+    out = torch.full_like(q, 7.0)
+    pa.pa_prefill_chunk(q, dw.k_cache, dw.v_cache, i32(cu, dev), dw.tables, dw.ctx, 64,
+                        int(w.context_lens.max()), w.scale, out=out)
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(w)
+    check_close(to_f64(out[:n]), _oracle_all(w, pk, pv), "bf16", "uniform declaration, short row")
+    assert bool((out[n:] == 7.0).all())
