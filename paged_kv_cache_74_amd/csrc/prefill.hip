@@ -120,6 +120,43 @@ struct PrefillLds {
   static constexpr int BUF = K_BYTES + V_BYTES + SIG_BYTES;
 };
 
+// Tiles loaded straight into LDS (bf16 caches, head_dim 128, blocks of 16
+// tokens or more): buffer loads with an LDS destination (each instruction
+// writes 64 lanes x 16 bytes of LDS in lane order) fill a ring of three
+// stages, two tiles ahead, with no register staging.  A stage holds the
+// tile's 32 K rows and 32 V rows as they sit in the cache (256 bytes each),
+// swizzled so that the operand reads meet no bank conflicts:
+//   * K: 16-byte chunk c of row r at chunk c ^ (r & 7).  A score operand read
+//     takes the same chunk of 8 consecutive rows per 8 lanes: 8 different
+//     chunk positions (16-byte accesses are served 8 lanes at a time, free
+//     when the 8 differ in address bits 4..6).
+//   * V: 64-byte block b of row r at block b ^ pfv_g(r).  The PV operand
+//     (V^T, 32 dims x 16 keys) comes from two ds_read_b64_tr_b16 per MFMA:
+//     each 16 lanes supply the rows of 4 keys and receive, per lane, one
+//     dim's 4 values.  The 32 lanes served together read 4 rows
+//     {x, x + 16, x + 1, x + 17} (x even, bit 4 clear) at one 64-byte block,
+//     which pfv_g sends to 4 different blocks of a 256-byte window.
+// Keys past the context load the context's last row instead (through the
+// same block), so every V row in LDS is finite; their scores are masked.
+constexpr int PF_DROW = 256;                    // bytes of a bf16 row at head_dim 128
+constexpr int PF_DSTAGE = 2 * PF_BN * PF_DROW;  // K and V of one tile
+constexpr int PF_DSTAGES = 3;
+__device__ __forceinline__ int pfv_g(int r) { return (r & 1) | ((r >> 3) & 2); }
+typedef short pf_s4_t __attribute__((ext_vector_type(4)));
+// One buffer-to-LDS load: 16 bytes per lane at voff from r, written to LDS at
+// lds_addr + 16 * lane.  Written in assembly so that the compiler, which does
+// not see it, inserts no waits of its own for it: the tile loop waits for
+// these loads itself (vmcnt) before the barrier that publishes a tile.  The
+// instruction has no register results.
+__device__ __forceinline__ void pf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t pf_lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
 // Workgroups are dispatched to the chip's 8 XCDs round robin (workgroup b on
 // XCD b % 8), each XCD with its own L2.  Renumbering them so that every XCD
 // holds a contiguous range of the work order puts the query tiles of one
@@ -443,9 +480,10 @@ __device__ __forceinline__ int widened_elem(int i, bool hi) {
   else return 2 * i + (hi ? 1 : 0);
 }
 
-template <int CDT, int HD, int G>
+template <int CDT, int HD, int G, bool DIRECT>
 __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t0, int t1, int nt,
                                               int wg, uint8_t* lds) {
+  static_assert(!DIRECT || (CDT == PA_BF16 && HD == 128), "direct tiles: bf16, head_dim 128");
   using LD = PrefillLds<CDT, HD>;
   constexpr int QB = PF_ROWS / G;            // queries per segment
   constexpr int EBITS = CDT == PA_BF16 ? 16 : CDT == PA_INT4 ? 4 : 8;
@@ -615,14 +653,15 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   auto compute = [&](const uint8_t* buf, int kt, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     const uint8_t* lk = buf;
-    const uint8_t* lv = buf + LD::K_BYTES;
+    const uint8_t* lv = buf + (DIRECT ? PF_BN * PF_DROW : LD::K_BYTES);
     const int kb = kt * PF_BN;
     f32x16_t sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const uint4 kx = *(const uint4*)(lk + lr * LD::KROW + (16 * t + 8 * grp) * 2);
+      const uint4 kx = DIRECT ? *(const uint4*)(lk + lr * PF_DROW + 16 * ((2 * t + grp) ^ (lr & 7)))
+                              : *(const uint4*)(lk + lr * LD::KROW + (16 * t + 8 * grp) * 2);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, kx);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(qreg[t][0], qreg[t][1], qreg[t][2], qreg[t][3]));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, sc, 0, 0, 0);
@@ -694,20 +733,38 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(P[0], P[1], P[2], P[3]));
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {   // V^T pairs x = 8 s + 4 grp .. + 3 of dim row 32 dt + lr
-        const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW + 32 * s + 16 * grp;
-        const uint2 lo = *(const uint2*)vrow;
-        const uint2 hi = *(const uint2*)(vrow + 8);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        bf16x8_t av;
+        if constexpr (DIRECT) {
+          // lane 16 j + i: key rows x + {0, 16, 1, 17}[i / 4] (+ 2 in the second read),
+          // x = 8 s + 4 grp, bytes 32 (j % 2) + 8 (i % 4) of 64-byte block dt; it
+          // receives dim 32 dt + 16 (j % 2) + i of those rows, the keys in the
+          // pair order of the weights: x, x + 16, x + 1, x + 17, x + 2, ...
+          const int i4 = (lane & 15) >> 2;
+          const int r1 = 8 * s + 4 * grp + (i4 >> 1) + 16 * (i4 & 1), r2 = r1 + 2;
+          const int cb = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+          const pf_s4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) pf_s4_t*)(lv + r1 * PF_DROW + 64 * (dt ^ pfv_g(r1)) + cb));
+          const pf_s4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) pf_s4_t*)(lv + r2 * PF_DROW + 64 * (dt ^ pfv_g(r2)) + cb));
+          const uint2 lo = __builtin_bit_cast(uint2, v1), hi = __builtin_bit_cast(uint2, v2);
+          av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          const uint8_t* vrow = lv + (32 * dt + lr) * LD::VROW + 32 * s + 16 * grp;
+          const uint2 lo = *(const uint2*)vrow;
+          const uint2 hi = *(const uint2*)(vrow + 8);
+          av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[dt], 0, 0, 0);
       }
     }
   };
 
+  // tiles below tfull hold only keys that every row of the segment sees
+  const int tfull = min(T, a.causal ? first_pos + 1 : T) / PF_BN;
+  if constexpr (!DIRECT) {
   // the next tile in registers while one is computed, two LDS buffers.  One
   // loop body per tile (the buffer offset alternates at run time) keeps the
   // accumulators in the same registers from tile to tile.
-  // tiles below tfull hold only keys that every row of the segment sees
-  const int tfull = min(T, a.causal ? first_pos + 1 : T) / PF_BN;
   TileRegs R0;
   int nb0 = 0, nb1 = 0;
   tab(t0, nb0, nb1);
@@ -734,6 +791,60 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   const int tm = max(t0, min(t1, tfull));
   for (int t = t0; t < tm; ++t) tile(t, std::false_type{});
   for (int t = tm; t < t1; ++t) tile(t, std::true_type{});
+  } else {
+    // Wave w loads K and V rows 8 w .. 8 w + 7 of a tile, two buffer-to-LDS
+    // instructions each (rows 8 w + 4 n .. + 3): lane i takes row
+    // 8 w + 4 n + i / 16 and the 16 bytes for LDS chunk i % 16.  Waves 0-1
+    // read the block of the tile's first key, waves 2-3 that of key 16 (the
+    // next table entry with blocks of 16 tokens, the same block otherwise).
+    const int prow = 8 * wave + (lane >> 4), pch = lane & 15;
+    const int64_t blk_bytes = (int64_t)a.block_size * a.tok_stride;
+    auto issue = [&](int t, int stage) {
+      const int jlo = min((t * PF_BN) >> a.bs_log2, jmax);
+      const int j = (wave >= 2 && a.block_size == 16) ? min(jlo + 1, jmax) : jlo;
+      int blk = uniform_load(table, j);
+      blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;
+      const int kstart = j << a.bs_log2;   // key of the block's first row
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + blk * blk_bytes, (int32_t)blk_bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + blk * blk_bytes, (int32_t)blk_bytes);
+      uint8_t* st = lds + stage * PF_DSTAGE;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int R = prow + 4 * n;
+        const int key = min(t * PF_BN + R, T - 1);   // past the context: its last row
+        const uint32_t ro = (uint32_t)((int64_t)(key - kstart) * a.tok_stride + kvh * PF_DROW);
+        const uint32_t ko = ro + 16 * (pch ^ (R & 7));
+        const uint32_t vo = ro + 16 * (4 * ((pch >> 2) ^ pfv_g(R)) + (pch & 3));
+        const int rowb = (8 * wave + 4 * n) * PF_DROW;
+        pf_load_lds16(rk, ko, __builtin_amdgcn_readfirstlane(pf_lds_addr(st + rowb)));
+        pf_load_lds16(rv, vo, __builtin_amdgcn_readfirstlane(pf_lds_addr(st + PF_BN * PF_DROW + rowb)));
+      }
+    };
+    // two tiles ahead; before a tile is read, this wave's four loads of it
+    // have landed (at most the four of the next tile still in flight), and
+    // the barrier makes every wave's visible and frees the stage the tile two
+    // ahead then goes to.  The first tile's loads and the query fragments are
+    // waited for together before the second tile is issued, so that no load
+    // the compiler tracks is still in flight in the loop (it would otherwise
+    // wait for all loads, the tile two ahead's among them, before the MFMAs)
+    issue(t0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (t0 + 1 < t1) issue(t0 + 1, 1);
+    int stage = 0;
+    auto dtile = [&](int t, auto masked) {
+      if (t + 1 < t1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      if (t + 2 < t1) issue(t + 2, stage == 0 ? 2 : stage - 1);
+      if (wave_ok) compute(lds + stage * PF_DSTAGE, t, masked);
+      stage = stage == 2 ? 0 : stage + 1;
+    };
+    const int tm = max(t0, min(t1, tfull));
+    for (int t = t0; t < tm; ++t) dtile(t, std::false_type{});
+    for (int t = tm; t < t1; ++t) dtile(t, std::true_type{});
+  }
   __syncthreads();   // the next piece reuses the LDS buffers
 
   const float ltot = lsum + shfl_xor(lsum, 32);
@@ -768,10 +879,10 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
   }
 }
 
-template <int CDT, int HD, int G>
+template <int CDT, int HD, int G, bool DIRECT>
 __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillArgs a) {
   using LD = PrefillLds<CDT, HD>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LD::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DIRECT ? PF_DSTAGES * PF_DSTAGE : 2 * LD::BUF];
   const int W = gridDim.x;
   const int wg = xcd_local_order(blockIdx.x, W);
   const int64_t u0 = uniform_load(a.wg_begin, wg), u1 = uniform_load(a.wg_begin, wg + 1);
@@ -786,7 +897,7 @@ __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillAr
     const int nu = uniform_load(a.seg_cu, g + 1) - uniform_load(a.seg_cu, g);
     const int end = (int)min((int64_t)nu, off + (u1 - u));
     const int tb = max(off - PF_OV, 0), te = max(end - PF_OV, 0);
-    if (te > tb) prefill_piece<CDT, HD, G>(a, g, tb, te, nu - PF_OV, wg, lds);
+    if (te > tb) prefill_piece<CDT, HD, G, DIRECT>(a, g, tb, te, nu - PF_OV, wg, lds);
     u += end - off;
     if (u >= u1) break;
     do { ++g; } while (uniform_load(a.seg_cu, g + 1) == uniform_load(a.seg_cu, g));
@@ -896,13 +1007,13 @@ static PfLayout pf_layout(int64_t num_seqs, int64_t nseg, int64_t wgs, int head_
   return l;
 }
 
-template <int CDT, int HD, int G>
+template <int CDT, int HD, int G, bool DIRECT>
 static int pf_resident_wgs() {
   static int cache[MAX_DEVICES] = {};   // per device and instantiation
   int& cached = cache[current_device()];
   if (!cached) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<CDT, HD, G>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<CDT, HD, G, DIRECT>, 256, 0) !=
             hipSuccess || per_cu <= 0)
       per_cu = 1;
     if (per_cu > PF_MAX_WGS_PER_CU) per_cu = PF_MAX_WGS_PER_CU;
@@ -911,10 +1022,10 @@ static int pf_resident_wgs() {
   return cached;
 }
 
-template <int CDT, int HD, int G>
-static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len,
-                           const PfLayout& l, char* ws, bool route, hipStream_t st) {
-  const int W = pf_resident_wgs<CDT, HD, G>();
+template <int CDT, int HD, int G, bool DIRECT>
+static pa_status pf_launch_k(PrefillArgs a, int num_seqs, int total_q, int max_q_len,
+                             const PfLayout& l, char* ws, bool route, hipStream_t st) {
+  const int W = pf_resident_wgs<CDT, HD, G, DIRECT>();
   a.hdr = (const int32_t*)(ws + l.hdr);
   a.seg_cu = (const int32_t*)(ws + l.seg);
   a.seg_desc = (const int4*)(ws + l.desc);
@@ -929,11 +1040,24 @@ static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_l
                        (int32_t*)(ws + l.wgb), (int32_t*)(ws + l.sw0),
                        route ? (int32_t*)(ws + l.drow_ctx) : nullptr,
                        route ? (int32_t*)(ws + l.drow_map) : nullptr);
-  if (e == PA_OK) e = launch(prefill_kernel<CDT, HD, G>, dim3(W), dim3(256), 0, st, a);
+  if (e == PA_OK) e = launch(prefill_kernel<CDT, HD, G, DIRECT>, dim3(W), dim3(256), 0, st, a);
   if (e == PA_OK)
     e = launch(prefill_merge_kernel<HD, G>, dim3(a.nseg_max * (PF_ROWS / MergeShape<HD>::ROWS)),
                dim3(256), 0, st, a, W);
   return e;
+}
+
+// bf16 caches at head_dim 128 with blocks of 16 tokens or more load their
+// tiles straight into LDS; the rest stage them through registers (8- and 4-bit
+// codes are widened on the way)
+template <int CDT, int HD, int G>
+static pa_status pf_launch(PrefillArgs a, int num_seqs, int total_q, int max_q_len,
+                           const PfLayout& l, char* ws, bool route, hipStream_t st) {
+  if constexpr (CDT == PA_BF16 && HD == 128) {
+    if (a.block_size >= 16)
+      return pf_launch_k<CDT, HD, G, true>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
+  }
+  return pf_launch_k<CDT, HD, G, false>(a, num_seqs, total_q, max_q_len, l, ws, route, st);
 }
 
 template <int CDT, int HD>
