@@ -482,7 +482,7 @@ __device__ __forceinline__ int widened_elem(int i, bool hi) {
 
 template <int CDT, int HD, int G, bool DIRECT>
 __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t0, int t1, int nt,
-                                              int wg, uint8_t* lds) {
+                                              int split, int wg, uint8_t* lds) {
   static_assert(!DIRECT || (CDT == PA_BF16 && HD == 128), "direct tiles: bf16, head_dim 128");
   using LD = PrefillLds<CDT, HD>;
   constexpr int QB = PF_ROWS / G;            // queries per segment
@@ -761,26 +761,35 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
 
   // tiles below tfull hold only keys that every row of the segment sees
   const int tfull = min(T, a.causal ? first_pos + 1 : T) / PF_BN;
+  // Order of the key tiles: step i < tfull computes tile (i + rot) mod tfull,
+  // the masked tiles follow in order.  rot makes the piece that starts at the
+  // segment's first split point (step `split`) start at tile 0, so that the
+  // workgroups starting at the k-th split point of the query tiles of one
+  // (sequence, KV head) read the same K/V tiles at about the same time and
+  // share them in L2.  Any order gives the same (m, l, O) up to rounding; the
+  // order is fixed by the plan, so results do not change from run to run.
+  const int rot = tfull > 0 ? (tfull - split % tfull) % tfull : 0;
+  auto tile_of = [&](int i) { return i < tfull ? (i + rot < tfull ? i + rot : i + rot - tfull) : i; };
   if constexpr (!DIRECT) {
   // the next tile in registers while one is computed, two LDS buffers.  One
   // loop body per tile (the buffer offset alternates at run time) keeps the
   // accumulators in the same registers from tile to tile.
   TileRegs R0;
   int nb0 = 0, nb1 = 0;
-  tab(t0, nb0, nb1);
+  tab(tile_of(t0), nb0, nb1);
   nb0 = (unsigned)nb0 < (unsigned)a.num_blocks ? nb0 : 0;
   nb1 = (unsigned)nb1 < (unsigned)a.num_blocks ? nb1 : 0;
-  gload(t0, nb0, nb1, R0);
-  tab(min(t0 + 1, t1 - 1), nb0, nb1);
+  gload(tile_of(t0), nb0, nb1, R0);
+  tab(tile_of(min(t0 + 1, t1 - 1)), nb0, nb1);
   nb0 = (unsigned)nb0 < (unsigned)a.num_blocks ? nb0 : 0;
   nb1 = (unsigned)nb1 < (unsigned)a.num_blocks ? nb1 : 0;
   int boff = 0;
   auto tile = [&](int t, auto masked) {
-    sstore(R0, lds + boff, t);
-    gload(min(t + 1, t1 - 1), nb0, nb1, R0);
+    sstore(R0, lds + boff, tile_of(t));
+    gload(tile_of(min(t + 1, t1 - 1)), nb0, nb1, R0);
     __syncthreads();
-    tab(min(t + 2, t1 - 1), nb0, nb1);
-    if (wave_ok) compute(lds + boff, t, masked);
+    tab(tile_of(min(t + 2, t1 - 1)), nb0, nb1);
+    if (wave_ok) compute(lds + boff, tile_of(t), masked);
     // ids outside the pool read block 0 (their keys are past the context or
     // the table breaks its contract); checked here, after the tile, where the
     // scalar loads have long returned
@@ -827,9 +836,9 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
     // waited for together before the second tile is issued, so that no load
     // the compiler tracks is still in flight in the loop (it would otherwise
     // wait for all loads, the tile two ahead's among them, before the MFMAs)
-    issue(t0, 0);
+    issue(tile_of(t0), 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (t0 + 1 < t1) issue(t0 + 1, 1);
+    if (t0 + 1 < t1) issue(tile_of(t0 + 1), 1);
     int stage = 0;
     auto dtile = [&](int t, auto masked) {
       if (t + 1 < t1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
@@ -837,8 +846,8 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      if (t + 2 < t1) issue(t + 2, stage == 0 ? 2 : stage - 1);
-      if (wave_ok) compute(lds + stage * PF_DSTAGE, t, masked);
+      if (t + 2 < t1) issue(tile_of(t + 2), stage == 0 ? 2 : stage - 1);
+      if (wave_ok) compute(lds + stage * PF_DSTAGE, tile_of(t), masked);
       stage = stage == 2 ? 0 : stage + 1;
     };
     const int tm = max(t0, min(t1, tfull));
@@ -894,10 +903,16 @@ __global__ __launch_bounds__(256, PREFILL_MIN_WGS) void prefill_kernel(PrefillAr
   // then its key tiles; a range that holds only start-up units of a segment
   // computes nothing there
   while (true) {
-    const int nu = uniform_load(a.seg_cu, g + 1) - uniform_load(a.seg_cu, g);
+    const int c0 = uniform_load(a.seg_cu, g);
+    const int nu = uniform_load(a.seg_cu, g + 1) - c0;
     const int end = (int)min((int64_t)nu, off + (u1 - u));
     const int tb = max(off - PF_OV, 0), te = max(end - PF_OV, 0);
-    if (te > tb) prefill_piece<CDT, HD, G, DIRECT>(a, g, tb, te, nu - PF_OV, wg, lds);
+    if (te > tb) {
+      // the segment's first split point: where the workgroup after the one
+      // holding its first unit begins (past the segment if none does)
+      const int split = max(uniform_load(a.wg_begin, uniform_load(a.seg_w0, g) + 1) - c0 - PF_OV, 0);
+      prefill_piece<CDT, HD, G, DIRECT>(a, g, tb, te, nu - PF_OV, split, wg, lds);
+    }
     u += end - off;
     if (u >= u1) break;
     do { ++g; } while (uniform_load(a.seg_cu, g + 1) == uniform_load(a.seg_cu, g));

@@ -187,11 +187,23 @@ def prefill_planner_starts(cu, wgb):
     return start, w0
 
 
-def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
+def pf_tile_order(split, tfull):
+    """The kernel's key-tile order in a segment: step i < tfull computes tile
+    (i + rot) mod tfull, rot chosen so that step `split` (where the segment's
+    first split point falls) computes tile 0; the masked tiles follow in order."""
+    rot = (tfull - split % tfull) % tfull if tfull > 0 else 0
+    return lambda i: (i + rot) % tfull if i < tfull else i
+
+
+def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV, tfull=None):
     """Prefill: a segment with n key tiles holds n + ov units (start-up units
     first); workgroup w takes units [wg_begin[w], wg_begin[w + 1]); a piece of
-    workgroup w in segment g -> slot w + g; the merge walks the workgroups from
-    seg_w0[g] and reads the pieces with tiles."""
+    workgroup w in segment g -> slot w + g, computing the steps of its range in
+    the rotated tile order (tiles below tfull[g] rotated); the merge walks the
+    workgroups from seg_w0[g] and reads the pieces with tiles.  Returns, per
+    segment, the first tile of each piece in order."""
+    if tfull is None:
+        tfull = list(tiles)
     units = [n + ov if n > 0 else 0 for n in tiles]
     cu = [0]
     for n in units:
@@ -201,6 +213,7 @@ def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
     assert wgb[0] == 0 and wgb[W] == U and all(a <= b for a, b in zip(wgb, wgb[1:]))
     start, w0 = prefill_planner_starts(cu, wgb)
     written, covered = {}, [[0] * n for n in tiles]
+    firsts = [[] for _ in tiles]
     for w in range(W):
         u0, u1 = wgb[w], wgb[w + 1]
         if u0 >= u1:
@@ -217,8 +230,13 @@ def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
                     slot = w + g
                     assert slot < W + nseg and slot not in written
                     written[slot] = (g, tb, te)
+                split = max(wgb[w0[g] + 1] - cu[g] - ov, 0)
+                order = pf_tile_order(split, tfull[g])
+                if tb == split and split < tfull[g]:
+                    assert order(tb) == 0
+                firsts[g].append(order(tb))
                 for t in range(tb, te):
-                    covered[g][t] += 1
+                    covered[g][order(t)] += 1
             u += end - off
             if u >= u1:
                 break
@@ -250,6 +268,7 @@ def replay_prefill(tiles, W, C=0, wt=PF_WT, ov=PF_OV):
             w += 1
         assert whole or got == tiles[g]
     assert read == set(written)
+    return firsts
 
 
 def test_decode_weighted_split_owner_and_exactness():
@@ -296,10 +315,29 @@ def test_prefill_split_covers_every_tile_once(seed):
         tiles = [rng.choice([0, 1, 2, 5, rng.randint(1, 40)]) for _ in range(rng.randint(1, 10))]
         if sum(tiles) == 0:
             continue
+        tfull = [max(0, n - rng.choice([0, 0, 1, 2, n])) for n in tiles]
         for W, C in ((1, 0), (2, 0), (3, 0), (5, 0), (17, 0), (256, 0), (768, 256), (24, 8),
                      (512, 256), (1024, 256), (17, 256), (912, 304)):
-            replay_prefill(tiles, W, C)
-            replay_prefill(tiles, W, C, wt=(7, 5, 3, 1), ov=rng.choice([0, 1, 5]))
+            replay_prefill(tiles, W, C, tfull=tfull)
+            replay_prefill(tiles, W, C, wt=(7, 5, 3, 1), ov=rng.choice([0, 1, 5]), tfull=tfull)
+
+
+def test_prefill_tile_order_aligns_the_split_points():
+    """Equal segments split at equal unit counts: the pieces that start at the
+    k-th split point of each segment start at the same key tile (the first split
+    point at tile 0), so the query tiles of one (sequence, KV head) read the same
+    K/V tiles at the same time."""
+    for n, nseg, W in ((92, 16, 64), (92, 16, 48), (1040, 16, 80)):
+        units = (n + PF_OV) * nseg
+        if units % W:
+            continue
+        firsts = replay_prefill([n] * nseg, W, 0, ov=PF_OV)
+        A = units // W
+        heads = [f for f in firsts if len(f) > 1]
+        assert heads
+        for f in heads:
+            assert f[1] == 0
+            assert f[1:] == [(k * A) % n for k in range(len(f) - 1)]
 
 
 PF_ROWS, PF_BN = 128, 32
@@ -359,9 +397,13 @@ def test_prefill_plan_covers_every_row_once(seed):
                     assert last_key < tiles * PF_BN  # the segment loads every key it sees
         assert len(seen) == sum(lens) * n_kv * G
         tiles = [t for (_, _, _, t) in segs]
+        tfull = []
+        for (s, _, qt, _) in segs:                       # tiles every row of the segment sees
+            T, L = ctx[s], lens[s]
+            tfull.append(min(T, T - L + qt * QB + 1 if causal else T) // PF_BN)
         if sum(tiles):
             for W, C in ((1, 0), (3, 0), (64, 0), (1000, 0), (768, 256)):
-                replay_prefill(tiles, W, C)
+                replay_prefill(tiles, W, C, tfull=tfull)
 
 
 def decode_row_lists(lens, ctx):
