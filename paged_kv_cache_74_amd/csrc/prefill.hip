@@ -126,10 +126,11 @@ struct PrefillLds {
 // stages, two tiles ahead, with no register staging.  A stage holds the
 // tile's 32 K rows and 32 V rows as they sit in the cache (256 bytes each),
 // swizzled so that the operand reads meet no bank conflicts:
-//   * K: 16-byte chunk c of row r at chunk c ^ (r & 7).  A score operand read
-//     takes the same chunk of 8 consecutive rows per 8 lanes: 8 different
-//     chunk positions (16-byte accesses are served 8 lanes at a time, free
-//     when the 8 differ in address bits 4..6).
+//   * K: 16-byte chunk c of row r at chunk c ^ (r & 15).  A score operand
+//     read takes the same chunk of 16 consecutive rows per 16 lanes: 16
+//     different chunk positions of the 256-byte bank window (16-byte reads
+//     are served 16 lanes at a time; with c ^ (r & 7) the pattern repeated
+//     every 8 rows and each read took twice its cycles).
 //   * V: 64-byte block b of row r at block b ^ pfv_g(r).  The PV operand
 //     (V^T, 32 dims x 16 keys) comes from two ds_read_b64_tr_b16 per MFMA:
 //     each 16 lanes supply the rows of 4 keys and receive, per lane, one
@@ -660,7 +661,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
     for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const uint4 kx = DIRECT ? *(const uint4*)(lk + lr * PF_DROW + 16 * ((2 * t + grp) ^ (lr & 7)))
+      const uint4 kx = DIRECT ? *(const uint4*)(lk + lr * PF_DROW + 16 * ((2 * t + grp) ^ (lr & 15)))
                               : *(const uint4*)(lk + lr * LD::KROW + (16 * t + 8 * grp) * 2);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, kx);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(qreg[t][0], qreg[t][1], qreg[t][2], qreg[t][3]));
@@ -822,7 +823,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillArgs& a, int g, int t
         const int R = prow + 4 * n;
         const int key = min(t * PF_BN + R, T - 1);   // past the context: its last row
         const uint32_t ro = (uint32_t)((int64_t)(key - kstart) * a.tok_stride + kvh * PF_DROW);
-        const uint32_t ko = ro + 16 * (pch ^ (R & 7));
+        const uint32_t ko = ro + 16 * (pch ^ (R & 15));
         const uint32_t vo = ro + 16 * (4 * ((pch >> 2) ^ pfv_g(R)) + (pch & 3));
         const int rowb = (8 * wave + 4 * n) * PF_DROW;
         pf_load_lds16(rk, ko, __builtin_amdgcn_readfirstlane(pf_lds_addr(st + rowb)));
