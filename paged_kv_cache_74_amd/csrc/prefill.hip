@@ -275,6 +275,7 @@ __device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t* wsum, int
 // work: {0, 0} in the header.
 constexpr int PF_PREP_LDS_SEQS = 4095;
 constexpr int PF_PREP_LDS_WGS = 2048;
+constexpr int PF_PREP_LDS_SEGS = 6143;
 __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int num_seqs, int total_q,
                                                             int max_q_len, int QB,
                                                             int num_wgs, int32_t* __restrict__ hdr,
@@ -289,6 +290,7 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
   __shared__ int64_t wsum[32];
   __shared__ int32_t seq_seg0_l[PF_PREP_LDS_SEQS + 1];
   __shared__ int32_t wgb_l[PF_PREP_LDS_WGS + 1];
+  __shared__ int32_t segcu_l[PF_PREP_LDS_SEGS + 1];
   const int t = threadIdx.x;
   const bool in_lds = num_seqs <= PF_PREP_LDS_SEQS;
   int32_t* seq_seg0 = in_lds ? seq_seg0_l : seq_seg0_g;
@@ -329,6 +331,10 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
     if (t == 1023) seq_seg0[num_seqs] = (int)g;
   }
   const int nseg = nseg_all <= a.nseg_max ? (int)nseg_all : 0;
+  // the segments' unit prefix sums (and, before the scan, their tile counts)
+  // in LDS for the searches of step 4 when they fit; each thread reads and
+  // writes only its own segments' entries until the barrier before step 4
+  const bool cu_in_lds = nseg <= PF_PREP_LDS_SEGS;
   __threadfence_block();
   __syncthreads();
   // 2. descriptors and tile counts, then their prefix sums
@@ -350,6 +356,7 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
       const int kvh = local / nq, qt = local % nq;
       const int n = seg_tiles(L, a.context_lens[s], qt, QB, a.causal);
       seg_desc[g] = make_int4(s, kvh, qt, n);
+      if (cu_in_lds) segcu_l[g] = n;
       ct += n > 0 ? n + PF_OV : 0;
     }
   }
@@ -362,11 +369,17 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
   if (ok) {
     int64_t c = ct_end - ct;
     for (int g = g0; g < g1; ++g) {
+      const int n = cu_in_lds ? segcu_l[g] : seg_desc[g].w;
       seg_cu[g] = (int)c;
-      c += seg_desc[g].w > 0 ? seg_desc[g].w + PF_OV : 0;
+      if (cu_in_lds) segcu_l[g] = (int)c;
+      c += n > 0 ? n + PF_OV : 0;
     }
   }
-  if (t == 0) seg_cu[nseg_used] = (int)U;
+  if (t == 0) {
+    seg_cu[nseg_used] = (int)U;
+    if (cu_in_lds) segcu_l[nseg_used] = (int)U;
+  }
+  const int32_t* scu = cu_in_lds ? segcu_l : seg_cu;
   const bool wgb_in_lds = num_wgs <= PF_PREP_LDS_WGS;
   const int32_t* wgb = wgb_in_lds ? wgb_l : wg_begin;
   for (int w = t; w <= num_wgs; w += 1024) {
@@ -386,13 +399,13 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(PrefillArgs a, int n
       int lo = 0, hi = nseg_used;               // seg_cu[lo] <= x < seg_cu[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (seg_cu[mid] <= x) lo = mid; else hi = mid;
+        if (scu[mid] <= x) lo = mid; else hi = mid;
       }
       wg_start[2 * w] = lo;
-      wg_start[2 * w + 1] = x - seg_cu[lo];
+      wg_start[2 * w + 1] = x - scu[lo];
     }
     for (int g = g0; g < min(g1, nseg_used); ++g) {
-      const int c = seg_cu[g];
+      const int c = scu[g];
       int lo = 0, hi = num_wgs;                 // wgb[lo] <= c < wgb[hi] = U
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
