@@ -185,21 +185,32 @@ __device__ __forceinline__ int seg_tiles(int L, int T, int qt, int QB, int causa
 
 // Weights of the work split.  With R resident workgroups per CU the grid is
 // dispatched in R rounds (blocks [r C, (r + 1) C) in round r), and the waves of
-// the R workgroups sharing a SIMD are issued oldest first: measured with equal
-// tile counts on the mixed step (three per CU), workgroups of rounds 0, 1 and 2
-// took 385, 403 and 435 us on average.  A workgroup of round r therefore takes
-// a share of the units proportional to pf_wt(r) (with weights 64, 59, 51 the
-// three rounds finished at 395, 399 and 405 us on average; with 64, 60, 53 at
-// 393, 401 and 410 us).  In the XCD-local work order
-// (xcd_local_order) workgroup w = x M + k, M = W / 8, was block 8 k + x, of
-// round k / (C / 8).  The weights only move split points; any other dispatch
-// order gives the same results, only less evenly timed.
+// the R workgroups sharing a SIMD are issued oldest first, so a workgroup of a
+// later round runs slower.  A workgroup of round r takes a share of the units
+// proportional to pf_wt(r).  Measured with per-workgroup timestamps on the
+// mixed step (three per CU): with weights 64, 59, 50 the rounds finished at
+// 316, 347 and 369 us on average; with 64, 52, 41 at 338, 337 and 350 us; with
+// 64, 50, 38 at 347, 335 and 342 us (the last workgroup ended at 369, 366 and
+// 362 us).  In the XCD-local work order (xcd_local_order) workgroup
+// w = x M + k, M = W / 8, was block 8 k + x, of round k / (C / 8).  The weights
+// only move split points; any other dispatch order gives the same results,
+// only less evenly timed.
 #ifndef PF_WT
-#define PF_WT 64, 59, 50, 47
+#define PF_WT 64, 51, 39, 36
 #endif
 __device__ __forceinline__ int pf_wt(int r) {
   constexpr int t[4] = {PF_WT};
   return t[r < 4 ? r : 3];
+}
+// Workgroups on odd XCDs (w / (W / 8) odd in the work order) take a share
+// scaled by PF_XW's second weight against the first: on the mixed step their
+// workgroups took 3.1-3.7% longer at equal shares, 0.1% longer at 33 : 32.
+#ifndef PF_XW
+#define PF_XW 33, 32
+#endif
+__device__ __forceinline__ int pf_xw(int x) {
+  constexpr int t[2] = {PF_XW};
+  return t[x & 1];
 }
 // sum of the split weights of workgroups [0, w) in the work order (equal
 // weights when the grid is not R whole rounds of 8-XCD-divisible CUs)
@@ -211,9 +222,10 @@ __device__ __forceinline__ int64_t pf_wsum(int w, int W, int C) {
   int64_t perx = 0;
   for (int r = 0; r < R; ++r) perx += (int64_t)P * pf_wt(r);
   const int q = w / M, k = w - q * M, rk = k / P;
-  int64_t acc = q * perx;
-  for (int r = 0; r < rk; ++r) acc += (int64_t)P * pf_wt(r);
-  return acc + (int64_t)(k - rk * P) * pf_wt(rk);
+  int64_t in = 0;   // workgroups [0, k) of XCD q
+  for (int r = 0; r < rk; ++r) in += (int64_t)P * pf_wt(r);
+  in += (int64_t)(k - rk * P) * pf_wt(rk);
+  return ((int64_t)((q + 1) / 2) * pf_xw(0) + (int64_t)(q / 2) * pf_xw(1)) * perx + pf_xw(q) * in;
 }
 // first unit of workgroup w: floor(U S(w) / S(W)), S the weight prefix sum
 __device__ __forceinline__ int64_t pf_split_begin(int w, int64_t U, int W, int C) {

@@ -134,11 +134,12 @@ def replay_decode(ctx, n_kv, hw, W, ov=DEC_OV["int8"]):
 
 
 PF_OV = 8                        # start-up units per segment with tiles (prefill.hip)
-PF_WT = (64, 59, 50, 47)         # split weights of the dispatch rounds (prefill.hip)
+PF_WT = (64, 51, 39, 36)         # split weights of the dispatch rounds (prefill.hip)
+PF_XW = (33, 32)                 # split weights of workgroups on even / odd XCDs
 XCDS = 8
 
 
-def pf_wsum(w, W, C, wt=PF_WT):
+def pf_wsum(w, W, C, wt=PF_WT, xw=PF_XW):
     """Sum of the split weights of workgroups [0, w) in the XCD-local work order."""
     if not (C > 0 and C % XCDS == 0 and W % C == 0 and W // C <= 4 and W % XCDS == 0):
         return 64 * w
@@ -146,13 +147,14 @@ def pf_wsum(w, W, C, wt=PF_WT):
     perx = sum(P * wt[r] for r in range(R))
     q, k = divmod(w, M)
     rk = k // P
-    return q * perx + sum(P * wt[r] for r in range(rk)) + (k - rk * P) * wt[rk]
+    inside = sum(P * wt[r] for r in range(rk)) + (k - rk * P) * wt[rk] if q < XCDS else 0
+    return ((q + 1) // 2 * xw[0] + q // 2 * xw[1]) * perx + xw[q % 2] * inside
 
 
-def pf_split(U, W, C, wt=PF_WT):
+def pf_split(U, W, C, wt=PF_WT, xw=PF_XW):
     """wg_begin: workgroup w takes units [b[w], b[w + 1])."""
-    S = pf_wsum(W, W, C, wt)
-    return [U * pf_wsum(w, W, C, wt) // S for w in range(W + 1)]
+    S = pf_wsum(W, W, C, wt, xw)
+    return [U * pf_wsum(w, W, C, wt, xw) // S for w in range(W + 1)]
 
 
 def prefill_planner_starts(cu, wgb):
@@ -494,14 +496,15 @@ def test_prefill_planner_workgroup_starts():
 
 def test_prefill_split_weights_follow_the_rounds():
     """With three rounds of 256 CUs (768 workgroups in the XCD-local order), the
-    workgroups of round r take units in proportion PF_WT[r]."""
+    workgroups of round r on XCD x take units in proportion PF_WT[r] PF_XW[x % 2]."""
     U, W, C = 10 ** 6, 768, 256
     wgb = pf_split(U, W, C)
     share = [wgb[w + 1] - wgb[w] for w in range(W)]
+    total = (C // XCDS) * sum(PF_WT[:3]) * (XCDS // 2) * (PF_XW[0] + PF_XW[1])
     for w in range(W):
-        k = w % (W // XCDS)                    # index inside the XCD's range
+        x, k = divmod(w, W // XCDS)            # XCD, index inside the XCD's range
         r = k // (C // XCDS)                   # its dispatch round
-        assert abs(share[w] - U * PF_WT[r] / (C * sum(PF_WT[:3]))) <= 1
+        assert abs(share[w] - U * PF_WT[r] * PF_XW[x % 2] / total) <= 1
 
 
 def row_g(t):
