@@ -617,6 +617,66 @@ __device__ __forceinline__ void locate_unit(const int32_t* __restrict__ ctx, int
   *before = carry;
 }
 
+// The start of workgroup w: the total units U, its range [u0, u1) and, when
+// the range is not empty, the sequence s holding u0 and the units before s.
+// Up to 64 * DEC_CTX_REGS sequences, context_lens is read in one round of
+// loads held in registers (every load issued before the first is used), and
+// U and s come from those registers; longer batches take the two passes of
+// unit_counts and locate_unit (one round of loads per 64 sequences each).
+constexpr int DEC_CTX_REGS = 4;
+__device__ __forceinline__ void wg_plan(const int32_t* __restrict__ ctx, int num_seqs, int nhg,
+                                        int ov, int w, int W, int* U, int64_t* u0, int64_t* u1,
+                                        int* seq, int* before) {
+  if (num_seqs > 64 * DEC_CTX_REGS) {
+    int pre;
+    unit_counts(ctx, num_seqs, nhg, ov, 0, &pre, U);
+    *u0 = wave_begin(w, *U, W);
+    *u1 = wave_begin(w + 1, *U, W);
+    if (*u0 < *u1) locate_unit(ctx, num_seqs, nhg, ov, (int)*u0, seq, before);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  int v[DEC_CTX_REGS];
+#pragma unroll
+  for (int c = 0; c < DEC_CTX_REGS; ++c) {
+    const int i = 64 * c + lane;
+    v[c] = i < num_seqs ? ctx[i] : 0;
+  }
+  int tot = 0;
+#pragma unroll
+  for (int c = 0; c < DEC_CTX_REGS; ++c) {
+    v[c] = nhg * units_of(v[c], ov);
+    tot += v[c];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  *U = __builtin_amdgcn_readfirstlane(tot);
+  *u0 = wave_begin(w, *U, W);
+  *u1 = wave_begin(w + 1, *U, W);
+  if (*u0 >= *u1) return;
+  const int x = (int)*u0;
+  int carry = 0;
+#pragma unroll
+  for (int c = 0; c < DEC_CTX_REGS; ++c) {
+    int incl = v[c];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const uint64_t hit = __ballot(carry + incl > x);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      *seq = __builtin_amdgcn_readfirstlane(64 * c + l);
+      *before = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v[c], l, 64));
+      return;
+    }
+    carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63, 64));
+  }
+  *seq = num_seqs - 1;   // not reached for x < U
+  *before = carry;
+}
+
 // Steps [st0, st1) of segment (s, kvh): online softmax, then the partial of
 // this piece into entry `slot` of the partial arrays.
 template <int CDT, int HD, int G, int NBUF>
@@ -776,14 +836,12 @@ __global__ __launch_bounds__(64 * max_hw(CDT, G)) void decode_split_kernel(Decod
   const int w = blockIdx.x;
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
-  int pre, U;
   constexpr int OV = decode_seg_ov(CDT);
-  unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
+  int U, s = 0, before = 0;
+  int64_t u0, u1;
+  wg_plan(a.context_lens, a.num_seqs, a.nhg, OV, w, W, &U, &u0, &u1, &s, &before);
   if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, U);   // for the merge
-  const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
-  int s, before;
-  locate_unit(a.context_lens, a.num_seqs, a.nhg, OV, (int)u0, &s, &before);
   const int len0 = units_of(uniform_load(a.context_lens, s), OV);
   const int r = (int)u0 - before;
   int hg = r / len0;
@@ -1407,19 +1465,17 @@ __global__ __launch_bounds__(64 * DECODE_MAX_HW, DECODE_MF_MIN_WGS) void decode_
   const int w = blockIdx.x;
   const int W = a.num_wgs;
   const int wv = threadIdx.x >> 6;
-  int pre, U;
   constexpr int OV = decode_seg_ov(CDT);
-  unit_counts(a.context_lens, a.num_seqs, a.nhg, OV, 0, &pre, &U);
+  int U, s = 0, before = 0;
+  int64_t u0, u1;
+  wg_plan(a.context_lens, a.num_seqs, a.nhg, OV, w, W, &U, &u0, &u1, &s, &before);
   if (w == 0 && threadIdx.x == 0) *(int4*)a.header = make_int4(W, a.hw, OV, U);   // for the merge
   if constexpr (APPEND) {   // sequences without tokens append nothing: slot -1
     if (w == 0 && a.slots_out)
       for (int i = threadIdx.x; i < a.num_seqs; i += blockDim.x)
         if (a.context_lens[i] <= 0) a.slots_out[i] = -1;
   }
-  const int64_t u0 = wave_begin(w, U, W), u1 = wave_begin(w + 1, U, W);
   if (u0 >= u1) return;
-  int s, before;
-  locate_unit(a.context_lens, a.num_seqs, a.nhg, OV, (int)u0, &s, &before);
   const int len0 = units_of(uniform_load(a.context_lens, s), OV);
   const int rr = (int)u0 - before;
   int hg = rr / len0;
