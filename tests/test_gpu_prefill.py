@@ -45,7 +45,10 @@ def test_prefill_small_config(dev, causal):
 # (n_q, n_kv, head_dim, block_size): every group size, both head dims, small and large blocks
 SHAPES = [(4, 4, 128, 16), (8, 4, 64, 16), (16, 2, 128, 32), (32, 8, 64, 4), (8, 1, 128, 1),
           # blocks of 64 and more: a tile starts inside its block; 8: one table entry per key
-          (8, 2, 128, 64), (16, 4, 64, 256), (8, 8, 128, 8)]
+          (8, 2, 128, 64), (16, 4, 64, 256), (8, 8, 128, 8),
+          # head_dim 128, bf16, blocks of 16 or more load tiles straight into LDS;
+          # with 128 and 256 a tile starts at one of 4 or 8 offsets of its block
+          (8, 2, 128, 128), (16, 4, 128, 256)]
 
 
 @pytest.mark.parametrize("nq,nkv,hd,bs", SHAPES)
