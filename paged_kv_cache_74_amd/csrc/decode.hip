@@ -1718,21 +1718,22 @@ static int64_t resident_wgs(int hw) {
 #ifndef DECODE_MFMA_MASK
 #define DECODE_MFMA_MASK ((1 << PA_BF16) | (1 << PA_FP8_E4M3) | (1 << PA_INT8) | (1 << PA_INT4))
 #endif
-// steps in flight per wave on the matrix-core path (fewer bytes per step for
-// narrower codes, so more steps)
+// steps in flight per wave on the matrix-core path.  Fewer buffers leave more
+// registers to the rest of the step: on the long-tail step int4 ran at 224 us
+// with two against 247-249 us with three or four, fp8 at 308 against 317 us,
+// bf16 (Llama-3 and long tail) 0.2-0.4% faster; int8 312 against 308 us, so it
+// keeps three (one A/B run each)
 #ifndef DECODE_MF_NBUF4
-#define DECODE_MF_NBUF4 4   // INT4
+#define DECODE_MF_NBUF4 2   // INT4
 #endif
 #ifndef DECODE_MF_NBUF8
 #define DECODE_MF_NBUF8 3   // INT8
 #endif
-// FP8: on the long-tail step 308 us with two steps against 317 us with three
-// (int8 the other way: 312 against 308 us), one A/B run
 #ifndef DECODE_MF_NBUF_FP8
 #define DECODE_MF_NBUF_FP8 2
 #endif
 #ifndef DECODE_MF_NBUF16
-#define DECODE_MF_NBUF16 3   // BF16
+#define DECODE_MF_NBUF16 2   // BF16
 #endif
 // staged loads on the matrix-core path where the layout allows (1), or per-head
 // loads everywhere (0)
